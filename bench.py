@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the PN-Mix key-cache path on one MI355X.
+
+One step = one generation step of every layer of the batch through the library: place the new
+key/value rows (pnmix_append_kv), decode attention over sinks + packed pages + fp16 residual
+(pnmix_decode_attn), and -- whenever a residual buffer reaches N tokens -- quantize it into a
+page (pnmix_quantize_k_page / pnmix_quantize_v_page, pnmix_commit_page).  The caches are built
+before timing from seeded synthetic inputs (prefill score of the first P tokens, bulk page
+quantization); W warm-up steps run untimed, then K steps are timed between device
+synchronisations.
+
+Prints ONE JSON line: throughput in KV token-heads per second (sum over steps and layers of
+B * cached tokens * H_kv / elapsed), the decode kernel's roofline (algorithmic bytes per call /
+event-timed duration), page-quantization and prefill-score sub-measurements, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(cfg, lens_list, kpb, vpb):
+    """Algorithmic bytes of one decode call: packed pages, fp16 sink/residual rows, mask,
+    queries and fp32 outputs, summed over (sequence, KV head)."""
+    ng = cfg.H_q // cfg.H_kv
+    words = (cfg.d // 2 + 31) // 32
+    tot = 0
+    for (s, n_p, r) in lens_list:
+        per_head = n_p * (kpb + vpb) + (s + r) * cfg.d * 2 * 2 + words * 4 + ng * cfg.d * 6
+        tot += per_head * cfg.H_kv + 16
+    return tot
+
+
+def build_layer(w, cfg, layer, B, T0, max_pages, steps, dev, P, synth, torch):
+    """Cache of one layer holding tokens [0, T0) and the inputs of `steps` decode steps."""
+    npairs = w.d // 2
+    sq = synth.pair_scales(w.H_q, npairs, w.sigma_ln, dev, w.name, layer, "q")
+    sk = synth.pair_scales(w.H_kv, npairs, w.sigma_ln, dev, w.name, layer, "k")
+    k = synth.rope_tokens(sk, B, torch.arange(T0 + steps, device=dev), w.d, w.pairing,
+                          w.rope_base, dev, w.name, layer, "k")
+    v = synth.values(B, w.H_kv, T0 + steps, w.d, dev, w.name, layer)
+    qp = synth.rope_tokens(sq, B, torch.arange(w.P, device=dev), w.d, w.pairing, w.rope_base,
+                           dev, w.name, layer, "qpre")
+    qs = synth.rope_tokens(sq, B, torch.arange(T0, T0 + steps, device=dev), w.d, w.pairing,
+                           w.rope_base, dev, w.name, layer, "qdec")
+    c = P.PNMixLayerCache(cfg, B, max_pages, dev)
+    c.prefill(qp, k[:, :, :w.P].contiguous(), v[:, :, :w.P].contiguous())
+    s = min(T0, w.N_s)
+    n_pages = (T0 - s) // w.N
+    if n_pages:
+        kj, _ = c.page_jobs(k, s, 0, n_pages)
+        _, vj = c.page_jobs(v, s, 0, n_pages)
+        P.pnmix_quantize_k_page(cfg, kj, c.mask)
+        P.pnmix_quantize_v_page(cfg, vj)
+    a = s + n_pages * w.N
+    rest = T0 - a
+    c.k_res[:, :, :rest] = k[:, :, a:T0]
+    c.v_res[:, :, :rest] = v[:, :, a:T0]
+    c.sink_len, c.n_pages, c.res_len = s, n_pages, rest
+    c._sync_lens()
+    # per-step inputs [steps][B][H][d], contiguous per step
+    q_steps = qs.permute(2, 0, 1, 3).contiguous()
+    k_steps = k[:, :, T0:T0 + steps].permute(2, 0, 1, 3).contiguous()
+    v_steps = v[:, :, T0:T0 + steps].permute(2, 0, 1, 3).contiguous()
+    torch.cuda.synchronize()
+    return c, q_steps, k_steps, v_steps, (k, v, qp, qs)
+
+
+def cpu_baseline(w, sample, seconds, threads):
+    """Time the oracle's float64 decode attention on sampled sequences of the workload."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    oc = oracle.Cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_V=w.b_V, g_V=w.g_V,
+                    N_s=w.N_s, N=w.N)
+    sm = float(np.float32(1.0 / math.sqrt(w.d)))
+    prepared = []
+    for (qp_b, k_b, v_b, qd_b, T) in sample:
+        _, _, _, mask = oracle.score_prefill(oc, qp_b, k_b[:, :w.P])
+        s = min(T, w.N_s)
+        n_pages = (T - s) // w.N
+        kp = np.zeros((w.H_kv, max(n_pages, 1), oracle.k_page_bytes(oc)), np.uint8)
+        vp = np.zeros((w.H_kv, max(n_pages, 1), oracle.v_page_bytes(oc)), np.uint8)
+        jobs = [(h, p) for h in range(w.H_kv) for p in range(n_pages)]
+
+        def qj(j, k_b=k_b, v_b=v_b, mask=mask, kp=kp, vp=vp, s=s):
+            h, p = j
+            kp[h, p] = oracle.quantize_k_page(oc, k_b[h, s + p * w.N:s + (p + 1) * w.N], mask[h])
+            vp[h, p] = oracle.quantize_v_page(oc, v_b[h, s + p * w.N:s + (p + 1) * w.N])
+
+        oracle.parallel_map(qj, jobs, threads)
+        a = s + n_pages * w.N
+        ks = np.zeros((w.H_kv, w.N_s, w.d), np.uint16)
+        vs = np.zeros_like(ks)
+        ks[:, :s], vs[:, :s] = k_b[:, :s], v_b[:, :s]
+        kr = np.zeros((w.H_kv, w.N, w.d), np.uint16)
+        vr = np.zeros_like(kr)
+        kr[:, :T - a], vr[:, :T - a] = k_b[:, a:T], v_b[:, a:T]
+        prepared.append((qd_b, ks, vs, kp, vp, kr, vr, mask, s, n_pages, T - a, T))
+
+    def run(i):
+        qd_b, ks, vs, kp, vp, kr, vr, mask, s, n_p, r, T = prepared[i % len(prepared)]
+        oracle.decode_attn_f64(oc, qd_b, ks, vs, kp, vp, kr, vr, mask, s, n_p, r, sm)
+        return T * w.H_kv
+
+    t0 = time.perf_counter()
+    run(0)
+    t_one = time.perf_counter() - t0
+    n_items = max(threads, int(seconds * threads / max(t_one, 1e-3)))
+    n_items = (n_items + threads - 1) // threads * threads
+    t0 = time.perf_counter()
+    work = sum(oracle.parallel_map(run, range(n_items), threads))
+    el = time.perf_counter() - t0
+    return {"value": work / el, "unit": "KV token-heads/s", "cores": threads, "kind": "oracle",
+            "sample": (f"float64 decode attention of {n_items} sequence-layers drawn from "
+                       f"{len(prepared)} sampled sequences of layer 0 (T={sample[0][4]}, "
+                       f"{w.H_kv} KV heads, {w.H_q} query heads), {el:.1f} s wall on "
+                       f"{threads} threads; page quantization excluded")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="qwen3-8b-36L-b32-8k")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence / KV head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_attention_pnmix_amd as P
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda"
+    w = synth.WORKLOADS[args.workload]
+    cfg = P.make_cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_V=w.b_V, g_V=w.g_V,
+                     N_s=w.N_s, N=w.N)
+    kpb, vpb = P.pnmix_k_page_bytes(cfg), P.pnmix_v_page_bytes(cfg)
+    W, K = args.warmup, args.steps
+    # the first timed step attends over exactly w.T tokens
+    T0 = w.T - W - 1
+    max_pages = (T0 + W + K - w.N_s) // w.N + 1
+    _say(f"[bench] workload={w.name} layers={w.layers} B={w.B} T0={T0} steps={K} warmup={W}")
+
+    caches, inputs = [], []
+    sample = []
+    n_sample = 4
+    t_build = time.perf_counter()
+    for layer in range(w.layers):
+        c, qst, kst, vst, raw = build_layer(w, cfg, layer, w.B, T0, max_pages, W + K, dev, P,
+                                            synth, torch)
+        caches.append(c)
+        inputs.append((qst, kst, vst))
+        if layer == 0 and not args.no_cpu_baseline:
+            k, v, qp, qs = raw
+            u16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+            for b in range(min(n_sample, w.B)):
+                sample.append((u16(qp[b]), u16(k[b, :, :T0]), u16(v[b, :, :T0]),
+                               u16(qs[b, :, 0]), T0))
+        del raw
+        for s in range(max_pages):  # page jobs of every flush slot, built before timing
+            if s >= c.n_pages:
+                c.flush_jobs(s)
+    torch.cuda.synchronize()
+    _say(f"[bench] caches built in {time.perf_counter() - t_build:.1f} s")
+
+    outs = [torch.empty(w.B, w.H_q, w.d, dtype=torch.float32, device=dev)
+            for _ in range(w.layers)]
+
+    def run_step(i, events=None, lens_log=None):
+        for layer, c in enumerate(caches):
+            qst, kst, vst = inputs[layer]
+            c.append(kst[i], vst[i])
+            if lens_log is not None:
+                lens_log.append((c.sink_len, c.n_pages, c.res_len))
+            if events is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                c.attend(qst[i], outs[layer])
+                e1.record()
+                events.append((e0, e1))
+            else:
+                c.attend(qst[i], outs[layer])
+            c.flush()
+
+    for i in range(W):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    events, lens_log = [], []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(W, W + K):
+        run_step(i, events, lens_log)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    tokheads = sum(w.B * (s + n_p * w.N + r) * w.H_kv for (s, n_p, r) in lens_log)
+    value = tokheads / elapsed
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in events]
+    bytes_calls = [decode_bytes(cfg, [ln] * w.B, kpb, vpb) for ln in lens_log]
+    dec_time = sum(durs)
+    achieved = sum(bytes_calls) / dec_time / 1e9
+    _say(f"[bench] {K} steps in {elapsed * 1e3:.1f} ms; decode calls avg "
+         f"{dec_time / len(durs) * 1e6:.1f} us, {achieved:.0f} GB/s")
+
+    # ---- page quantization: one bulk event over every layer's residual buffers
+    n_jobs = w.layers * w.B * w.H_kv
+    scratch_k = torch.empty(n_jobs, kpb, dtype=torch.uint8, device=dev)
+    scratch_v = torch.empty(n_jobs, vpb, dtype=torch.uint8, device=dev)
+    srcs_k, srcs_v, dk, dv, rows = [], [], [], [], []
+    masks = torch.cat([c.mask.reshape(-1, c.mask.shape[-1]) for c in caches]).contiguous()
+    for layer, c in enumerate(caches):
+        for bh in range(w.B * w.H_kv):
+            j = layer * w.B * w.H_kv + bh
+            srcs_k.append(c.k_res.data_ptr() + bh * w.N * w.d * 2)
+            srcs_v.append(c.v_res.data_ptr() + bh * w.N * w.d * 2)
+            dk.append(scratch_k.data_ptr() + j * kpb)
+            dv.append(scratch_v.data_ptr() + j * vpb)
+            rows.append(j)
+    kj = P.page_jobs(srcs_k, w.d, dk, rows, dev)
+    vj = P.page_jobs(srcs_v, w.d, dv, rows, dev)
+    qk_t, qv_t = [], []
+    for rep in range(6):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        P.pnmix_quantize_k_page(cfg, kj, masks)
+        e[1].record()
+        P.pnmix_quantize_v_page(cfg, vj)
+        e[2].record()
+        torch.cuda.synchronize()
+        if rep:
+            qk_t.append(e[0].elapsed_time(e[1]) * 1e-3)
+            qv_t.append(e[1].elapsed_time(e[2]) * 1e-3)
+    tk, tv = float(np.median(qk_t)), float(np.median(qv_t))
+    kbytes = n_jobs * (w.N * w.d * 2 + kpb)
+    vbytes = n_jobs * (w.N * w.d * 2 + vpb)
+    quant = {"pages_per_launch": n_jobs, "k_us": tk * 1e6, "v_us": tv * 1e6,
+             "k_GBps": kbytes / tk / 1e9, "v_GBps": vbytes / tv / 1e9,
+             "kv_GBps": (kbytes + vbytes) / (tk + tv) / 1e9,
+             "kv_frac_of_peak": (kbytes + vbytes) / (tk + tv) / 1e9 / HBM_PEAK_GBS}
+
+    # ---- prefill score of one layer's prompt batch (and the long prefill if the workload has one)
+    score = {}
+    for (Bs, Ps) in ([(w.B, w.P)] + ([(1, w.prefill_score_P)] if w.prefill_score_P else [])):
+        sq = synth.pair_scales(w.H_q, w.d // 2, w.sigma_ln, dev, w.name, 0, "q")
+        sk = synth.pair_scales(w.H_kv, w.d // 2, w.sigma_ln, dev, w.name, 0, "k")
+        qpp = synth.rope_tokens(sq, Bs, torch.arange(Ps, device=dev), w.d, w.pairing,
+                                w.rope_base, dev, w.name, "score", "q")
+        kpp = synth.rope_tokens(sk, Bs, torch.arange(Ps, device=dev), w.d, w.pairing,
+                                w.rope_base, dev, w.name, "score", "k")
+        ws = torch.empty(P.pnmix_score_workspace_bytes(cfg, Bs, Ps), dtype=torch.uint8,
+                         device=dev)
+        ts = []
+        for rep in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            P.pnmix_score_prefill(cfg, qpp, kpp, ws=ws, want_sigma=False)
+            e1.record()
+            torch.cuda.synchronize()
+            if rep:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = float(np.median(ts))
+        nb = Bs * Ps * (w.H_q + w.H_kv) * w.d * 2
+        score[f"B{Bs}_P{Ps}"] = {"us": t * 1e6, "GBps": nb / t / 1e9}
+
+    cpu = None
+    if not args.no_cpu_baseline and sample:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        cpu = cpu_baseline(w, sample, args.cpu_seconds, threads)
+
+    line = {
+        "metric": "decode-attn KV tokens·heads/s & % of HBM peak; K/V page-quant GB/s",
+        "value": value,
+        "unit": "KV token-heads/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": elapsed / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 in / packed u8 cache / fp32 attention",
+        "data": "synthetic (seeded; log-normal persistent pair outliers, RoPE, V ~ N(0,1))",
+        "config": {"workload": w.name, "layers": w.layers, "global_batch": w.B,
+                   "kv_tokens_at_first_timed_step": w.T, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "head_dim": w.d, "r": w.r, "G": w.G, "b_H": 3, "b_L": 1, "b_V": w.b_V,
+                   "N_s": w.N_s, "N": w.N, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "pnmix_decode_attn (split-K kernel + LSE merge)",
+                     "bytes_per_call": sum(bytes_calls) / len(bytes_calls),
+                     "avg_call_us": dec_time / len(durs) * 1e6},
+        "page_quant": quant,
+        "prefill_score": score,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,56 @@
+// common.h -- device helpers shared by the gfx950 kernels of libpnmix.so.
+//
+// Build contract (see build.py): hipcc --offload-arch=gfx950 -O3 -ffp-contract=off, IEEE fp32
+// division and square root (HIP's default correctly rounded expansion), fp16 denormals kept.
+// Under these flags every float expression below is the IEEE operation it spells, so the
+// quantizer and the score reproduce the reference arithmetic bit for bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pnmix.h"
+
+namespace pnmix {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float h2f(uint16_t u) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, u));
+}
+
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 under the default rounding mode), with
+// fp16 subnormals.
+__device__ __forceinline__ uint16_t f2h(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+__device__ __forceinline__ float canon(float x) { return x + 0.0f; }  // -0 -> +0
+
+// Mask bit of RoPE pair `pair` in a row of uint32 words (bit i = pair i, LSB first).
+__device__ __forceinline__ bool pair_selected(const uint32_t* row, int pair) {
+  return (row[pair >> 5] >> (pair & 31)) & 1u;
+}
+
+// Pair of channel `c` under the pairing: adjacent (2i, 2i+1) or split-half (i, i + d/2).
+__device__ __forceinline__ int pair_of_channel(int c, int d, int pairing) {
+  return pairing == PNMIX_PAIRS_ADJACENT ? (c >> 1) : (c < d / 2 ? c : c - d / 2);
+}
+
+// Rank of channel c among the salient channels in ascending channel order, or -1 when c is
+// not salient (or its rank would reach 2 * n_hi).  Salient channels are both channels of every selected pair.
+__device__ __forceinline__ int salient_rank(const uint32_t* row, int c, int d, int pairing,
+                                            int n_hi) {
+  const int p = pair_of_channel(c, d, pairing);
+  if (!pair_selected(row, p)) return -1;
+  int below = 0;  // selected pairs with index < p
+  for (int w = 0; w < (p >> 5); ++w) below += __popc(row[w]);
+  if (p & 31) below += __popc(row[p >> 5] & ((1u << (p & 31)) - 1u));
+  const int r = pairing == PNMIX_PAIRS_ADJACENT ? 2 * below + (c & 1)
+                                                : (c < d / 2 ? below : n_hi + below);
+  // a mask with more than n_hi pairs set (outside the contract) must not index past the
+  // n_sal columns of the upper-bit plane: such channels are treated as 1-bit
+  return r < 2 * n_hi ? r : -1;
+}
+
+}  // namespace pnmix

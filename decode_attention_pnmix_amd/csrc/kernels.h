@@ -1,0 +1,40 @@
+// kernels.h -- internal launch interface between the C ABI (pnmix_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pnmix.h"
+
+namespace pnmix {
+
+hipError_t launch_score(const pnmix_cfg& c, int B, int P, const uint16_t* q, const uint16_t* k,
+                        float* sigma, uint32_t* mask, void* ws, hipStream_t stream);
+size_t score_workspace_bytes(const pnmix_cfg& c, int B, int P);
+
+hipError_t launch_quantize_k(const pnmix_cfg& c, int n_pages, const pnmix_page* pages,
+                             const uint32_t* mask, hipStream_t stream);
+hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* pages,
+                             hipStream_t stream);
+
+struct DecodePlan {
+  int splits;           // split-K partitions per (sequence, KV head)
+  int blocks_per_split; // cache blocks (sink block, pages, residual block) per partition
+  size_t ws_bytes;
+};
+DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages);
+hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_t* q,
+                         const uint16_t* k_sink, const uint16_t* v_sink, const uint8_t* k_pages,
+                         const uint8_t* v_pages, const uint16_t* k_res, const uint16_t* v_res,
+                         const pnmix_seq_len* lens, const uint32_t* mask, float sm_scale,
+                         float* out, void* ws, hipStream_t stream);
+
+hipError_t launch_append_kv(const pnmix_cfg& c, int B, const uint16_t* k_new,
+                            const uint16_t* v_new, uint16_t* k_sink, uint16_t* v_sink,
+                            uint16_t* k_res, uint16_t* v_res, pnmix_seq_len* lens,
+                            hipStream_t stream);
+hipError_t launch_commit_page(const pnmix_cfg& c, int B, int max_pages, pnmix_seq_len* lens,
+                              hipStream_t stream);
+
+}  // namespace pnmix

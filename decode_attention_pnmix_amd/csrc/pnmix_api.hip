@@ -1,0 +1,196 @@
+// pnmix_api.hip -- the C ABI of libpnmix.so: host-side validation, size queries and launches.
+// Declarations and the contract of every entry point are in include/pnmix.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "kernels.h"
+#include "pnmix.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pnmix_status fail(pnmix_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pnmix_status ok() {
+  g_err[0] = '\0';
+  return PNMIX_OK;
+}
+
+pnmix_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PNMIX_E_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+pnmix_status check(const pnmix_cfg* c) {
+  if (!c) return fail(PNMIX_E_INVALID, "cfg is NULL");
+  if (c->H_q <= 0 || c->H_kv <= 0) return fail(PNMIX_E_INVALID, "H_q, H_kv must be positive");
+  if (c->H_q % c->H_kv) return fail(PNMIX_E_INVALID, "H_q %% H_kv != 0");
+  if (c->H_q / c->H_kv > 16) return fail(PNMIX_E_UNSUPPORTED, "n_g = H_q/H_kv > 16");
+  if (c->d != 32 && c->d != 64 && c->d != 128)
+    return fail(c->d > 0 && c->d % 2 == 0 ? PNMIX_E_UNSUPPORTED : PNMIX_E_INVALID,
+                "head_dim %d not in {32, 64, 128}", c->d);
+  if (c->pairing != PNMIX_PAIRS_ADJACENT && c->pairing != PNMIX_PAIRS_SPLIT_HALF)
+    return fail(PNMIX_E_INVALID, "pairing %d unknown", c->pairing);
+  if (c->n_hi_pairs < 0 || c->n_hi_pairs > c->d / 2)
+    return fail(PNMIX_E_INVALID, "n_hi_pairs %d outside [0, d/2]", c->n_hi_pairs);
+  if (c->N != 128) return fail(PNMIX_E_UNSUPPORTED, "page length N = %d (only 128)", c->N);
+  if (c->G <= 0 || c->N % c->G) return fail(PNMIX_E_INVALID, "G = %d does not divide N", c->G);
+  if (c->G != 32 && c->G != 64 && c->G != 128)
+    return fail(PNMIX_E_UNSUPPORTED, "G = %d not in {32, 64, 128}", c->G);
+  if (c->b_H != 3 || c->b_L != 1)
+    return fail(PNMIX_E_UNSUPPORTED, "(b_H, b_L) = (%d, %d); only (3, 1)", c->b_H, c->b_L);
+  if (c->b_V != 2) return fail(PNMIX_E_UNSUPPORTED, "b_V = %d; only 2", c->b_V);
+  if (c->g_V <= 0 || c->d % c->g_V) return fail(PNMIX_E_INVALID, "g_V = %d does not divide d", c->g_V);
+  if (c->g_V != 16 && c->g_V != 32 && c->g_V != 64 && c->g_V != 128)
+    return fail(PNMIX_E_UNSUPPORTED, "g_V = %d not in {16, 32, 64, 128}", c->g_V);
+  if (c->N_s < 0 || c->N_s > 128) return fail(PNMIX_E_INVALID, "N_s = %d outside [0, 128]", c->N_s);
+  return PNMIX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pnmix_status pnmix_check_cfg(const pnmix_cfg* cfg) {
+  const pnmix_status s = check(cfg);
+  return s == PNMIX_OK ? ok() : s;
+}
+
+int32_t pnmix_hi_pairs(double r, int32_t d) {
+  if (!(r >= 0.0) || d <= 0) return 0;
+  if (r > 1.0) r = 1.0;
+  return (int32_t)std::floor(r * (double)(d / 2) + 1e-9);
+}
+
+size_t pnmix_mask_words(const pnmix_cfg* c) { return c ? (size_t)(c->d / 2 + 31) / 32 : 0; }
+
+size_t pnmix_k_page_bytes(const pnmix_cfg* c) {
+  if (!c || c->G <= 0) return 0;
+  return (size_t)c->N * c->d / 8 + (size_t)c->N * 2 * c->n_hi_pairs / 4 +
+         4 * (size_t)(c->N / c->G) * c->d;
+}
+
+size_t pnmix_v_page_bytes(const pnmix_cfg* c) {
+  if (!c || c->g_V <= 0) return 0;
+  return (size_t)c->N * c->d * c->b_V / 8 + 4 * (size_t)c->N * (c->d / c->g_V);
+}
+
+size_t pnmix_score_workspace_bytes(const pnmix_cfg* c, int32_t B, int32_t P) {
+  if (check(c) != PNMIX_OK || B <= 0 || P <= 0) return 0;
+  return pnmix::score_workspace_bytes(*c, B, P);
+}
+
+int32_t pnmix_decode_splits(const pnmix_cfg* c, int32_t B, int32_t max_pages) {
+  if (check(c) != PNMIX_OK || B <= 0 || max_pages < 0) return 0;
+  return pnmix::decode_plan(*c, B, max_pages).splits;
+}
+
+size_t pnmix_decode_workspace_bytes(const pnmix_cfg* c, int32_t B, int32_t max_pages) {
+  if (check(c) != PNMIX_OK || B <= 0 || max_pages < 0) return 0;
+  return pnmix::decode_plan(*c, B, max_pages).ws_bytes;
+}
+
+const char* pnmix_last_error(void) { return g_err; }
+
+pnmix_status pnmix_score_prefill(const pnmix_cfg* c, int32_t B, int32_t P, const uint16_t* q,
+                                 const uint16_t* k, float* sigma, uint32_t* mask, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (B <= 0 || P <= 0) return fail(PNMIX_E_INVALID, "B = %d, P = %d must be positive", B, P);
+  if ((long long)B * (c->H_q + c->H_kv) > 65535)
+    return fail(PNMIX_E_UNSUPPORTED, "B * (H_q + H_kv) > 65535");
+  if (!q || !k || !mask || !ws) return fail(PNMIX_E_INVALID, "q, k, mask and ws must be non-NULL");
+  if (ws_bytes < pnmix::score_workspace_bytes(*c, B, P))
+    return fail(PNMIX_E_WORKSPACE, "score workspace %zu < %zu bytes", ws_bytes,
+                pnmix::score_workspace_bytes(*c, B, P));
+  return hip_status(pnmix::launch_score(*c, B, P, q, k, sigma, mask, ws, (hipStream_t)stream),
+                    "pnmix_score_prefill");
+}
+
+pnmix_status pnmix_quantize_k_page(const pnmix_cfg* c, int32_t n_pages, const pnmix_page* pages,
+                                   const uint32_t* mask, void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (n_pages < 0) return fail(PNMIX_E_INVALID, "n_pages = %d < 0", n_pages);
+  if (n_pages == 0) return ok();
+  if (!pages || !mask) return fail(PNMIX_E_INVALID, "pages and mask must be non-NULL");
+  return hip_status(pnmix::launch_quantize_k(*c, n_pages, pages, mask, (hipStream_t)stream),
+                    "pnmix_quantize_k_page");
+}
+
+pnmix_status pnmix_quantize_v_page(const pnmix_cfg* c, int32_t n_pages, const pnmix_page* pages,
+                                   void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (n_pages < 0) return fail(PNMIX_E_INVALID, "n_pages = %d < 0", n_pages);
+  if (n_pages == 0) return ok();
+  if (!pages) return fail(PNMIX_E_INVALID, "pages must be non-NULL");
+  return hip_status(pnmix::launch_quantize_v(*c, n_pages, pages, (hipStream_t)stream),
+                    "pnmix_quantize_v_page");
+}
+
+pnmix_status pnmix_decode_attn(const pnmix_cfg* c, int32_t B, int32_t max_pages,
+                               const uint16_t* q, const uint16_t* k_sink, const uint16_t* v_sink,
+                               const uint8_t* k_pages, const uint8_t* v_pages,
+                               const uint16_t* k_res, const uint16_t* v_res,
+                               const pnmix_seq_len* lens, const uint32_t* mask, float sm_scale,
+                               float* out, void* ws, size_t ws_bytes, void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (B <= 0 || max_pages < 0)
+    return fail(PNMIX_E_INVALID, "B = %d must be positive, max_pages = %d >= 0", B, max_pages);
+  if ((long long)B * c->H_kv > 65535) return fail(PNMIX_E_UNSUPPORTED, "B * H_kv > 65535");
+  if (!q || !k_res || !v_res || !lens || !mask || !out || !ws)
+    return fail(PNMIX_E_INVALID, "q, k_res, v_res, lens, mask, out and ws must be non-NULL");
+  if (c->N_s > 0 && (!k_sink || !v_sink))
+    return fail(PNMIX_E_INVALID, "k_sink and v_sink must be non-NULL when N_s > 0");
+  if (max_pages > 0 && (!k_pages || !v_pages))
+    return fail(PNMIX_E_INVALID, "k_pages and v_pages must be non-NULL when max_pages > 0");
+  if (!std::isfinite(sm_scale)) return fail(PNMIX_E_INVALID, "sm_scale is not finite");
+  const size_t need = pnmix::decode_plan(*c, B, max_pages).ws_bytes;
+  if (ws_bytes < need)
+    return fail(PNMIX_E_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(pnmix::launch_decode(*c, B, max_pages, q, k_sink, v_sink, k_pages, v_pages,
+                                         k_res, v_res, lens, mask, sm_scale, out, ws,
+                                         (hipStream_t)stream),
+                    "pnmix_decode_attn");
+}
+
+pnmix_status pnmix_append_kv(const pnmix_cfg* c, int32_t B, const uint16_t* k_new,
+                             const uint16_t* v_new, uint16_t* k_sink, uint16_t* v_sink,
+                             uint16_t* k_res, uint16_t* v_res, pnmix_seq_len* lens,
+                             void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (B <= 0) return fail(PNMIX_E_INVALID, "B = %d must be positive", B);
+  if (!k_new || !v_new || !k_res || !v_res || !lens)
+    return fail(PNMIX_E_INVALID, "k_new, v_new, k_res, v_res and lens must be non-NULL");
+  if (c->N_s > 0 && (!k_sink || !v_sink))
+    return fail(PNMIX_E_INVALID, "k_sink and v_sink must be non-NULL when N_s > 0");
+  return hip_status(pnmix::launch_append_kv(*c, B, k_new, v_new, k_sink, v_sink, k_res, v_res,
+                                            lens, (hipStream_t)stream),
+                    "pnmix_append_kv");
+}
+
+pnmix_status pnmix_commit_page(const pnmix_cfg* c, int32_t B, int32_t max_pages,
+                               pnmix_seq_len* lens, void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (B <= 0 || max_pages < 0 || !lens)
+    return fail(PNMIX_E_INVALID, "B > 0, max_pages >= 0 and lens non-NULL required");
+  return hip_status(pnmix::launch_commit_page(*c, B, max_pages, lens, (hipStream_t)stream),
+                    "pnmix_commit_page");
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// score.hip -- Eq. 6 prefill pair-norm saliency and the fixed pair mask on gfx950.
+//
+// "PN-Mix: Key-Cache Precision Allocation from RoPE Channel-Pair Norms", Core equations, Eq. 6:
+// sigma_{h,i} = (1/n_g) sum_{h' in g^-1(h)} E_t||q_{h',t,i}|| * E_s||k_{h,s,i}||, then the top
+// floor(r d/2) pairs of each KV head form a bit mask stored once (Korean summary page,
+// "무엇과 다른가": B x L x H_kv x d/2 bits).
+//
+// Two passes.  Pass 1 gives each (sequence, head, 64-token chunk) one wave; lane i owns RoPE
+// pair i and adds its pair norms over the chunk in ascending token order, reading one token row
+// per step (coalesced: adjacent pairs are one dword per lane, split-half pairs two halves).
+// Pass 2 gives each (sequence, KV head) one workgroup: its waves add the chunk sums of one head
+// each in ascending chunk order, divide by P, then wave 0 forms sigma, ranks the pairs through
+// LDS and writes the mask with a wave ballot.  The summation order is fixed, so sigma and the
+// mask are bit-identical to the reference oracle.
+#include "common.h"
+#include "kernels.h"
+
+namespace pnmix {
+
+constexpr int kChunk = 64;
+
+__global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          float* __restrict__ chunk_sums,
+                                                          int H_q, int H_kv, int d, int pairing,
+                                                          int P, int n_chunks) {
+  const int chunk = blockIdx.x;
+  const int seq_head = blockIdx.y;  // b * (H_q + H_kv) + head
+  const int H = H_q + H_kv;
+  const int b = seq_head / H;
+  const int head = seq_head % H;
+  const int np = d / 2;
+  const int i = threadIdx.x;
+  if (i >= np) return;
+  const uint16_t* src = head < H_q ? q + ((int64_t)b * H_q + head) * P * d
+                                   : k + ((int64_t)b * H_kv + (head - H_q)) * P * d;
+  const int c0 = pairing == PNMIX_PAIRS_ADJACENT ? 2 * i : i;
+  const int c1 = pairing == PNMIX_PAIRS_ADJACENT ? 2 * i + 1 : i + np;
+  const int t0 = chunk * kChunk;
+  const int t1 = min(t0 + kChunk, P);
+  float s = 0.0f;
+#pragma unroll 8
+  for (int t = t0; t < t1; ++t) {
+    const float x = h2f(src[(int64_t)t * d + c0]);
+    const float y = h2f(src[(int64_t)t * d + c1]);
+    const float a = x * x;
+    const float bb = y * y;
+    s = s + sqrtf(a + bb);
+  }
+  chunk_sums[((int64_t)seq_head * n_chunks + chunk) * np + i] = s;
+}
+
+__global__ void __launch_bounds__(256) score_select_kernel(const float* __restrict__ chunk_sums,
+                                                           float* __restrict__ sigma,
+                                                           uint32_t* __restrict__ mask, int H_q,
+                                                           int H_kv, int d, int P, int n_chunks,
+                                                           int n_hi, int words) {
+  __shared__ float means[17][64];  // n_g query heads (<= 16) then the KV head
+  __shared__ float sig[64];
+  const int seq = blockIdx.x / H_kv;
+  const int h = blockIdx.x % H_kv;
+  const int ng = H_q / H_kv;
+  const int np = d / 2;
+  const int H = H_q + H_kv;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  for (int r = wave; r <= ng; r += nwaves) {
+    const int head = r < ng ? h * ng + r : H_q + h;
+    if (lane < np) {
+      const float* cs = chunk_sums + ((int64_t)(seq * H + head) * n_chunks) * np + lane;
+      float s = 0.0f;
+      for (int c = 0; c < n_chunks; ++c) s = s + cs[(int64_t)c * np];
+      means[r][lane] = s / (float)P;
+    }
+  }
+  __syncthreads();
+  float sg = 0.0f;
+  if (wave == 0 && lane < np) {
+    float a = 0.0f;
+    for (int r = 0; r < ng; ++r) a = a + means[r][lane];
+    sg = (a / (float)ng) * means[ng][lane];
+    sig[lane] = sg;
+    if (sigma) sigma[((int64_t)seq * H_kv + h) * np + lane] = sg;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  int rank = 0;
+  if (lane < np) {
+    for (int j = 0; j < np; ++j) {
+      const float o = sig[j];
+      rank += (o > sg || (o == sg && j < lane)) ? 1 : 0;
+    }
+  }
+  const unsigned long long bits = __ballot(lane < np && rank < n_hi);
+  if (lane < words) {
+    mask[((int64_t)seq * H_kv + h) * words + lane] = (uint32_t)(bits >> (32 * lane));
+  }
+}
+
+hipError_t launch_score(const pnmix_cfg& c, int B, int P, const uint16_t* q, const uint16_t* k,
+                        float* sigma, uint32_t* mask, void* ws, hipStream_t stream) {
+  const int n_chunks = (P + kChunk - 1) / kChunk;
+  float* chunk_sums = static_cast<float*>(ws);
+  dim3 g1(n_chunks, B * (c.H_q + c.H_kv));
+  hipLaunchKernelGGL(score_chunks_kernel, g1, dim3(64), 0, stream, q, k, chunk_sums, c.H_q,
+                     c.H_kv, c.d, c.pairing, P, n_chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int words = (c.d / 2 + 31) / 32;
+  hipLaunchKernelGGL(score_select_kernel, dim3(B * c.H_kv), dim3(256), 0, stream, chunk_sums,
+                     sigma, mask, c.H_q, c.H_kv, c.d, P, n_chunks, c.n_hi_pairs, words);
+  return hipGetLastError();
+}
+
+size_t score_workspace_bytes(const pnmix_cfg& c, int B, int P) {
+  const size_t n_chunks = (size_t)(P + kChunk - 1) / kChunk;
+  const size_t bytes = (size_t)B * (c.H_q + c.H_kv) * n_chunks * (c.d / 2) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+}  // namespace pnmix

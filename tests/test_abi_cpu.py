@@ -1,0 +1,127 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every declared symbol,
+validates arguments on the host before any HIP call, and reports a missing device as
+PNMIX_E_HIP (no CPU fallback)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_pnmix_amd as P
+from decode_attention_pnmix_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pnmix.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pnmix_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = P.lib()
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTED)
+
+
+def _cfg(**kw):
+    base = dict(H_q=32, H_kv=8, d=128, pairing=1, n_hi_pairs=32, G=128, b_H=3, b_L=1, b_V=2,
+                g_V=32, N_s=32, N=128)
+    base.update(kw)
+    return L.pnmix_cfg(*[base[n] for n, _ in L.pnmix_cfg._fields_])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, L.PNMIX_OK),
+    ({"H_q": 30}, L.PNMIX_E_INVALID),
+    ({"H_q": 8 * 17}, L.PNMIX_E_UNSUPPORTED),
+    ({"d": 96}, L.PNMIX_E_UNSUPPORTED),
+    ({"d": 33}, L.PNMIX_E_INVALID),
+    ({"pairing": 2}, L.PNMIX_E_INVALID),
+    ({"n_hi_pairs": 65}, L.PNMIX_E_INVALID),
+    ({"n_hi_pairs": -1}, L.PNMIX_E_INVALID),
+    ({"G": 48}, L.PNMIX_E_INVALID),
+    ({"G": 16}, L.PNMIX_E_UNSUPPORTED),
+    ({"b_H": 4, "b_L": 2}, L.PNMIX_E_UNSUPPORTED),
+    ({"b_V": 4}, L.PNMIX_E_UNSUPPORTED),
+    ({"g_V": 24}, L.PNMIX_E_INVALID),
+    ({"N": 64}, L.PNMIX_E_UNSUPPORTED),
+    ({"N_s": -1}, L.PNMIX_E_INVALID),
+    ({"d": 32, "g_V": 32, "n_hi_pairs": 8, "pairing": 0, "H_q": 4, "H_kv": 2}, L.PNMIX_OK),
+])
+def test_check_cfg(kw, status):
+    st = P.lib().pnmix_check_cfg(ctypes.byref(_cfg(**kw)))
+    assert st == status, P.pnmix_last_error()
+    if status != L.PNMIX_OK:
+        assert P.pnmix_last_error()
+
+
+def test_sizes_match_the_oracle(orc):
+    for d, r, G, g_V in ((128, 0.5, 128, 32), (128, 0.4, 64, 32), (32, 0.5, 128, 32),
+                         (64, 0.25, 32, 16)):
+        n_hi = P.pnmix_hi_pairs(r, d)
+        assert n_hi == orc.hi_pairs(r, d)
+        c = _cfg(d=d, n_hi_pairs=n_hi, G=G, g_V=g_V)
+        oc = orc.Cfg(32, 8, d, 1, n_hi, G=G, g_V=g_V)
+        assert P.pnmix_k_page_bytes(c) == orc.k_page_bytes(oc)
+        assert P.pnmix_v_page_bytes(c) == orc.v_page_bytes(oc)
+        assert P.pnmix_mask_words(c) == orc.mask_words(oc)
+    assert P.pnmix_hi_pairs(0.4, 128) == 25
+    assert P.pnmix_hi_pairs(0.0, 128) == 0 and P.pnmix_hi_pairs(1.0, 128) == 64
+
+
+def test_decode_plan_queries():
+    c = _cfg()
+    for B, mp in ((1, 255), (32, 63), (110, 63), (1, 0), (4, 3)):
+        s = P.pnmix_decode_splits(c, B, mp)
+        assert 1 <= s <= mp + 2
+        assert P.pnmix_decode_workspace_bytes(c, B, mp) >= B * 8 * s * 4 * (128 + 2) * 4
+    assert P.pnmix_decode_splits(_cfg(G=48), 1, 10) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)
+
+
+def test_validation_before_launch():
+    lib = P.lib()
+    c = _cfg()
+    ws = P.pnmix_score_workspace_bytes(c, 2, 141)
+    assert ws > 0 and ws % 256 == 0
+    # null inputs
+    assert lib.pnmix_score_prefill(ctypes.byref(c), 2, 141, None, FAKE, None, FAKE, FAKE, ws,
+                                   None) == L.PNMIX_E_INVALID
+    # workspace too small
+    assert lib.pnmix_score_prefill(ctypes.byref(c), 2, 141, FAKE, FAKE, None, FAKE, FAKE, ws - 1,
+                                   None) == L.PNMIX_E_WORKSPACE
+    assert lib.pnmix_score_prefill(ctypes.byref(c), 0, 141, FAKE, FAKE, None, FAKE, FAKE, ws,
+                                   None) == L.PNMIX_E_INVALID
+    assert lib.pnmix_quantize_k_page(ctypes.byref(c), 4, None, FAKE, None) == L.PNMIX_E_INVALID
+    assert lib.pnmix_quantize_k_page(ctypes.byref(c), -1, FAKE, FAKE, None) == L.PNMIX_E_INVALID
+    assert lib.pnmix_quantize_v_page(ctypes.byref(c), 0, None, None) == L.PNMIX_OK
+    dws = P.pnmix_decode_workspace_bytes(c, 4, 10)
+    args = [FAKE] * 9
+    assert lib.pnmix_decode_attn(ctypes.byref(c), 4, 10, *args, ctypes.c_float(0.088), FAKE,
+                                 FAKE, dws - 1, None) == L.PNMIX_E_WORKSPACE
+    assert lib.pnmix_decode_attn(ctypes.byref(c), 4, 10, *args, ctypes.c_float(float("nan")),
+                                 FAKE, FAKE, dws, None) == L.PNMIX_E_INVALID
+    assert lib.pnmix_decode_attn(ctypes.byref(c), 4, 10, None, *args[1:],
+                                 ctypes.c_float(0.088), FAKE, FAKE, dws,
+                                 None) == L.PNMIX_E_INVALID
+    assert lib.pnmix_decode_attn(ctypes.byref(_cfg(b_V=3)), 4, 10, *args, ctypes.c_float(0.1),
+                                 FAKE, FAKE, dws, None) == L.PNMIX_E_UNSUPPORTED
+
+
+def test_no_device_is_an_error_not_a_fallback():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = P.lib()
+    c = _cfg()
+    ws = P.pnmix_score_workspace_bytes(c, 1, 141)
+    st = lib.pnmix_score_prefill(ctypes.byref(c), 1, 141, FAKE, FAKE, None, FAKE, FAKE, ws, None)
+    assert st == L.PNMIX_E_HIP
+    assert "HIP error" in P.pnmix_last_error()

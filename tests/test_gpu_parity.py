@@ -1,0 +1,346 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: sigma, the pair mask, packed K and V pages (codes and fp16 metadata).
+Within max-abs 2e-3 of the float64 oracle: decode attention outputs.
+Every workload runs at its full per-layer shape in the launch configuration the benchmark
+times; large ones are compared on sampled sequences.  Edge cases: ragged lengths, empty
+sequences, full residual buffers, constant / signed-zero / extreme / subnormal groups.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_pnmix_amd as P
+import oracle
+import synth
+from _cases import cfgs, fill_cache_bulk, layer_inputs, oracle_decode, say, sm_scale, u16
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build(force=False)
+    P.lib()
+
+
+# ------------------------------------------------------------------------------- score (Eq. 6)
+
+def _score_case(w, layer, B, P_):
+    lc, oc = cfgs(w)
+    say(f"[score] {w.name} layer={layer} B={B} P={P_}")
+    qp, k, _, _ = layer_inputs(w, layer, B, P_, P_)
+    sigma, mask = P.pnmix_score_prefill(lc, qp, k)
+    torch.cuda.synchronize()
+    qh, kh = u16(qp), u16(k)
+    sig_g = sigma.cpu().numpy()
+    mask_g = mask.cpu().numpy().view(np.uint32)
+
+    def one(b):
+        _, _, s, m = oracle.score_prefill(oc, qh[b], kh[b])
+        return s, m
+
+    res = oracle.parallel_map(one, range(B))
+    for b, (s, m) in enumerate(res):
+        assert np.array_equal(sig_g[b].view(np.uint32), s.view(np.uint32)), f"sigma b={b}"
+        assert np.array_equal(mask_g[b], m), f"mask b={b}"
+        assert all(sum(bin(int(x)).count("1") for x in m[h]) == w.n_hi_pairs
+                   for h in range(w.H_kv))
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_score_parity(name):
+    w = synth.WORKLOADS[name]
+    _score_case(w, 0, w.B, w.P)
+
+
+def test_score_parity_long_prefill():
+    w = synth.WORKLOADS["llama3.1-8b-32L-b110-8k"]
+    _score_case(w, 1, 1, w.prefill_score_P)
+
+
+def test_score_ragged_chunks_and_tiny_P():
+    w = synth.WORKLOADS["qwen3-8b-1L-32k"]
+    for P_ in (1, 63, 64, 65, 200):
+        _score_case(w, 2, 3, P_)
+
+
+def test_pair_norm_bits_through_score():
+    """P = 1 and keys (1, 0) in every pair: sigma = ||q pair|| exactly; random finite fp16 bits
+    exercise the fp32 square root and the pair-norm arithmetic bit for bit."""
+    d, H = 128, 16
+    lc = P.make_cfg(H, H, d, 1, 32)
+    oc = oracle.Cfg(H, H, d, 1, 32)
+    g = torch.Generator().manual_seed(1)
+    B = 512
+    bits = torch.randint(0, 1 << 16, (B, H, 1, d), generator=g, dtype=torch.int32)
+    bits = torch.where((bits & 0x7C00) == 0x7C00, bits & 0x83FF, bits)  # finite only
+    q = bits.to(torch.int16).cuda()
+    k = torch.zeros(B, H, 1, d, dtype=torch.float16)
+    k[..., :d // 2] = 1.0
+    k = k.cuda()
+    sigma, _ = P.pnmix_score_prefill(lc, q.view(torch.float16), k)
+    torch.cuda.synchronize()
+    qh = q.cpu().numpy().view(np.uint16)
+    ref = oracle.pair_norm(qh[..., 0, :d // 2], qh[..., 0, d // 2:])
+    assert np.array_equal(sigma.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# -------------------------------------------------------------------------- page quantization
+
+def _quant_compare(w, lc, oc, src_gpu, mask_rows_gpu, sample, label):
+    """Quantize every page of src [n][N][d] on the GPU; compare `sample` pages with the oracle."""
+    n = src_gpu.shape[0]
+    kpb, vpb = P.pnmix_k_page_bytes(lc), P.pnmix_v_page_bytes(lc)
+    kd = torch.zeros(n, kpb, dtype=torch.uint8, device="cuda")
+    vd = torch.zeros(n, vpb, dtype=torch.uint8, device="cuda")
+    es = src_gpu.element_size()
+    srcs = [src_gpu.data_ptr() + i * w.N * w.d * es for i in range(n)]
+    kj = P.page_jobs(srcs, w.d, [kd.data_ptr() + i * kpb for i in range(n)], range(n), "cuda")
+    vj = P.page_jobs(srcs, w.d, [vd.data_ptr() + i * vpb for i in range(n)], range(n), "cuda")
+    P.pnmix_quantize_k_page(lc, kj, mask_rows_gpu)
+    P.pnmix_quantize_v_page(lc, vj)
+    torch.cuda.synchronize()
+    sh = u16(src_gpu[sample])
+    mh = mask_rows_gpu[sample].cpu().numpy().view(np.uint32)
+    kg = kd[sample].cpu().numpy()
+    vg = vd[sample].cpu().numpy()
+
+    def one(i):
+        return (oracle.quantize_k_page(oc, sh[i], mh[i]), oracle.quantize_v_page(oc, sh[i]))
+
+    res = oracle.parallel_map(one, range(len(sample)))
+    for i, (ko, vo) in enumerate(res):
+        assert np.array_equal(kg[i], ko), f"{label}: K page {sample[i]} differs"
+        assert np.array_equal(vg[i], vo), f"{label}: V page {sample[i]} differs"
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_quant_parity(name):
+    w = synth.WORKLOADS[name]
+    lc, oc = cfgs(w)
+    B = w.B
+    T = w.T if w.B * w.H_kv * w.T <= 32 * 8 * 32768 else 8192
+    say(f"[quant] {name} B={B} T={T}")
+    qp, k, v, _ = layer_inputs(w, 3, B, T)
+    _, mask = P.pnmix_score_prefill(lc, qp, k[:, :, :w.P].contiguous())
+    n_pages = (T - w.N_s) // w.N
+    # pages of keys and of values: [B][H_kv][n_pages][N][d]
+    kp = k[:, :, w.N_s:w.N_s + n_pages * w.N].reshape(B, w.H_kv, n_pages, w.N, w.d)
+    vp = v[:, :, w.N_s:w.N_s + n_pages * w.N].reshape(B, w.H_kv, n_pages, w.N, w.d)
+    rows = mask.reshape(B * w.H_kv, -1)
+    mrow = rows.repeat_interleave(n_pages, dim=0).contiguous()
+    n = B * w.H_kv * n_pages
+    rng = np.random.default_rng(0)
+    sample = np.unique(np.concatenate([[0, n - 1], rng.choice(n, min(n, 192), replace=False)]))
+    _quant_compare(w, lc, oc, kp.reshape(n, w.N, w.d).contiguous(), mrow, sample, name + "/K")
+    # value pages go through the same jobs with the value tokens
+    _quant_compare(w, lc, oc, vp.reshape(n, w.N, w.d).contiguous(), mrow, sample, name + "/V")
+
+
+@pytest.mark.parametrize("G,d,pairing,r", [(128, 128, 1, 0.5), (64, 128, 1, 0.4),
+                                           (32, 64, 0, 0.25), (128, 32, 0, 1.0),
+                                           (64, 128, 0, 0.0)])
+def test_quant_adversarial_pages(G, d, pairing, r):
+    """Constant channels and groups, signed zeros, +-65504, subnormals, exact midpoints and
+    random finite bit patterns."""
+    w = synth.Workload("adv", 1, 1, 8, 2, d, pairing, 1e4, 64, 512, r, G)
+    lc, oc = cfgs(w)
+    say(f"[quant-adv] G={G} d={d} pairing={pairing} r={r}")
+    g = torch.Generator().manual_seed(G + d)
+    n = 96
+    x = torch.randn(n, 128, d, generator=g) * torch.exp(torch.randn(n, 1, d, generator=g) * 2)
+    x[0] = 1.25                                   # constant page
+    x[1, :, 0] = -0.0
+    x[1, 64:, 0] = 0.0                            # {-0, +0} group
+    x[2, :, 1] = 65504.0
+    x[2, 7, 1] = -65504.0                         # full fp16 range
+    x[3] = x[3] * 1e-7                            # subnormal fp16 values
+    x[4, :, :] = torch.arange(128).view(128, 1).float() % 8  # exact 3-bit levels
+    x[5, :, :] = (torch.arange(128).view(128, 1) % 3).float() * 0.5  # 1-bit midpoints
+    x[6, :, : d // 2] = 3.0                       # half of the channels constant
+    x[7, ::2] = x[7, 0]                           # tied values
+    xh = x.to(torch.float16)
+    bits = torch.randint(0, 1 << 16, (8, 128, d), generator=g, dtype=torch.int32)
+    bits = torch.where((bits & 0x7C00) == 0x7C00, bits & 0x83FF, bits)
+    xh[8:16] = bits.to(torch.int16).view(torch.float16)
+    src = xh.cuda().contiguous()
+    words = P.pnmix_mask_words(lc)
+    nh = w.n_hi_pairs
+    masks = torch.zeros(n, words, dtype=torch.int64)
+    for i in range(n):
+        sel = torch.randperm(d // 2, generator=g)[:nh]
+        for p in sel.tolist():
+            masks[i, p // 32] |= 1 << (p % 32)
+    masks = masks.to(torch.int32).cuda()
+    _quant_compare(w, lc, oc, src, masks.contiguous(), np.arange(n), "adversarial")
+
+
+# ----------------------------------------------------------------------------- decode attention
+
+DECODE_CASES = {
+    "tiny": (None, 1),
+    "qwen3-8b-1L-32k": (None, 1),
+    "qwen3-8b-36L-b32-8k": (None, 4),
+    "llama3.1-8b-32L-b110-8k": (None, 4),
+    "qwen3-32b-64L-b32-32k": (None, 2),
+}
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_decode_parity(name):
+    w = synth.WORKLOADS[name]
+    lc, oc = cfgs(w)
+    _, n_sample = DECODE_CASES[name]
+    T = w.T
+    say(f"[decode] {name} B={w.B} T={T}")
+    qp, k, v, qd = layer_inputs(w, 5, w.B, T)
+    cache = fill_cache_bulk(w, lc, qp, k, v, T)
+    out = cache.attend(qd)
+    torch.cuda.synchronize()
+    out_h = out.cpu().numpy()
+    mask_g = cache.mask.cpu().numpy().view(np.uint32)
+    rng = np.random.default_rng(1)
+    picks = sorted(set([0, w.B - 1] + rng.choice(w.B, n_sample, replace=False).tolist()))
+    picks = picks[: max(n_sample, 1) + 1]
+    for b in picks:
+        ref = oracle_decode(w, oc, u16(qp[b]), u16(k[b]), u16(v[b]), u16(qd[b]), T,
+                            sm_scale(w.d))
+        # the oracle's own mask equals the library's (checked bit-exactly in the score tests)
+        err = np.abs(out_h[b] - ref).max()
+        say(f"   b={b} max|err|={err:.3e}")
+        assert err <= ATOL, (name, b, err)
+    del cache, k, v
+
+
+def test_decode_ragged_lengths_and_edges():
+    """Per-sequence lengths in one batch: empty, sinks only, partial sinks, residual only, full
+    residual (N rows), pages with and without residual, n_pages = max_pages."""
+    w = synth.Workload("ragged", 1, 1, 8, 2, 64, 1, 1e4, 64, 1024, 0.5, 64, g_V=16)
+    lc, oc = cfgs(w)
+    max_pages = 7
+    lens_list = [(0, 0, 0), (5, 0, 0), (32, 0, 0), (32, 0, 77), (32, 0, 128), (32, 1, 0),
+                 (32, 3, 1), (32, 7, 128), (32, 7, 0), (32, 2, 64)]
+    B = len(lens_list)
+    Tmax = 32 + max_pages * 128 + 128
+    say(f"[decode-ragged] B={B}")
+    qp, k, v, qd = layer_inputs(w, 0, B, Tmax, 64)
+    kpb, vpb = P.pnmix_k_page_bytes(lc), P.pnmix_v_page_bytes(lc)
+    _, mask = P.pnmix_score_prefill(lc, qp, k[:, :, :64].contiguous())
+    k_sink = torch.zeros(B, 2, 32, 64, dtype=torch.float16, device="cuda")
+    v_sink = torch.zeros_like(k_sink)
+    k_res = torch.zeros(B, 2, 128, 64, dtype=torch.float16, device="cuda")
+    v_res = torch.zeros_like(k_res)
+    k_pages = torch.zeros(B, 2, max_pages, kpb, dtype=torch.uint8, device="cuda")
+    v_pages = torch.zeros(B, 2, max_pages, vpb, dtype=torch.uint8, device="cuda")
+    lens = torch.zeros(B, 4, dtype=torch.int32)
+    srcs, kd, vd, rows, vsrcs = [], [], [], [], []
+    for b, (s, npg, r) in enumerate(lens_list):
+        lens[b, :3] = torch.tensor([s, npg, r])
+        k_sink[b, :, :s] = k[b, :, :s]
+        v_sink[b, :, :s] = v[b, :, :s]
+        for h in range(2):
+            for p in range(npg):
+                off = ((b * 2 + h) * Tmax + 32 + p * 128) * 64 * 2
+                srcs.append(k.data_ptr() + off)
+                vsrcs.append(v.data_ptr() + off)
+                kd.append(k_pages.data_ptr() + ((b * 2 + h) * max_pages + p) * kpb)
+                vd.append(v_pages.data_ptr() + ((b * 2 + h) * max_pages + p) * vpb)
+                rows.append(b * 2 + h)
+        a = 32 + npg * 128
+        k_res[b, :, :r] = k[b, :, a:a + r]
+        v_res[b, :, :r] = v[b, :, a:a + r]
+    P.pnmix_quantize_k_page(lc, P.page_jobs(srcs, 64, kd, rows, "cuda"), mask)
+    P.pnmix_quantize_v_page(lc, P.page_jobs(vsrcs, 64, vd, rows, "cuda"))
+    out = P.pnmix_decode_attn(lc, qd, k_sink, v_sink, k_pages, v_pages, k_res, v_res,
+                              lens.cuda(), mask, sm_scale(64))
+    torch.cuda.synchronize()
+    out_h = out.cpu().numpy()
+    mask_h = mask.cpu().numpy().view(np.uint32)
+    kh, vh = u16(k), u16(v)
+    for b, (s, npg, r) in enumerate(lens_list):
+        if s + npg + r == 0:
+            assert np.all(out_h[b] == 0)
+            continue
+        # the oracle places the same token ranges itself
+        kp = np.zeros((2, max_pages, kpb), np.uint8)
+        vp = np.zeros((2, max_pages, vpb), np.uint8)
+        for h in range(2):
+            for p in range(npg):
+                a = 32 + p * 128
+                kp[h, p] = oracle.quantize_k_page(oc, kh[b, h, a:a + 128], mask_h[b, h])
+                vp[h, p] = oracle.quantize_v_page(oc, vh[b, h, a:a + 128])
+        ks = np.zeros((2, 32, 64), np.uint16)
+        vs = np.zeros_like(ks)
+        ks[:, :s] = kh[b, :, :s]
+        vs[:, :s] = vh[b, :, :s]
+        a = 32 + npg * 128
+        kr = np.zeros((2, 128, 64), np.uint16)
+        vr = np.zeros_like(kr)
+        kr[:, :r] = kh[b, :, a:a + r]
+        vr[:, :r] = vh[b, :, a:a + r]
+        ref = oracle.decode_attn_f64(oc, u16(qd[b]), ks, vs, kp, vp, kr, vr, mask_h[b], s, npg,
+                                     r, sm_scale(64))
+        err = np.abs(out_h[b] - ref).max()
+        assert err <= ATOL, (lens_list[b], err)
+
+
+def test_decode_split_count_does_not_change_results():
+    """The same sequence alone (many splits) and inside a batch of 64 (fewer splits)."""
+    w = synth.WORKLOADS["qwen3-8b-1L-32k"]
+    lc, _ = cfgs(w)
+    T = 4096 + 32 + 50
+    qp, k, v, qd = layer_inputs(w, 7, 1, T)
+    c1 = fill_cache_bulk(w, lc, qp, k, v, T)
+    o1 = c1.attend(qd)
+    B = 64
+    c2 = fill_cache_bulk(w, lc, qp.expand(B, -1, -1, -1).contiguous(),
+                         k.expand(B, -1, -1, -1).contiguous(),
+                         v.expand(B, -1, -1, -1).contiguous(), T)
+    o2 = c2.attend(qd.expand(B, -1, -1).contiguous())
+    torch.cuda.synchronize()
+    n1 = P.pnmix_decode_splits(lc, 1, c1.max_pages)
+    n2 = P.pnmix_decode_splits(lc, B, c2.max_pages)
+    assert n1 != n2
+    assert torch.equal(c1.k_pages[0], c2.k_pages[B - 1])
+    assert (o2 - o1).abs().max().item() <= 1e-5
+
+
+# ------------------------------------------------------------------------ online vs bulk fill
+
+def test_online_fill_equals_bulk_fill():
+    """Prefill P = 64, then one decode step at a time up to 512 cached tokens (attend, then
+    quantize when the residual buffer is full): every packed page equals bulk quantization of
+    the same tokens, and outputs match the oracle along the way."""
+    w = synth.WORKLOADS["tiny"]
+    lc, oc = cfgs(w)
+    T = w.T
+    qp, k, v, _ = layer_inputs(w, 0, 1, T)
+    npairs = w.d // 2
+    sq = synth.pair_scales(w.H_q, npairs, w.sigma_ln, "cuda", w.name, 0, "q")
+    c = P.PNMixLayerCache(lc, 1, 4)
+    c.prefill(qp, k[:, :, :w.P].contiguous(), v[:, :, :w.P].contiguous())
+    assert c.n_score_calls == 1
+    mask0 = c.mask.clone()
+    checks = {w.P + 1, 159, 160, 161, 288, 289, T}
+    for t in range(w.P, T):
+        qt = synth.rope_tokens(sq, 1, torch.tensor([t], device="cuda"), w.d, w.pairing,
+                               w.rope_base, "cuda", w.name, 0, "qstep", t)[:, :, 0].contiguous()
+        o = c.step(qt, k[:, :, t].contiguous(), v[:, :, t].contiguous())
+        if t + 1 in checks:
+            torch.cuda.synchronize()
+            ref = oracle_decode(w, oc, u16(qp[0]), u16(k[0]), u16(v[0]), u16(qt[0]), t + 1,
+                                sm_scale(w.d))
+            assert np.abs(o[0].cpu().numpy() - ref).max() <= ATOL, t
+    assert c.n_score_calls == 1 and torch.equal(c.mask, mask0)  # mask fixed after prefill
+    bulk = fill_cache_bulk(w, lc, qp, k, v, T, max_pages=4)
+    torch.cuda.synchronize()
+    assert (c.sink_len, c.n_pages, c.res_len) == (bulk.sink_len, bulk.n_pages, bulk.res_len)
+    assert torch.equal(c.k_pages[:, :, :c.n_pages], bulk.k_pages[:, :, :bulk.n_pages])
+    assert torch.equal(c.v_pages[:, :, :c.n_pages], bulk.v_pages[:, :, :bulk.n_pages])
+    assert torch.equal(c.k_sink, bulk.k_sink)
+    assert torch.equal(c.k_res[:, :, :c.res_len], bulk.k_res[:, :, :bulk.res_len])

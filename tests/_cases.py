@@ -76,13 +76,24 @@ def fill_cache_bulk(w, lc, qp, k, v, T, max_pages=None):
     return c
 
 
-def oracle_decode(w, oc, qp_b, k_b, v_b, qd_b, T, sm_scale, mask_b=None, threads=None):
+def placement(w, T, online=False):
+    """(sink_len, n_pages, res_len) of a cache holding T tokens.  Bulk placement packs every
+    full page (residual 0..N-1 rows); the online policy attends before it quantizes, so in the
+    step that fills the residual buffer attention sees N fp16 residual rows (1..N rows)."""
+    s = min(T, w.N_s)
+    if T <= w.N_s:
+        return s, 0, 0
+    n_pages = (T - s - 1) // w.N if online else (T - s) // w.N
+    return s, n_pages, T - s - n_pages * w.N
+
+
+def oracle_decode(w, oc, qp_b, k_b, v_b, qd_b, T, sm_scale, mask_b=None, threads=None,
+                  online=False):
     """Oracle output [H_q][d] for one sequence from its fp16 inputs (host numpy uint16):
     its own score -> mask, its own page quantization, float64 attention."""
     if mask_b is None:
         _, _, _, mask_b = oracle.score_prefill(oc, qp_b, k_b[:, :qp_b.shape[1]])
-    s = min(T, w.N_s)
-    n_pages = (T - w.N_s) // w.N if T >= w.N_s else 0
+    s, n_pages, _ = placement(w, T, online)
     mp = max(n_pages, 1)
     kp = np.zeros((w.H_kv, mp, oracle.k_page_bytes(oc)), np.uint8)
     vp = np.zeros((w.H_kv, mp, oracle.v_page_bytes(oc)), np.uint8)
@@ -101,6 +112,7 @@ def oracle_decode(w, oc, qp_b, k_b, v_b, qd_b, T, sm_scale, mask_b=None, threads
     vs[:, :s] = v_b[:, :s]
     a = s + n_pages * w.N
     rest = T - a
+    assert 0 <= rest <= w.N
     kr = np.zeros((w.H_kv, w.N, w.d), np.uint16)
     vr = np.zeros_like(kr)
     kr[:, :rest] = k_b[:, a:T]

@@ -334,8 +334,8 @@ def test_online_fill_equals_bulk_fill():
         if t + 1 in checks:
             torch.cuda.synchronize()
             ref = oracle_decode(w, oc, u16(qp[0]), u16(k[0]), u16(v[0]), u16(qt[0]), t + 1,
-                                sm_scale(w.d))
-            assert np.abs(o[0].cpu().numpy() - ref).max() <= ATOL, t
+                                sm_scale(w.d), online=True)
+            assert np.abs(o[0].cpu().numpy() - ref).max() <= ATOL, t + 1
     assert c.n_score_calls == 1 and torch.equal(c.mask, mask0)  # mask fixed after prefill
     bulk = fill_cache_bulk(w, lc, qp, k, v, T, max_pages=4)
     torch.cuda.synchronize()

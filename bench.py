@@ -1,18 +1,21 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the PN-Mix key-cache path on one MI355X.
 
-One step = one generation step of every layer of the batch through the library: place the new
-key/value rows (pnmix_append_kv), decode attention over sinks + packed pages + fp16 residual
+One step = one generation step of every layer through the library: place the new key/value
+rows (pnmix_append_kv), decode attention over sinks + packed pages + fp16 residual
 (pnmix_decode_attn), and -- whenever a residual buffer reaches N tokens -- quantize it into a
 page (pnmix_quantize_k_page / pnmix_quantize_v_page, pnmix_commit_page).  The caches are built
 before timing from seeded synthetic inputs (prefill score of the first P tokens, bulk page
-quantization); W warm-up steps run untimed, then K steps are timed between device
-synchronisations.
+quantization); W warm-up steps run eagerly, then the K timed steps are captured once in a HIP
+graph and replayed between device synchronisations, so host launch overhead stays out of the
+timed region.  A workload with fewer than `--min-layers` layers is run over that many distinct
+copies of its layer (different seeds), so that the caches touched per step exceed the on-die
+last-level cache and every step reads HBM.
 
 Prints ONE JSON line: throughput in KV token-heads per second (sum over steps and layers of
-B * cached tokens * H_kv / elapsed), the decode kernel's roofline (algorithmic bytes per call /
-event-timed duration), page-quantization and prefill-score sub-measurements, and the CPU
-oracle timed on a bounded sample of the same workload.
+B * cached tokens * H_kv / elapsed), the decode call's roofline (algorithmic bytes per call /
+event-timed duration of the call), page-quantization and prefill-score sub-measurements, and
+the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -24,22 +27,21 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "qwen3-8b-1L-32k"
 
 
 def _say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes(cfg, lens_list, kpb, vpb):
+def decode_bytes(cfg, lens, B, kpb, vpb):
     """Algorithmic bytes of one decode call: packed pages, fp16 sink/residual rows, mask,
-    queries and fp32 outputs, summed over (sequence, KV head)."""
+    queries and fp32 outputs, over the B sequences and their KV heads."""
+    s, n_p, r = lens
     ng = cfg.H_q // cfg.H_kv
     words = (cfg.d // 2 + 31) // 32
-    tot = 0
-    for (s, n_p, r) in lens_list:
-        per_head = n_p * (kpb + vpb) + (s + r) * cfg.d * 2 * 2 + words * 4 + ng * cfg.d * 6
-        tot += per_head * cfg.H_kv + 16
-    return tot
+    per_head = n_p * (kpb + vpb) + (s + r) * cfg.d * 2 * 2 + words * 4 + ng * cfg.d * (2 + 4)
+    return B * (per_head * cfg.H_kv + 16)
 
 
 def build_layer(w, cfg, layer, B, T0, max_pages, steps, dev, P, synth, torch):
@@ -123,24 +125,27 @@ def cpu_baseline(w, sample, seconds, threads):
     work = sum(oracle.parallel_map(run, range(n_items), threads))
     el = time.perf_counter() - t0
     return {"value": work / el, "unit": "KV token-heads/s", "cores": threads, "kind": "oracle",
-            "sample": (f"float64 decode attention of {n_items} sequence-layers drawn from "
-                       f"{len(prepared)} sampled sequences of layer 0 (T={sample[0][4]}, "
-                       f"{w.H_kv} KV heads, {w.H_q} query heads), {el:.1f} s wall on "
-                       f"{threads} threads; page quantization excluded")}
+            "sample": (f"float64 decode attention (the oracle's dequantize-then-softmax) of "
+                       f"{n_items} sequence-layers drawn from {len(prepared)} sampled sequences "
+                       f"(T={sample[0][4]}, {w.H_kv} KV heads, {w.H_q} query heads), "
+                       f"{el:.1f} s wall on {threads} threads; page quantization excluded")}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128)
-    ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="qwen3-8b-36L-b32-8k")
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--min-layers", type=int, default=16,
+                    help="run a workload with fewer layers over this many distinct layer copies")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roofline-reps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence / KV head with no exchange; see DESIGN.md)",
+              "(the path shards by sequence and KV head with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -159,16 +164,17 @@ def main():
                      N_s=w.N_s, N=w.N)
     kpb, vpb = P.pnmix_k_page_bytes(cfg), P.pnmix_v_page_bytes(cfg)
     W, K = args.warmup, args.steps
+    layers = max(w.layers, args.min_layers)
     # the first timed step attends over exactly w.T tokens
     T0 = w.T - W - 1
     max_pages = (T0 + W + K - w.N_s) // w.N + 1
-    _say(f"[bench] workload={w.name} layers={w.layers} B={w.B} T0={T0} steps={K} warmup={W}")
+    _say(f"[bench] workload={w.name} layers={w.layers} (run over {layers}) B={w.B} T0={T0} "
+         f"steps={K} warmup={W} max_pages={max_pages}")
 
-    caches, inputs = [], []
-    sample = []
+    caches, inputs, sample = [], [], []
     n_sample = 4
     t_build = time.perf_counter()
-    for layer in range(w.layers):
+    for layer in range(layers):
         c, qst, kst, vst, raw = build_layer(w, cfg, layer, w.B, T0, max_pages, W + K, dev, P,
                                             synth, torch)
         caches.append(c)
@@ -180,55 +186,81 @@ def main():
                 sample.append((u16(qp[b]), u16(k[b, :, :T0]), u16(v[b, :, :T0]),
                                u16(qs[b, :, 0]), T0))
         del raw
-        for s in range(max_pages):  # page jobs of every flush slot, built before timing
-            if s >= c.n_pages:
-                c.flush_jobs(s)
+        for s in range(c.n_pages, max_pages):  # page jobs of every flush slot, built up front
+            c.flush_jobs(s)
     torch.cuda.synchronize()
     _say(f"[bench] caches built in {time.perf_counter() - t_build:.1f} s")
 
-    outs = [torch.empty(w.B, w.H_q, w.d, dtype=torch.float32, device=dev)
-            for _ in range(w.layers)]
+    outs = [torch.empty(w.B, w.H_q, w.d, dtype=torch.float32, device=dev) for _ in caches]
 
-    def run_step(i, events=None, lens_log=None):
+    def run_step(i, lens_log=None):
         for layer, c in enumerate(caches):
             qst, kst, vst = inputs[layer]
             c.append(kst[i], vst[i])
-            if lens_log is not None:
+            if lens_log is not None and layer == 0:
                 lens_log.append((c.sink_len, c.n_pages, c.res_len))
-            if events is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                c.attend(qst[i], outs[layer])
-                e1.record()
-                events.append((e0, e1))
-            else:
-                c.attend(qst[i], outs[layer])
+            c.attend(qst[i], outs[layer])
             c.flush()
 
     for i in range(W):
         run_step(i)
     torch.cuda.synchronize()
 
-    events, lens_log = [], []
+    # ---- capture the K timed steps once, then replay them from the same starting state
+    saved_lens = [c.lens.clone() for c in caches]
+    saved_host = [(c.sink_len, c.n_pages, c.res_len) for c in caches]
+    lens_log = []
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(W, W + K):
+            run_step(i, lens_log)
+
+    def restore():
+        for c, sl, sh in zip(caches, saved_lens, saved_host):
+            c.lens.copy_(sl)
+            c.sink_len, c.n_pages, c.res_len = sh
+        torch.cuda.synchronize()
+
+    restore()
+    graph.replay()  # untimed pass over the captured steps
+    restore()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(W, W + K):
-        run_step(i, events, lens_log)
+    graph.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-
-    tokheads = sum(w.B * (s + n_p * w.N + r) * w.H_kv for (s, n_p, r) in lens_log)
+    tokheads = sum(layers * w.B * (s + n_p * w.N + r) * w.H_kv for (s, n_p, r) in lens_log)
     value = tokheads / elapsed
-    durs = [a.elapsed_time(b) * 1e-3 for a, b in events]
-    bytes_calls = [decode_bytes(cfg, [ln] * w.B, kpb, vpb) for ln in lens_log]
-    dec_time = sum(durs)
-    achieved = sum(bytes_calls) / dec_time / 1e9
-    _say(f"[bench] {K} steps in {elapsed * 1e3:.1f} ms; decode calls avg "
-         f"{dec_time / len(durs) * 1e6:.1f} us, {achieved:.0f} GB/s")
+    _say(f"[bench] {K} steps x {layers} layers in {elapsed * 1e3:.2f} ms "
+         f"({elapsed / K * 1e3:.3f} ms/step)")
 
-    # ---- page quantization: one bulk event over every layer's residual buffers
-    n_jobs = w.layers * w.B * w.H_kv
+    # ---- decode-call roofline: every layer's call timed with HIP events on torch's stream
+    # (the stream the library launches on), state after the timed steps
+    restore()
+    for i in range(W, W + K):  # replay eagerly to the end state so lens match the host
+        run_step(i)
+    torch.cuda.synchronize()
+    lens_now = (caches[0].sink_len, caches[0].n_pages, caches[0].res_len)
+    qlast = [inputs[l][0][W + K - 1] for l in range(layers)]
+    durs = []
+    for rep in range(args.roofline_reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in caches]
+        for layer, c in enumerate(caches):
+            ev[layer][0].record()
+            c.attend(qlast[layer], outs[layer])
+            ev[layer][1].record()
+        torch.cuda.synchronize()
+        if rep:
+            durs += [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    call_s = float(np.mean(durs))
+    call_bytes = decode_bytes(cfg, lens_now, w.B, kpb, vpb)
+    achieved = call_bytes / call_s / 1e9
+    _say(f"[bench] decode call: {call_bytes / 1e6:.2f} MB in {call_s * 1e6:.2f} us avg "
+         f"(median {np.median(durs) * 1e6:.2f}) -> {achieved:.0f} GB/s")
+
+    # ---- page quantization: one bulk launch per kernel over every layer's residual buffers
+    n_jobs = layers * w.B * w.H_kv
     scratch_k = torch.empty(n_jobs, kpb, dtype=torch.uint8, device=dev)
     scratch_v = torch.empty(n_jobs, vpb, dtype=torch.uint8, device=dev)
     srcs_k, srcs_v, dk, dv, rows = [], [], [], [], []
@@ -305,15 +337,15 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16 in / packed u8 cache / fp32 attention",
         "data": "synthetic (seeded; log-normal persistent pair outliers, RoPE, V ~ N(0,1))",
-        "config": {"workload": w.name, "layers": w.layers, "global_batch": w.B,
-                   "kv_tokens_at_first_timed_step": w.T, "H_q": w.H_q, "H_kv": w.H_kv,
-                   "head_dim": w.d, "r": w.r, "G": w.G, "b_H": 3, "b_L": 1, "b_V": w.b_V,
-                   "N_s": w.N_s, "N": w.N, "parallelism": "single GPU"},
+        "config": {"workload": w.name, "layers": w.layers, "layer_copies_per_step": layers,
+                   "global_batch": w.B, "kv_tokens_at_first_timed_step": w.T, "H_q": w.H_q,
+                   "H_kv": w.H_kv, "head_dim": w.d, "r": w.r, "G": w.G, "b_H": 3, "b_L": 1,
+                   "b_V": w.b_V, "g_V": w.g_V, "N_s": w.N_s, "N": w.N,
+                   "parallelism": "single GPU", "timed": "one HIP graph of K steps"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "pnmix_decode_attn (split-K kernel + LSE merge)",
-                     "bytes_per_call": sum(bytes_calls) / len(bytes_calls),
-                     "avg_call_us": dec_time / len(durs) * 1e6},
+                     "kernel": "pnmix_decode_attn (split kernel + merge kernel, one call)",
+                     "bytes_per_call": call_bytes, "avg_call_us": call_s * 1e6},
         "page_quant": quant,
         "prefill_score": score,
         "cpu_baseline": cpu,

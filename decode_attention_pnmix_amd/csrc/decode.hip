@@ -1,28 +1,54 @@
 // decode.hip -- split-K GQA decode attention straight over the PN-Mix packed cache (gfx950).
 //
-// PN-Mix paper (arXiv 2610.19605), sec. 2, Eq. 1: causal GQA softmax attention; the
-// kernel-implementation appendix: each decode step visits the sink region, the quantized region
-// and the residual region, and the dequantized cache is never written back -- each quantized
-// group is unpacked and dequantized on chip and consumed at once.  TriAxialKV fact sheet:
-// flash-decoding splits merged by online log-sum-exp.
+// PN-Mix paper (arXiv 2610.19605), sec. 2, Eq. 1: causal GQA softmax attention at the decode
+// position; kernel-implementation appendix: each step visits the sink region, the quantized
+// region and the residual region, and the dequantized cache is never written back (each packed
+// group is unpacked on chip and consumed at once).  TriAxialKV fact sheet: flash-decoding
+// splits merged by online log-sum-exp.
 //
-// Work decomposition.  The cache of one (sequence, KV head) is a list of blocks: block 0 holds
-// the fp16 sinks, blocks 1..n_pages the packed pages, the last block the fp16 residual rows.
-// A workgroup takes one (sequence, KV head, split) and a contiguous run of blocks; all n_g
-// query heads of the GQA group are served from the same load of each page, so every packed
-// byte is read once per step.  Inside a block, 32-token sub-tiles are dequantized into LDS
-// (k = S q + Z with the page's fp16 S, Z), logits and an online softmax per head are kept in
-// fp32, and the partial (m, l, o) of the split goes to the workspace.  A second kernel merges
-// the splits: m = max m_j, l = sum e^(m_j - m) l_j, o = sum e^(m_j - m) o_j / l.
+// Work decomposition.  One wave (workgroup of 64) takes one (sequence, KV head, split).  A page
+// split walks a contiguous run of packed pages; one extra split per (sequence, KV head) takes the
+// fp16 sink and residual rows.  All n_g query heads of the GQA group are served from one read of
+// each page, so every packed byte crosses HBM once per step.  Partials (m, l, o) in log2 units go
+// to the workspace; a second kernel merges them.
+//
+// Page split, per page (keys quantized per channel, k = S_c q + Z_c; values per token and group,
+// v = S_tg q + Z_tg):
+//   logit(h, t) = sum_c (qt_hc S_c) code_tc + sum_c qt_hc Z_c,   qt = q * sm_scale * log2(e)
+//   o(h, c)    += sum_t (p_ht S_tg) code_tc + sum_t p_ht Z_tg
+// * q.K runs on the int8 matrix cores (v_mfma_i32_16x16x64_i8).  The per-page products
+//   qt_hc S_c become 32-bit fixed point (a per-head power-of-two scale from max|qt| max S) and are
+//   split into four signed base-256 digits: rows of the A operand are (head, digit), columns of
+//   the B operand are 16 keys, K is 64 channels.  The B operand is the packed code itself: the
+//   LSB plane byte of (channel, 8 tokens) and the upper-bit plane byte of (salient channel,
+//   4 tokens) are masked in place, one bit field per MFMA, so a tile holds the keys 8i + b of a
+//   page (i = 0..15) and a 16-byte load of either plane feeds eight tiles.  Integer accumulation
+//   is exact; the four digit partials of a key sit in one lane and are combined in fp32.
+// * p.V runs on the fp16 matrix cores (v_mfma_f32_16x16x32_f16).  Rows are (head, value group):
+//   w = p S_tg 2^k (2^k a per-page power of two that puts the page's largest w just under 2^15,
+//   far from the fp16 subnormal floor; the accumulator is rescaled with the softmax factor when
+//   k changes) is split into fp16 hi + lo (two MFMAs, about 22 bits, both halves rounded to
+//   nearest even), columns are 16 channels,
+//   K is 32 keys.  The 2-bit value codes enter as fp16 subnormals code * 2^-16 (the field moved
+//   to bits 8..9 of its half, a shift and an AND per two codes), scaled back by 2^16 at the end.
+//   Codes at the bottom of the subnormal range (code * 2^-24) are exact one product at a time
+//   but lose bits in the matrix core's 32-term sums (an absolute error near 2^-24 per
+//   instruction, measured); at 2^-16 the sums are as accurate as fp32 accumulation.
+// * The Z terms and the softmax bookkeeping run on the vector ALU in fp32.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace pnmix {
 
-constexpr int kDecThreads = 256;
-constexpr int kSub = 32;       // tokens per LDS sub-tile
-constexpr int kMaxG = 16;      // max query heads per KV head
-constexpr int kMaxDim = 128;
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kN = 128;  // page and residual length
+constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -36,195 +62,930 @@ struct DecodeArgs {
   const uint32_t* mask;
   float* part_o;   // [B*H_kv][splits][n_g][d]
   float* part_ml;  // [B*H_kv][splits][n_g][2]
-  float sm_scale;
-  int H_q, H_kv, d, pairing, n_hi, G, g_V, N_s, max_pages, words;
+  float qscale;    // sm_scale * log2(e)
+  int H_q, H_kv, n_g, pairing, n_hi, n_sal, G, KG, g_V, NGV, N_s, max_pages, words;
   int64_t kpb, vpb;
-  int splits, bps;
+  int splits, page_splits, pps;
+  int lds_T;       // bytes of the digit table (KG * NT * 16 rows * TL)
 };
 
-__global__ void __launch_bounds__(kDecThreads) decode_split_kernel(DecodeArgs a) {
-  __shared__ float qs[kMaxG][kMaxDim];
-  __shared__ float Kd[kSub][kMaxDim + 1];
-  __shared__ float Vd[kSub][kMaxDim];
-  __shared__ float pl[kMaxG][kSub];
-  __shared__ float alpha_s[kMaxG];
-  __shared__ int srank[kMaxDim];
+template <int D>
+struct Shape {
+  static constexpr int KL = (D + 63) / 64;   // 64-channel K-steps over the LSB plane
+  static constexpr int KHM = KL;             // at most this many over the upper-bit plane
+  static constexpr int TL = 64 * (KL + KHM); // bytes per (head, digit) row of the digit table
+  static constexpr int NM0 = (D + 63) / 64;  // 16-quad column halves of the p.V product
+  static constexpr int JL = D / 4;           // 4-channel units per head
+};
 
-  const int split = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int b = bh / a.H_kv;
-  const int h = bh % a.H_kv;
-  const int ng = a.H_q / a.H_kv;
-  const int d = a.d;
-  const int tid = threadIdx.x;
-  constexpr int N = 128;  // page and residual length
+// ---------------------------------------------------------------------------- small helpers
 
-  pnmix_seq_len L = a.lens[b];
-  const int sink_len = min(max(L.sink_len, 0), a.N_s);
-  const int n_pages = min(max(L.n_pages, 0), a.max_pages);
-  const int res_len = min(max(L.res_len, 0), N);
-  const int nblk = n_pages + 2;
-  const int blk0 = split * a.bps;
-  const int blk1 = min(blk0 + a.bps, nblk);
+// lanes outside the pattern keep their own value (bound_ctrl off, full row and bank masks)
+template <int CTRL>
+__device__ __forceinline__ float dpp_c(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, x), __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// all-reduce over the 16 lanes of a row (lanes 16r .. 16r+15)
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_c<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_c<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_c<0x124>(x));  // row_ror:4
+  x = fmaxf(x, dpp_c<0x128>(x));  // row_ror:8
+  return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x = x + dpp_c<0xB1>(x);
+  x = x + dpp_c<0x4E>(x);
+  x = x + dpp_c<0x124>(x);
+  x = x + dpp_c<0x128>(x);
+  return x;
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+// all-reduce over aligned groups of W lanes (W a power of two, 8 <= W <= 64): DPP inside a row
+// of 16, lane shuffles across rows
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  x = x + dpp_c<0xB1>(x);
+  x = x + dpp_c<0x4E>(x);
+  if (W == 8) return x + __shfl_xor(x, 4, 64);
+  x = x + dpp_c<0x124>(x);
+  x = x + dpp_c<0x128>(x);
+  if (W >= 32) x = x + __shfl_xor(x, 16, 64);
+  if (W >= 64) x = x + __shfl_xor(x, 32, 64);
+  return x;
+}
+template <int W>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dpp_c<0xB1>(x));
+  x = fmaxf(x, dpp_c<0x4E>(x));
+  if (W == 8) return fmaxf(x, __shfl_xor(x, 4, 64));
+  x = fmaxf(x, dpp_c<0x124>(x));
+  x = fmaxf(x, dpp_c<0x128>(x));
+  if (W >= 32) x = fmaxf(x, __shfl_xor(x, 16, 64));
+  if (W >= 64) x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u<0xB1>(x));
+  x = max(x, dpp_u<0x4E>(x));
+  x = max(x, dpp_u<0x124>(x));
+  x = max(x, dpp_u<0x128>(x));
+  x = max(x, (uint32_t)__shfl_xor((int)x, 16, 64));
+  return max(x, (uint32_t)__shfl_xor((int)x, 32, 64));
+}
 
-  const uint32_t* mrow = a.mask + (int64_t)bh * a.words;
-  for (int i = tid; i < ng * d; i += blockDim.x) {
-    const int hh = i / d, c = i % d;
-    qs[hh][c] = h2f(a.q[((int64_t)b * a.H_q + h * ng + hh) * d + c]);
-  }
-  for (int c = tid; c < d; c += blockDim.x) srank[c] = salient_rank(mrow, c, d, a.pairing, a.n_hi);
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+// two fp32 -> packed fp16, round to nearest even (v_cvt_pk_f16_f32): the lo half of a split
+// then carries no same-sign rounding bias even where it falls into the fp16 subnormal range
+__device__ __forceinline__ uint32_t pk_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, v2h{(_Float16)a, (_Float16)b});
+}
+__device__ __forceinline__ float pow2i(int e) {  // 2^e for e in [-126, 127]
+  return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+__device__ __forceinline__ float sel4(const v4f& v, int i) {
+  float r = v[0];
+  r = i == 1 ? v[1] : r;
+  r = i == 2 ? v[2] : r;
+  r = i == 3 ? v[3] : r;
+  return r;
+}
 
-  // thread-owned output accumulators: (head, channel) pairs i = tid + k * blockDim.x
-  constexpr int kAcc = kMaxG * kMaxDim / kDecThreads;
-  float acc[kAcc];
+// Balanced base-256 digits of x (|x| < 2^30): byte d of the result, read as int8, is digit d
+// and x = sum_d 256^d digit_d.
+__device__ __forceinline__ uint32_t digits4(int x) {
+  return ((uint32_t)x + 0x80808080u) ^ 0x80808080u;
+}
+// 4 x 4 byte transpose: out[d] byte i = byte d of y[i]
+__device__ __forceinline__ void transpose4(const uint32_t y[4], uint32_t out[4]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(y[1], y[0], 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(y[1], y[0], 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(y[3], y[2], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(y[3], y[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// Key codes of tile b as int8 B-operand bytes.  Tile b holds token 8i + b of octet i (LSB plane
+// bit b; upper-bit plane row 2i + b/4, field b%4).  Each field is masked in place, scaled by
+// sL(b) for the LSB and sH(b) = 2 sL(b) for the upper bits (their weight in the code is 2), so
+// one accumulator holds sL(b) * sum digit * code.
+template <int B>
+__device__ __forceinline__ uint32_t lsb_field(uint32_t w) {
+  if (B <= 4) return w & (0x01010101u << B);
+  if (B == 5) return (w >> 4) & 0x02020202u;
+  if (B == 6) return (w >> 3) & 0x08080808u;
+  return (w >> 4) & 0x08080808u;
+}
+template <int B>
+__device__ __forceinline__ uint32_t hi_field(uint32_t w) {
+  if (B == 0) return (w << 1) & 0x06060606u;
+  if (B == 1) return w & 0x0C0C0C0Cu;
+  if (B == 2) return (w >> 1) & 0x18181818u;
+  if (B == 3) return (w >> 2) & 0x30303030u;
+  if (B == 4) return (w << 5) & 0x60606060u;
+  if (B == 5) return w & 0x0C0C0C0Cu;
+  if (B == 6) return w & 0x30303030u;
+  return (w >> 2) & 0x30303030u;
+}
+__device__ constexpr float kInvSL[8] = {1.0f, 0.5f, 0.25f, 0.125f, 0.0625f, 0.5f, 0.125f, 0.125f};
+
+__device__ __forceinline__ v4u load16(const uint8_t* p) {
+  return *reinterpret_cast<const v4u*>(p);
+}
+
+// 16 bytes at an address that is only 2-byte aligned (upper-bit plane rows of odd length)
+__device__ __forceinline__ v4u load16_a2(const uint8_t* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
+  const uint32_t sh = (uint32_t)(a & 3);
+  uint32_t d[5];
 #pragma unroll
-  for (int k = 0; k < kAcc; ++k) acc[k] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;  // valid in threads tid < ng (one head each)
-  __syncthreads();
+  for (int i = 0; i < 5; ++i) d[i] = q[i];
+  v4u r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = sh ? __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh) : d[i];
+  return r;
+}
 
-  const int n_sal = 2 * a.n_hi;
-  for (int blk = blk0; blk < blk1; ++blk) {
-    int ntok;
-    const uint8_t* kp = nullptr;
-    const uint8_t* vp = nullptr;
-    const uint16_t* ksrc = nullptr;
-    const uint16_t* vsrc = nullptr;
-    if (blk == 0) {
-      ntok = sink_len;
-      ksrc = a.k_sink + (int64_t)bh * a.N_s * d;
-      vsrc = a.v_sink + (int64_t)bh * a.N_s * d;
-    } else if (blk == nblk - 1) {
-      ntok = res_len;
-      ksrc = a.k_res + (int64_t)bh * N * d;
-      vsrc = a.v_res + (int64_t)bh * N * d;
-    } else {
-      ntok = N;
-      kp = a.k_pages + ((int64_t)bh * a.max_pages + (blk - 1)) * a.kpb;
-      vp = a.v_pages + ((int64_t)bh * a.max_pages + (blk - 1)) * a.vpb;
-    }
-    for (int st = 0; st < ntok; st += kSub) {
-      const int nt = min(kSub, ntok - st);
-      // ---- dequantize the sub-tile into LDS
-      for (int i = tid; i < nt * d; i += blockDim.x) {
-        const int t = i / d, c = i % d;
-        const int tt = st + t;
-        float kv, vv;
-        if (kp) {
-          const uint8_t* lo = kp;
-          const uint8_t* hi = kp + N * d / 8;
-          const uint16_t* S = reinterpret_cast<const uint16_t*>(hi + N * n_sal / 4);
-          const uint16_t* Z = S + (N / a.G) * d;
-          uint32_t code = (lo[(tt >> 3) * d + c] >> (tt & 7)) & 1u;
-          const int r = srank[c];
-          if (r >= 0) code |= ((hi[(tt >> 2) * n_sal + r] >> (2 * (tt & 3))) & 3u) << 1;
-          const int g = tt / a.G;
-          kv = h2f(S[g * d + c]) * (float)code + h2f(Z[g * d + c]);
-          const int ngv = d / a.g_V;
-          const uint16_t* VS = reinterpret_cast<const uint16_t*>(vp + N * d / 4);
-          const uint16_t* VZ = VS + N * ngv;
-          const uint32_t vcode =
-              (vp[((tt >> 4) * (d / 4) + (c >> 2)) * 16 + (tt & 15)] >> (2 * (c & 3))) & 3u;
-          const int gv = c / a.g_V;
-          vv = h2f(VS[tt * ngv + gv]) * (float)vcode + h2f(VZ[tt * ngv + gv]);
-        } else {
-          kv = h2f(ksrc[(int64_t)tt * d + c]);
-          vv = h2f(vsrc[(int64_t)tt * d + c]);
-        }
-        Kd[t][c] = kv;
-        Vd[t][c] = vv;
-      }
-      __syncthreads();
-      // ---- logits
-      for (int i = tid; i < ng * nt; i += blockDim.x) {
-        const int hh = i / nt, t = i % nt;
-        float s = 0.0f;
-        for (int c = 0; c < d; ++c) s += qs[hh][c] * Kd[t][c];
-        pl[hh][t] = s * a.sm_scale;
-      }
-      __syncthreads();
-      // ---- online softmax, one thread per head
-      if (tid < ng) {
-        float mx = m_run;
-        for (int t = 0; t < nt; ++t) mx = fmaxf(mx, pl[tid][t]);
-        const float al = expf(m_run - mx);  // m_run = -inf on the first tile: al = 0
-        float sum = 0.0f;
-        for (int t = 0; t < nt; ++t) {
-          const float p = expf(pl[tid][t] - mx);
-          pl[tid][t] = p;
-          sum += p;
-        }
-        l_run = l_run * al + sum;
-        m_run = mx;
-        alpha_s[tid] = al;
-      }
-      __syncthreads();
-      // ---- o = o * alpha + P V
-#pragma unroll
-      for (int k = 0; k < kAcc; ++k) {
-        const int i = tid + k * kDecThreads;
-        if (i < ng * d) {
-          const int hh = i / d, c = i % d;
-          float s = acc[k] * alpha_s[hh];
-          for (int t = 0; t < nt; ++t) s += pl[hh][t] * Vd[t][c];
-          acc[k] = s;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // ---- partials of this split
-  const int64_t pbase = ((int64_t)bh * a.splits + split) * ng;
-#pragma unroll
-  for (int k = 0; k < kAcc; ++k) {
-    const int i = tid + k * kDecThreads;
-    if (i < ng * d) a.part_o[pbase * d + i] = acc[k];
-  }
-  if (tid < ng) {
-    a.part_ml[(pbase + tid) * 2 + 0] = m_run;
-    a.part_ml[(pbase + tid) * 2 + 1] = l_run;
+// ------------------------------------------------------------------------- partial writers
+
+template <int D>
+__device__ void write_empty_partial(const DecodeArgs& a, int64_t pbase) {
+  for (int i = threadIdx.x; i < a.n_g * D; i += 64) a.part_o[pbase * D + i] = 0.0f;
+  if ((int)threadIdx.x < a.n_g) {
+    a.part_ml[(pbase + threadIdx.x) * 2 + 0] = -INFINITY;
+    a.part_ml[(pbase + threadIdx.x) * 2 + 1] = 0.0f;
   }
 }
 
-__global__ void __launch_bounds__(128) decode_merge_kernel(const float* __restrict__ part_o,
+// -------------------------------------------------------------- fp16 sink + residual split
+
+// One wave over the fp16 rows, 64 tokens per chunk (token order: sinks, then residual rows).
+// Every load of a chunk is issued at once: each lane's key row (one token per lane for the
+// logits) and the chunk's value rows, staged in LDS with coalesced 16-byte loads (one channel
+// pair per lane for p.V).  Logits go through LDS one head at a time to keep registers low.
+template <int D, int NT>
+__device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, int64_t pbase,
+                            int sink_len, int res_len, uint8_t* lds) {
+  constexpr int NH = 4 * NT;
+  const int lane = threadIdx.x;
+  const int ng = a.n_g;
+  uint32_t* q2 = reinterpret_cast<uint32_t*>(lds);                  // [NH][D/2] fp16 pairs
+  float* pb = reinterpret_cast<float*>(lds + NH * D * 2);           // [64][NH] logits, then p
+  uint16_t* vst = reinterpret_cast<uint16_t*>(pb + 64 * NH);        // [64][D] value rows
+  for (int i = lane; i < NH * D / 2; i += 64) {
+    const int hh = i / (D / 2), c2 = i % (D / 2);
+    q2[i] = hh < ng ? *reinterpret_cast<const uint32_t*>(
+                          a.q + ((int64_t)b * a.H_q + (int64_t)h * ng + hh) * D + 2 * c2)
+                    : 0u;
+  }
+  __syncthreads();
+  float m[NH], l[NH], acc[NH][2];
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.0f;
+    acc[i][0] = acc[i][1] = 0.0f;
+  }
+  const int T16 = sink_len + res_len;
+  const uint16_t* ks = a.k_sink + bh * a.N_s * D;
+  const uint16_t* vs = a.v_sink + bh * a.N_s * D;
+  const uint16_t* kr = a.k_res + bh * kN * D;
+  const uint16_t* vr = a.v_res + bh * kN * D;
+  const bool chan = 2 * lane < D;
+  constexpr int PER = D / 8;  // 16-byte pieces per row
+  for (int c0 = 0; c0 < T16; c0 += 64) {
+    const int nt = min(64, T16 - c0);
+    // value rows of the chunk: piece i of the chunk is row i / PER, part i % PER
+    v4u vpc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = lane + 64 * j;
+      const int tr = i / PER, part = i % PER;
+      const int t = c0 + tr;
+      const uint16_t* vrow = t < sink_len ? vs + (int64_t)t * D : vr + (int64_t)(t - sink_len) * D;
+      vpc[j] = tr < nt ? *reinterpret_cast<const v4u*>(vrow + 8 * part) : v4u{0, 0, 0, 0};
+    }
+    const int tok = c0 + lane;
+    const bool valid = lane < nt;
+    v4u krow[PER];
+    {
+      const uint16_t* row = tok < sink_len ? ks + (int64_t)tok * D : kr + (int64_t)(tok - sink_len) * D;
+#pragma unroll
+      for (int c8 = 0; c8 < PER; ++c8)
+        krow[c8] = valid ? *reinterpret_cast<const v4u*>(row + 8 * c8) : v4u{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) *reinterpret_cast<v4u*>(vst + 8 * (lane + 64 * j)) = vpc[j];
+#pragma unroll 1
+    for (int i = 0; i < NH; ++i) {
+      float sacc = 0.0f;
+#pragma unroll
+      for (int c8 = 0; c8 < PER; ++c8) {
+        const v4u qv = *reinterpret_cast<const v4u*>(q2 + i * (D / 2) + 4 * c8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sacc = __builtin_fmaf(f16lo(qv[e]), f16lo(krow[c8][e]), sacc);
+          sacc = __builtin_fmaf(f16hi(qv[e]), f16hi(krow[c8][e]), sacc);
+        }
+      }
+      pb[lane * NH + i] = valid ? sacc * a.qscale : -INFINITY;
+    }
+    float alpha[NH];
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const float lgi = pb[lane * NH + i];
+      const float cm = group_max<64>(lgi);
+      const float mn = fmaxf(m[i], cm);
+      alpha[i] = __builtin_amdgcn_exp2f(m[i] - mn);
+      m[i] = mn;
+      pb[lane * NH + i] = valid ? __builtin_amdgcn_exp2f(lgi - mn) : 0.0f;
+    }
+    __syncthreads();  // p and the value rows are in LDS
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      acc[i][0] *= alpha[i];
+      acc[i][1] *= alpha[i];
+      l[i] *= alpha[i];
+    }
+    for (int tt = 0; tt < nt; ++tt) {
+      const uint32_t vv = chan ? *reinterpret_cast<const uint32_t*>(vst + tt * D + 2 * lane) : 0u;
+      const float v0 = f16lo(vv), v1 = f16hi(vv);
+#pragma unroll
+      for (int i = 0; i < NH; ++i) {
+        const float p = pb[tt * NH + i];
+        acc[i][0] = __builtin_fmaf(p, v0, acc[i][0]);
+        acc[i][1] = __builtin_fmaf(p, v1, acc[i][1]);
+        l[i] += p;
+      }
+    }
+    __syncthreads();  // LDS is reused by the next chunk
+  }
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    if (i >= ng) break;
+    if (chan) {
+      a.part_o[(pbase + i) * D + 2 * lane] = acc[i][0];
+      a.part_o[(pbase + i) * D + 2 * lane + 1] = acc[i][1];
+    }
+    if (lane == 0) {
+      a.part_ml[(pbase + i) * 2 + 0] = T16 > 0 ? m[i] : -INFINITY;
+      a.part_ml[(pbase + i) * 2 + 1] = l[i];
+    }
+  }
+}
+
+// The fp16 split of every (sequence, KV head): its partial is split index page_splits.
+template <int D, int NT>
+__global__ void __launch_bounds__(64) decode_fp16_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int64_t bh = blockIdx.x;
+  const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
+  const pnmix_seq_len L = a.lens[b];
+  const int sink_len = min(max(L.sink_len, 0), a.N_s);
+  const int res_len = min(max(L.res_len, 0), kN);
+  const int64_t pbase = (bh * a.splits + a.page_splits) * a.n_g;
+  fp16_region<D, NT>(a, b, h, bh, pbase, sink_len, res_len, lds);
+}
+
+// ----------------------------------------------------------------------------- page split
+
+template <int D, int NT, int KG>
+__global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
+  using S_ = Shape<D>;
+  constexpr int KL = S_::KL, KHM = S_::KHM, TL = S_::TL, NM0 = S_::NM0, JL = S_::JL;
+  constexpr int NH = 4 * NT;
+  constexpr int UK = (NT * D + 63) / 64;  // LSB prep units per lane
+  extern __shared__ __align__(16) uint8_t lds[];
+
+  const int lane = threadIdx.x;
+  const int split = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
+  const int ng = a.n_g;
+  const pnmix_seq_len L = a.lens[b];
+  const int n_pages = min(max(L.n_pages, 0), a.max_pages);
+  const int64_t pbase = (bh * a.splits + split) * ng;
+
+  const int p0 = split * a.pps;
+  const int p1 = min(p0 + a.pps, n_pages);
+  if (p0 >= p1) {
+    write_empty_partial<D>(a, pbase);
+    return;
+  }
+
+  // LDS: digit table T [KG][NT][16][TL] bytes, p buffer [NT][4][128] f32, key scales of the page
+  // [KG][D] fp16, bias [KG][NH] f32, salient channel of each rank [D] int16.
+  uint8_t* T = lds;
+  float* P = reinterpret_cast<float*>(lds + a.lds_T);
+  uint16_t* Sl = reinterpret_cast<uint16_t*>(P + NT * 4 * kN);
+  float* biasl = reinterpret_cast<float*>(Sl + 4 * D);
+  int16_t* sal = reinterpret_cast<int16_t*>(biasl + 4 * NH);
+
+  const int G = a.G, n_sal = a.n_sal, NGV = a.NGV;
+  const int KH = (n_sal + 63) / 64;
+  const int JH = (n_sal + 3) / 4;  // 4-rank units per head of the upper-bit part
+
+  // ---- once per split: clear the digit table, salient ranks, scaled queries
+  for (int i = lane * 16; i < a.lds_T; i += 64 * 16) *reinterpret_cast<v4u*>(T + i) = v4u{0, 0, 0, 0};
+  const uint32_t* mrow = a.mask + bh * a.words;
+  for (int c = lane; c < D; c += 64) sal[c] = -1;
+  __syncthreads();
+  for (int c = lane; c < D; c += 64) {
+    const int r = salient_rank(mrow, c, D, a.pairing, a.n_hi);
+    if (r >= 0) sal[r] = (int16_t)c;
+  }
+  // LSB prep units: unit u = lane + 64k -> head hu = u / JL (0..NH-1), channels 4 (u % JL) + 0..3
+  float qv[UK][4];
+  float qmaxu[UK];
+#pragma unroll
+  for (int k = 0; k < UK; ++k) {
+    const int u = lane + 64 * k;
+    const int hu = u / JL, j = u % JL;
+    const bool ok = u < NT * D && hu < ng;
+    uint2 qq = make_uint2(0u, 0u);
+    if (ok) qq = *reinterpret_cast<const uint2*>(a.q + ((int64_t)b * a.H_q + (int64_t)h * ng + hu) * D + 4 * j);
+    qv[k][0] = f16lo(qq.x) * a.qscale;
+    qv[k][1] = f16hi(qq.x) * a.qscale;
+    qv[k][2] = f16lo(qq.y) * a.qscale;
+    qv[k][3] = f16hi(qq.y) * a.qscale;
+    float mx = fmaxf(fmaxf(fabsf(qv[k][0]), fabsf(qv[k][1])), fmaxf(fabsf(qv[k][2]), fabsf(qv[k][3])));
+    qmaxu[k] = group_max<(JL < 64 ? JL : 64)>(mx);
+  }
+  // max |qt| of the head this lane has in the q.K output (head 4t + lane/16)
+  float qmaxC[NT];
+  {
+    float* qm = P;  // scratch before P is used
+    if (lane < 64) {
+#pragma unroll
+      for (int k = 0; k < UK; ++k) {
+        const int u = lane + 64 * k;
+        if (u < NT * D && (u % JL) == 0) qm[u / JL] = qmaxu[k];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) qmaxC[t] = qm[4 * t + lane / 16];
+    __syncthreads();
+  }
+  // upper-bit prep units: uh = lane + 64k -> head uh / JH, ranks 4 (uh % JH) + 0..3
+  constexpr int UKH = (NT * 4 * (D / 4) + 63) / 64;
+  int hc[UKH][4];
+  float hq[UKH][4];
+  float hqmax[UKH];
+#pragma unroll
+  for (int k = 0; k < UKH; ++k) {
+    const int uh = lane + 64 * k;
+    const int hu = JH ? uh / JH : 0, jr = JH ? uh % JH : 0;
+    const bool ok = JH && uh < NH * JH && hu < ng;
+    hqmax[k] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * jr + i;
+      const int cs = (ok && r < n_sal) ? sal[r] : -1;
+      hc[k][i] = (cs >= 0 && cs < D) ? cs : -1;  // a mask outside the contract stays in range
+      hq[k][i] = hc[k][i] >= 0 ? (float)__builtin_bit_cast(_Float16,
+                     a.q[((int64_t)b * a.H_q + (int64_t)h * ng + hu) * D + hc[k][i]]) * a.qscale
+                               : 0.0f;
+    }
+  }
+  // max|qt| of head hu for the upper-bit units: from the LSB units' head maxima via LDS
+  {
+    float* qm = P;
+#pragma unroll
+    for (int k = 0; k < UK; ++k) {
+      const int u = lane + 64 * k;
+      if (u < NT * D && (u % JL) == 0) qm[u / JL] = qmaxu[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < UKH; ++k) {
+      const int uh = lane + 64 * k;
+      const int hu = JH ? uh / JH : 0;
+      hqmax[k] = (JH && uh < NH * JH) ? qm[hu] : 0.0f;
+    }
+    __syncthreads();
+  }
+
+  // running softmax state of head 4t + lane/16; p.V accumulators [t][m0][u] in C layout
+  float m_run[NT], l_run[NT];
+  float zacc[NT][4];
+  int k_run = 0;  // p.V operands carry p S 2^k_run (keeps w clear of the fp16 subnormal floor)
+  v4f acc[NT][NM0][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) zacc[t][g] = 0.0f;
+#pragma unroll
+    for (int m0 = 0; m0 < NM0; ++m0)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[t][m0][u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  const int oct = lane & 15;  // octet of the q.K B operand (keys 8 oct + b)
+  const int qb = lane >> 4;   // K block (16 channels / 8 keys) of this lane
+  const int kg_lane = (8 * oct) / G;  // key group of this lane's keys
+  const int64_t page_base = bh * a.max_pages;
+  const int sOff = kN * D / 8 + kN * n_sal / 4;      // K page: S after lo and hi planes
+  const int zOff = sOff + 2 * KG * D;
+
+  // Key side of one page in registers: this lane's packed codes (LSB rows and upper-bit rows
+  // 2 oct, 2 oct + 1) and the scales of its prep units.  The next page's are loaded into them as
+  // soon as the current page's q.K is done, so their latency hides behind softmax and p.V.
+  v4u wL[KL], wH0[KHM], wH1[KHM];
+  uint2 sv[UK][KG], zv[UK][KG];  // [k][kg] 4 fp16 of S and Z for the unit's channels
+  auto load_k = [&](int pgk) {
+    const uint8_t* kp = a.k_pages + (page_base + pgk) * a.kpb;
+#pragma unroll
+    for (int ks = 0; ks < KL; ++ks) {
+      const int c0 = 64 * ks + 16 * qb;
+      wL[ks] = c0 < D ? load16(kp + oct * D + c0) : v4u{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KHM; ++ks) {
+      const int r0 = 64 * ks + 16 * qb;
+      wH0[ks] = wH1[ks] = v4u{0, 0, 0, 0};
+      if (ks < KH && r0 < n_sal) {
+        const uint8_t* hp = kp + kN * D / 8 + r0;
+        if ((n_sal & 15) == 0) {
+          wH0[ks] = *reinterpret_cast<const v4u*>(hp + (2 * oct) * n_sal);
+          wH1[ks] = *reinterpret_cast<const v4u*>(hp + (2 * oct + 1) * n_sal);
+        } else {
+          wH0[ks] = load16_a2(hp + (2 * oct) * n_sal);
+          wH1[ks] = load16_a2(hp + (2 * oct + 1) * n_sal);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UK; ++k) {
+      const int u = lane + 64 * k;
+      const int j = u % JL;
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg) {
+        sv[k][kg] = zv[k][kg] = make_uint2(0u, 0u);
+        if (u < NT * D) {
+          sv[k][kg] = *reinterpret_cast<const uint2*>(kp + sOff + 2 * (kg * D + 4 * j));
+          zv[k][kg] = *reinterpret_cast<const uint2*>(kp + zOff + 2 * (kg * D + 4 * j));
+        }
+      }
+    }
+  };
+  load_k(p0);
+
+  for (int pg = p0; pg < p1; ++pg) {
+    const uint8_t* vp = a.v_pages + (page_base + pg) * a.vpb;
+    const uint16_t* VS = reinterpret_cast<const uint16_t*>(vp + kN * D / 4);  // [NGV][N]
+    const uint16_t* VZ = VS + NGV * kN;
+
+    // ---- value side of this page, issued now, consumed after q.K: scales of this lane's p.V
+    // rows (group gA, 8 keys of octet 4s + qb), offsets of its q.K keys (8 oct + b) per group,
+    // codes byte [octet][m][key] for m = 16 m0 + (lane & 15)
+    const int R = lane & 15, hlA = R >> 2, gA = R & 3;
+    v4u sS[4], zZ[4];
+    uint2 cw[4][NM0];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      sS[s] = gA < NGV ? *reinterpret_cast<const v4u*>(VS + gA * kN + 8 * (4 * s + qb))
+                       : v4u{0, 0, 0, 0};
+      zZ[s] = s < NGV ? *reinterpret_cast<const v4u*>(VZ + s * kN + 8 * oct) : v4u{0, 0, 0, 0};
+#pragma unroll
+      for (int m0 = 0; m0 < NM0; ++m0) {
+        const int m = 16 * m0 + (lane & 15);
+        cw[s][m0] = m < D / 4 ? *reinterpret_cast<const uint2*>(vp + ((int64_t)(4 * s + qb) * (D / 4) + m) * 8)
+                              : make_uint2(0u, 0u);
+      }
+    }
+
+    // ---- key scales: page maximum -> per-head fixed-point exponent
+    uint32_t smax = 0u;
+#pragma unroll
+    for (int k = 0; k < UK; ++k) {
+      const int u = lane + 64 * k;
+      const int j = u % JL;
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg) {
+        smax = max(smax, max(max(sv[k][kg].x & 0xFFFFu, sv[k][kg].x >> 16),
+                             max(sv[k][kg].y & 0xFFFFu, sv[k][kg].y >> 16)));
+        if (u < JL) *reinterpret_cast<uint2*>(Sl + kg * D + 4 * j) = sv[k][kg];
+      }
+    }
+    smax = wave_max_u32(smax);
+    const float Smax = (float)__builtin_bit_cast(_Float16, (uint16_t)smax);
+    // 2^sigma with |qt S 2^sigma| < 2^30 for every channel of the head
+    auto sigma_of = [&](float qmax) -> int {
+      const float M = qmax * Smax;
+      if (!(M > 0.0f)) return 0;
+      const int e = (int)((__builtin_bit_cast(uint32_t, M) >> 23) & 0xFF) - 127;
+      return min(max(29 - e, -126), 126);
+    };
+
+    // ---- digit table, LSB part, and the Z bias of each head
+#pragma unroll
+    for (int k = 0; k < UK; ++k) {
+      const int u = lane + 64 * k;
+      const int hu = u / JL, j = u % JL;
+      const bool ok = u < NT * D;
+      const float sc = pow2i(sigma_of(qmaxu[k]));
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg) {
+        const float s4[4] = {f16lo(sv[k][kg].x), f16hi(sv[k][kg].x), f16lo(sv[k][kg].y), f16hi(sv[k][kg].y)};
+        const float z4[4] = {f16lo(zv[k][kg].x), f16hi(zv[k][kg].x), f16lo(zv[k][kg].y), f16hi(zv[k][kg].y)};
+        uint32_t y[4], dg[4];
+        float bz = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y[i] = digits4((int)((qv[k][i] * sc) * s4[i]));
+          bz = __builtin_fmaf(qv[k][i], z4[i], bz);
+        }
+        transpose4(y, dg);
+        bz = group_sum<(JL < 64 ? JL : 64)>(bz);
+        if (ok) {
+          const int t = hu / 4, hl = hu % 4;
+          uint8_t* row = T + ((kg * NT + t) * 16 + 4 * hl) * TL + 4 * j;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) *reinterpret_cast<uint32_t*>(row + d * TL) = dg[d];
+          if (j == 0) biasl[kg * NH + hu] = bz;
+        }
+      }
+    }
+    __syncthreads();  // Sl and the LSB digits are in LDS
+
+    // ---- digit table, upper-bit part: ranks of salient channels, code weight 2 is in sH
+#pragma unroll
+    for (int k = 0; k < UKH; ++k) {
+      const int uh = lane + 64 * k;
+      if (!(JH && uh < NH * JH)) continue;
+      const int hu = uh / JH, jr = uh % JH;
+      const float sc = pow2i(sigma_of(hqmax[k]));
+      const int t = hu / 4, hl = hu % 4;
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg) {
+        uint32_t y[4], dg[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float s = hc[k][i] >= 0 ? (float)__builtin_bit_cast(_Float16, Sl[kg * D + hc[k][i]]) : 0.0f;
+          y[i] = digits4((int)((hq[k][i] * sc) * s));
+        }
+        transpose4(y, dg);
+        uint8_t* row = T + ((kg * NT + t) * 16 + 4 * hl) * TL + 64 * KL + 4 * jr;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) *reinterpret_cast<uint32_t*>(row + d * TL) = dg[d];
+      }
+    }
+    __syncthreads();
+
+    // ---- A operands (digit rows) of every tile and key group
+    v4i A[KG][NT][KL + KHM];
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KL + KHM; ++ks)
+          A[kg][t][ks] = *reinterpret_cast<const v4i*>(T + ((kg * NT + t) * 16 + (lane & 15)) * TL +
+                                                       64 * ks + 16 * qb);
+    }
+    float inv2s[NT], bias[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      inv2s[t] = pow2i(-sigma_of(qmaxC[t]));
+      bias[t] = biasl[kg_lane * NH + 4 * t + qb];
+    }
+
+    // ---- q.K: tile b holds keys 8 oct + b; the lane's q.K output head is 4t + qb
+    float lg[NT][8];
+#define PNMIX_QK_TILE(BB)                                                                      \
+    {                                                                                          \
+      v4i bL[KL], bH[KHM];                                                                     \
+      _Pragma("unroll") for (int ks = 0; ks < KL; ++ks) {                                      \
+        v4u w = wL[ks];                                                                        \
+        bL[ks] = v4i{(int)lsb_field<BB>(w[0]), (int)lsb_field<BB>(w[1]),                       \
+                     (int)lsb_field<BB>(w[2]), (int)lsb_field<BB>(w[3])};                      \
+      }                                                                                        \
+      _Pragma("unroll") for (int ks = 0; ks < KHM; ++ks) {                                     \
+        v4u w = (BB < 4) ? wH0[ks] : wH1[ks];                                                  \
+        bH[ks] = v4i{(int)hi_field<BB>(w[0]), (int)hi_field<BB>(w[1]),                         \
+                     (int)hi_field<BB>(w[2]), (int)hi_field<BB>(w[3])};                        \
+      }                                                                                        \
+      _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                         \
+        v4i csel = v4i{0, 0, 0, 0};                                                            \
+        _Pragma("unroll") for (int kg = 0; kg < KG; ++kg) {                                    \
+          v4i c = v4i{0, 0, 0, 0};                                                             \
+          _Pragma("unroll") for (int ks = 0; ks < KL; ++ks)                                    \
+            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[kg][t][ks], bL[ks], c, 0, 0, 0);       \
+          _Pragma("unroll") for (int ks = 0; ks < KHM; ++ks)                                   \
+            if (ks < KH) c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[kg][t][KL + ks], bH[ks], c, 0, 0, 0); \
+          csel = (KG == 1 || kg == kg_lane) ? c : csel;                                        \
+        }                                                                                      \
+        const float v = (((float)csel[3] * 256.0f + (float)csel[2]) * 256.0f +                 \
+                         (float)csel[1]) * 256.0f + (float)csel[0];                            \
+        lg[t][BB] = __builtin_fmaf(v, inv2s[t] * kInvSL[BB], bias[t]);                         \
+      }                                                                                        \
+    }
+    PNMIX_QK_TILE(0) PNMIX_QK_TILE(1) PNMIX_QK_TILE(2) PNMIX_QK_TILE(3)
+    PNMIX_QK_TILE(4) PNMIX_QK_TILE(5) PNMIX_QK_TILE(6) PNMIX_QK_TILE(7)
+#undef PNMIX_QK_TILE
+
+    // ---- the key side of this page is consumed: fetch the next page's
+    if (pg + 1 < p1) load_k(pg + 1);
+
+    // ---- the page's power-of-two p.V operand scale 2^k: p S 2^k < 2^15 for every key, group
+    uint32_t svmax = 0u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) svmax = max(svmax, max(sS[s][e] & 0xFFFFu, sS[s][e] >> 16));
+    svmax = wave_max_u32(svmax);
+    int k_page = 0;
+    {
+      const float Sv = (float)__builtin_bit_cast(_Float16, (uint16_t)svmax);
+      if (Sv > 0.0f) {
+        const int e = (int)((__builtin_bit_cast(uint32_t, Sv) >> 23) & 0xFF) - 127;
+        k_page = min(max(14 - e, 0), 64);
+      }
+    }
+    if (pg == p0) k_run = k_page;
+    const float kscale = pow2i(k_page);
+
+    // ---- online softmax per head; p 2^k to LDS; value-offset term on the vector ALU
+    bool rescale = k_page != k_run;
+    float alpha[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float pm = lg[t][0];
+#pragma unroll
+      for (int bb = 1; bb < 8; ++bb) pm = fmaxf(pm, lg[t][bb]);
+      pm = row_max16(pm);
+      const float mn = fmaxf(m_run[t], pm);
+      alpha[t] = __builtin_amdgcn_exp2f(m_run[t] - mn);
+      rescale |= (alpha[t] != 1.0f);
+      m_run[t] = mn;
+      float p[8], ps = 0.0f;
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) {
+        p[bb] = __builtin_amdgcn_exp2f(lg[t][bb] - mn);
+        ps += p[bb];
+      }
+      l_run[t] = l_run[t] * alpha[t] + ps;
+      float* prow = P + (t * 4 + qb) * kN + 8 * oct;
+      *reinterpret_cast<v4f*>(prow) = v4f{p[0], p[1], p[2], p[3]} * kscale;
+      *reinterpret_cast<v4f*>(prow + 4) = v4f{p[4], p[5], p[6], p[7]} * kscale;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (g >= NGV) break;
+        const v4u zz = zZ[g];
+        float s = zacc[t][g] * alpha[t];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s = __builtin_fmaf(p[2 * e], f16lo(zz[e]), s);
+          s = __builtin_fmaf(p[2 * e + 1], f16hi(zz[e]), s);
+        }
+        zacc[t][g] = s;
+      }
+    }
+    if (__any(rescale)) {
+      const float kf = pow2i(k_page - k_run);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float f = alpha[t] * kf;
+#pragma unroll
+        for (int m0 = 0; m0 < NM0; ++m0)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[t][m0][u] *= f;
+      }
+    }
+    k_run = k_page;
+    __syncthreads();  // p visible
+
+    // ---- p.V: A rows (head hl, value group g) = lane & 15, K block qb = 8 keys of octet 4s + qb
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int octv = 4 * s + qb;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float* prow = P + (t * 4 + hlA) * kN + 8 * octv;
+        const v4f pa = *reinterpret_cast<const v4f*>(prow);
+        const v4f pc = *reinterpret_cast<const v4f*>(prow + 4);
+        const float pe[8] = {pa[0], pa[1], pa[2], pa[3], pc[0], pc[1], pc[2], pc[3]};
+        float sw[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sw[2 * e] = f16lo(sS[s][e]);
+          sw[2 * e + 1] = f16hi(sS[s][e]);
+        }
+        float w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = __builtin_fmaf(pe[e], sw[e], 0.0f);
+        // K element order (matches the codes below): (0,2), (1,3), (4,6), (5,7)
+        const uint32_t h02 = pk_rne(w[0], w[2]), h13 = pk_rne(w[1], w[3]);
+        const uint32_t h46 = pk_rne(w[4], w[6]), h57 = pk_rne(w[5], w[7]);
+        const uint32_t l02 = pk_rne(__builtin_fmaf(pe[0], sw[0], -f16lo(h02)), __builtin_fmaf(pe[2], sw[2], -f16hi(h02)));
+        const uint32_t l13 = pk_rne(__builtin_fmaf(pe[1], sw[1], -f16lo(h13)), __builtin_fmaf(pe[3], sw[3], -f16hi(h13)));
+        const uint32_t l46 = pk_rne(__builtin_fmaf(pe[4], sw[4], -f16lo(h46)), __builtin_fmaf(pe[6], sw[6], -f16hi(h46)));
+        const uint32_t l57 = pk_rne(__builtin_fmaf(pe[5], sw[5], -f16lo(h57)), __builtin_fmaf(pe[7], sw[7], -f16hi(h57)));
+        const v8h Ahi = __builtin_bit_cast(v8h, v4u{h02, h13, h46, h57});
+        const v8h Alo = __builtin_bit_cast(v8h, v4u{l02, l13, l46, l57});
+#pragma unroll
+        for (int m0 = 0; m0 < NM0; ++m0) {
+          const uint32_t w0 = cw[s][m0].x, w1 = cw[s][m0].y;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            // field u of every byte moved to bits 8..9 of its fp16 half: value code * 2^-16
+            const uint32_t M = 0x03000300u;
+            const v8h Bv = __builtin_bit_cast(
+                v8h, v4u{(w0 << (8 - 2 * u)) & M, (w0 >> (2 * u)) & M, (w1 << (8 - 2 * u)) & M,
+                         (w1 >> (2 * u)) & M});
+            acc[t][m0][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, acc[t][m0][u], 0, 0, 0);
+            acc[t][m0][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, acc[t][m0][u], 0, 0, 0);
+          }
+        }
+      }
+    }
+    __syncthreads();  // P, T and Sl are rewritten by the next page
+  }
+
+  // ---- partials of this split: head 4t + qb in both output layouts
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float lt = row_sum16(l_run[t]);
+    float zs[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) zs[g] = row_sum16(zacc[t][g]);
+    const int hh = 4 * t + qb;
+    if (hh < ng) {
+#pragma unroll
+      for (int m0 = 0; m0 < NM0; ++m0)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = 4 * (16 * m0 + (lane & 15)) + u;
+          if (c < D) {
+            const int gi = c / a.g_V;
+            const float zsg = gi == 0 ? zs[0] : gi == 1 ? zs[1] : gi == 2 ? zs[2] : zs[3];
+            const float v = sel4(acc[t][m0][u], gi) * pow2i(16 - k_run) + zsg;
+            a.part_o[(pbase + hh) * D + c] = v;
+          }
+        }
+      if ((lane & 15) == 0) {
+        a.part_ml[(pbase + hh) * 2 + 0] = m_run[t];
+        a.part_ml[(pbase + hh) * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------- merge
+
+// One workgroup per (sequence, query head): 256 threads find the maximum over the splits, put
+// each split's weight 2^(m_s - m) in LDS, then sum the weighted outputs with the splits spread
+// over 256 / d groups of threads and add the group sums in a fixed order (deterministic).
+__global__ void __launch_bounds__(256) decode_merge_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            float* __restrict__ out, int H_q,
                                                            int H_kv, int d, int splits) {
+  __shared__ float wts[1024];
+  __shared__ float red[256];
+  __shared__ float osum[256];
   const int bhq = blockIdx.x;  // b * H_q + hq
   const int b = bhq / H_q;
   const int hq = bhq % H_q;
   const int ng = H_q / H_kv;
   const int h = hq / ng, hh = hq % ng;
   const int64_t bh = (int64_t)b * H_kv + h;
+  const int tid = threadIdx.x;
   float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, part_ml[((bh * splits + s) * ng + hh) * 2]);
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float l = 0.0f, o = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-      const int64_t p = (bh * splits + s) * ng + hh;
-      const float ms = part_ml[p * 2];
-      if (ms == -INFINITY) continue;  // empty split
-      const float w = expf(ms - m);
-      l += w * part_ml[p * 2 + 1];
-      o += w * part_o[p * d + c];
-    }
-    out[(int64_t)bhq * d + c] = l > 0.0f ? o / l : 0.0f;
+  for (int s = tid; s < splits; s += 256) m = fmaxf(m, part_ml[((bh * splits + s) * ng + hh) * 2]);
+  red[tid] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
   }
+  m = red[0];
+  __syncthreads();
+  float lsum = 0.0f;
+  for (int s = tid; s < splits; s += 256) {
+    const int64_t p = (bh * splits + s) * ng + hh;
+    const float ms = part_ml[p * 2];
+    const float wv = (m == -INFINITY || ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - m);
+    if (s < 1024) wts[s] = wv;
+    lsum += wv * part_ml[p * 2 + 1];
+  }
+  red[tid] = lsum;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = red[tid] + red[tid + o];
+    __syncthreads();
+  }
+  const float l = red[0];
+  const int ngrp = 256 / d;  // d in {32, 64, 128}
+  const int c = tid % d, grp = tid / d;
+  float o = 0.0f;
+  for (int s = grp; s < splits; s += ngrp) {
+    const float wv = s < 1024 ? wts[s] : 0.0f;
+    if (wv != 0.0f) o += wv * part_o[((bh * splits + s) * ng + hh) * d + c];
+  }
+  osum[tid] = o;
+  __syncthreads();
+  if (tid < d) {
+    float t = 0.0f;
+    for (int g = 0; g < ngrp; ++g) t += osum[g * d + tid];
+    out[(int64_t)bhq * d + tid] = l > 0.0f ? t / l : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------------- host
+
+// 4-head tiles of the GQA group; 3 tiles run as 4 (the extra heads are zero)
+static int n_tiles(const pnmix_cfg& c) {
+  const int t = (c.H_q / c.H_kv + 3) / 4;
+  return t == 3 ? 4 : t;
+}
+
+static size_t lds_T_bytes(const pnmix_cfg& c) {
+  const int KL = (c.d + 63) / 64;
+  const int TL = 64 * 2 * KL;
+  return (size_t)(c.N / c.G) * n_tiles(c) * 16 * TL;
+}
+
+static size_t lds_bytes(const pnmix_cfg& c) {
+  const int NT = n_tiles(c);
+  return lds_T_bytes(c) + (size_t)NT * 4 * kN * 4 + 4 * c.d * 2 + 4 * 4 * NT * 4 + c.d * 2;
+}
+
+static size_t lds_fp16_bytes(const pnmix_cfg& c) {
+  const int NT = n_tiles(c);
+  return (size_t)4 * NT * c.d * 2 + 64 * 4 * NT * 4 + 64 * (size_t)c.d * 2;
 }
 
 DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   DecodePlan p;
-  const int nblk = max_pages + 2;
   const long long items = (long long)B * c.H_kv;
-  // aim for >= 2048 workgroups (8 per CU) while keeping >= 4 blocks per split
-  int splits = (int)((2048 + items - 1) / items);
-  splits = max(1, min(splits, (nblk + 3) / 4));
-  p.blocks_per_split = (nblk + splits - 1) / splits;
-  p.splits = (nblk + p.blocks_per_split - 1) / p.blocks_per_split;
+  // about two resident waves per SIMD (256 CUs x 4 SIMDs), pages split evenly: one round of
+  // waves covers the grid, so no tail of late waves
+  const long long target = 2048;
+  int ps = (int)std::max<long long>(1, target / std::max<long long>(items, 1) - 1);
+  ps = std::min(ps, std::max(max_pages, 1));
+  ps = std::min(ps, 1023);  // the merge kernel keeps at most 1024 split weights in LDS
+  int pps = max_pages > 0 ? (max_pages + ps - 1) / ps : 1;
+  ps = max_pages > 0 ? (max_pages + pps - 1) / pps : 0;
+  p.page_splits = ps;
+  p.pages_per_split = pps;
+  p.splits = ps + 1;
   const int ng = c.H_q / c.H_kv;
   const size_t per = (size_t)items * p.splits * ng;
-  size_t o_bytes = (per * c.d * sizeof(float) + 255) & ~(size_t)255;
+  const size_t o_bytes = (per * c.d * sizeof(float) + 255) & ~(size_t)255;
   p.ws_bytes = o_bytes + ((per * 2 * sizeof(float) + 255) & ~(size_t)255);
+  p.lds_bytes = std::max(lds_bytes(c), lds_fp16_bytes(c));
   return p;
+}
+
+template <int D, int NT, int KG>
+static hipError_t launch_k(const DecodePlan& p, int B, const pnmix_cfg& c, const DecodeArgs& a,
+                           hipStream_t stream) {
+  if (p.page_splits > 0) {
+    hipLaunchKernelGGL((decode_kernel<D, NT, KG>), dim3(p.page_splits, B * c.H_kv), dim3(64),
+                       lds_bytes(c), stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_fp16_kernel<D, NT>), dim3(B * c.H_kv), dim3(64), lds_fp16_bytes(c),
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int NT>
+static hipError_t launch_t(const DecodePlan& p, int B, const pnmix_cfg& c, const DecodeArgs& a,
+                           hipStream_t stream) {
+  switch (c.N / c.G) {
+    case 1: return launch_k<D, NT, 1>(p, B, c, a, stream);
+    case 2: return launch_k<D, NT, 2>(p, B, c, a, stream);
+    default: return launch_k<D, NT, 4>(p, B, c, a, stream);
+  }
+}
+
+template <int D>
+static hipError_t launch_d(const DecodePlan& p, int B, const pnmix_cfg& c, const DecodeArgs& a,
+                           hipStream_t stream) {
+  switch (n_tiles(c)) {
+    case 1: return launch_t<D, 1>(p, B, c, a, stream);
+    case 2: return launch_t<D, 2>(p, B, c, a, stream);
+    default: return launch_t<D, 4>(p, B, c, a, stream);
+  }
 }
 
 hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_t* q,
@@ -248,26 +1009,34 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
   a.part_o = static_cast<float*>(ws);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                        ((per * c.d * sizeof(float) + 255) & ~(size_t)255));
-  a.sm_scale = sm_scale;
+  a.qscale = sm_scale * kLog2e;
   a.H_q = c.H_q;
   a.H_kv = c.H_kv;
-  a.d = c.d;
+  a.n_g = ng;
   a.pairing = c.pairing;
   a.n_hi = c.n_hi_pairs;
+  a.n_sal = 2 * c.n_hi_pairs;
   a.G = c.G;
+  a.KG = c.N / c.G;
   a.g_V = c.g_V;
+  a.NGV = c.d / c.g_V;
   a.N_s = c.N_s;
   a.max_pages = max_pages;
   a.words = (c.d / 2 + 31) / 32;
   a.kpb = (int64_t)pnmix_k_page_bytes(&c);
   a.vpb = (int64_t)pnmix_v_page_bytes(&c);
   a.splits = p.splits;
-  a.bps = p.blocks_per_split;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(p.splits, B * c.H_kv), dim3(kDecThreads), 0,
-                     stream, a);
-  hipError_t e = hipGetLastError();
+  a.page_splits = p.page_splits;
+  a.pps = p.pages_per_split;
+  a.lds_T = (int)lds_T_bytes(c);
+  hipError_t e;
+  switch (c.d) {
+    case 32: e = launch_d<32>(p, B, c, a, stream); break;
+    case 64: e = launch_d<64>(p, B, c, a, stream); break;
+    default: e = launch_d<128>(p, B, c, a, stream); break;
+  }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(B * c.H_q), dim3(128), 0, stream, a.part_o,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(B * c.H_q), dim3(256), 0, stream, a.part_o,
                      a.part_ml, out, c.H_q, c.H_kv, c.d, p.splits);
   return hipGetLastError();
 }

@@ -19,9 +19,11 @@ hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* 
                              hipStream_t stream);
 
 struct DecodePlan {
-  int splits;           // split-K partitions per (sequence, KV head)
-  int blocks_per_split; // cache blocks (sink block, pages, residual block) per partition
-  size_t ws_bytes;
+  int splits;           // split-K partitions per (sequence, KV head): page splits + 1 fp16 split
+  int page_splits;      // partitions over the packed pages
+  int pages_per_split;  // contiguous pages per page partition
+  size_t ws_bytes;      // workspace for the partials
+  size_t lds_bytes;     // dynamic LDS of the split kernel
 };
 DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages);
 hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_t* q,

@@ -53,6 +53,8 @@ pnmix_status check(const pnmix_cfg* c) {
   if (c->g_V <= 0 || c->d % c->g_V) return fail(PNMIX_E_INVALID, "g_V = %d does not divide d", c->g_V);
   if (c->g_V != 16 && c->g_V != 32 && c->g_V != 64 && c->g_V != 128)
     return fail(PNMIX_E_UNSUPPORTED, "g_V = %d not in {16, 32, 64, 128}", c->g_V);
+  if (c->d / c->g_V > 4)
+    return fail(PNMIX_E_UNSUPPORTED, "d / g_V = %d value groups per token (at most 4)", c->d / c->g_V);
   if (c->N_s < 0 || c->N_s > 128) return fail(PNMIX_E_INVALID, "N_s = %d outside [0, 128]", c->N_s);
   return PNMIX_OK;
 }
@@ -158,7 +160,11 @@ pnmix_status pnmix_decode_attn(const pnmix_cfg* c, int32_t B, int32_t max_pages,
   if (max_pages > 0 && (!k_pages || !v_pages))
     return fail(PNMIX_E_INVALID, "k_pages and v_pages must be non-NULL when max_pages > 0");
   if (!std::isfinite(sm_scale)) return fail(PNMIX_E_INVALID, "sm_scale is not finite");
-  const size_t need = pnmix::decode_plan(*c, B, max_pages).ws_bytes;
+  const pnmix::DecodePlan plan = pnmix::decode_plan(*c, B, max_pages);
+  if (plan.lds_bytes > 65536)
+    return fail(PNMIX_E_UNSUPPORTED, "n_g = %d with G = %d needs %zu bytes of LDS (> 64 KiB)",
+                c->H_q / c->H_kv, c->G, plan.lds_bytes);
+  const size_t need = plan.ws_bytes;
   if (ws_bytes < need)
     return fail(PNMIX_E_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(pnmix::launch_decode(*c, B, max_pages, q, k_sink, v_sink, k_pages, v_pages,

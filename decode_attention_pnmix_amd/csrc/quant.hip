@@ -139,8 +139,8 @@ __global__ void __launch_bounds__(kQuantThreads) quantize_v_kernel(const pnmix_p
   __syncthreads();
   const int ng = d / g_V;
   uint8_t* codes = job.dst;
-  uint16_t* S = reinterpret_cast<uint16_t*>(codes + kN * d / 4);
-  uint16_t* Z = S + kN * ng;
+  uint16_t* S = reinterpret_cast<uint16_t*>(codes + kN * d / 4);  // [ng][N]
+  uint16_t* Z = S + kN * ng;                                        // [ng][N]
   for (int it = threadIdx.x; it < kN * ng; it += blockDim.x) {
     const int gi = it % ng, t = it / ng;
     const uint16_t* row = tile + t * d + gi * g_V;
@@ -155,10 +155,10 @@ __global__ void __launch_bounds__(kQuantThreads) quantize_v_kernel(const pnmix_p
       uint32_t byte = 0u;
       for (int u = 0; u < 4; ++u) byte |= group_code(q, h2f(row[4 * m + u])) << (2 * u);
       const int mcol = gi * g_V / 4 + m;
-      codes[((t / 16) * (d / 4) + mcol) * 16 + (t % 16)] = (uint8_t)byte;
+      codes[((t / 8) * (d / 4) + mcol) * 8 + (t % 8)] = (uint8_t)byte;
     }
-    S[t * ng + gi] = q.S;
-    Z[t * ng + gi] = q.Z;
+    S[gi * kN + t] = q.S;
+    Z[gi * kN + t] = q.Z;
   }
 }
 

@@ -59,7 +59,7 @@ typedef enum {
 /* Problem statement of one attention layer ([PNMIX] sec. 2 and 5; [REPRO]).
  * Supported: H_q % H_kv == 0 with n_g = H_q / H_kv <= 16; d in {32, 64, 128};
  * 0 <= n_hi_pairs <= d/2; N == 128; G in {32, 64, 128}; (b_H, b_L) == (3, 1); b_V == 2;
- * g_V in {16, 32, 64, 128} dividing d; 0 <= N_s <= 128. */
+ * g_V in {16, 32, 64, 128} dividing d with d / g_V <= 4 value groups per token; 0 <= N_s <= 128. */
 typedef struct {
   int32_t H_q, H_kv, d, pairing;
   int32_t n_hi_pairs; /* floor(r * d / 2): pnmix_hi_pairs(r, d) */
@@ -143,9 +143,9 @@ pnmix_status pnmix_quantize_k_page(const pnmix_cfg* cfg, int32_t n_pages,
 /* Value page quantization and packing ([PNMIX] sec. 2 and kernel-implementation appendix;
  * [SUMMARY]): per token and channel group of g_V channels, Eq. 2 at b_V = 2 bits with the
  * constant rule; stored S = h(s), Z = h(mn).  Layout:
- *   codes [N/16][d/4][16]  byte [j][m][k] = channels 4m..4m+3 of token 16j+k, channel 4m+u
- *                          in bits 2u..2u+1
- *   S [N][d/g_V] fp16, then Z [N][d/g_V] fp16.
+ *   codes [N/8][d/4][8]  byte [j][m][k] = channels 4m..4m+3 of token 8j+k, channel 4m+u in
+ *                        bits 2u..2u+1
+ *   S [d/g_V][N] fp16, then Z [d/g_V][N] fp16 (group-major: one group's N tokens contiguous).
  * Bit-exact with the reference oracle. */
 pnmix_status pnmix_quantize_v_page(const pnmix_cfg* cfg, int32_t n_pages,
                                    const pnmix_page* pages, void* stream);

@@ -127,7 +127,7 @@ int64_t orc_k_page_bytes(const orc_cfg* c) {
          2 * 2 * (int64_t)(c->N / c->G) * c->d;
 }
 
-/* V page: codes [N/16][d/4][16] + S [N][d/g_V] + Z [N][d/g_V] (fp16) */
+/* V page: codes [N/8][d/4][8] + S [d/g_V][N] + Z [d/g_V][N] (fp16) */
 int64_t orc_v_page_bytes(const orc_cfg* c) {
   return (int64_t)c->N * c->d * c->b_V / 8 + 2 * 2 * (int64_t)c->N * (c->d / c->g_V);
 }
@@ -335,8 +335,8 @@ int orc_quantize_k_page(const orc_cfg* c, const uint16_t* src, int64_t src_row_s
 /* V page ([PNMIX] sec. 2 and kernel-implementation appendix; [SUMMARY]): values are
  * quantized per token over channel groups of g_V at b_V = 2 bits (Eq. 2, constant rule);
  * every 4 consecutive channels of one token share a byte, channel 4m + u in bits
- * 2u..2u+1.  Bytes are arranged [N/16][d/4][16]: byte [j][m][k] belongs to token 16j + k.
- * Then S[t][g], Z[t][g] as little-endian fp16 ([N][d/g_V] each). */
+ * 2u..2u+1.  Bytes are arranged [N/8][d/4][8]: byte [j][m][k] belongs to token 8j + k.
+ * Then S[g][t], Z[g][t] as little-endian fp16 ([d/g_V][N] each, group-major). */
 int orc_quantize_v_page(const orc_cfg* c, const uint16_t* src, int64_t src_row_stride,
                         uint8_t* dst) {
   if (orc_check_cfg(c) || !src || !dst) return 1;
@@ -350,14 +350,14 @@ int orc_quantize_v_page(const orc_cfg* c, const uint16_t* src, int64_t src_row_s
     for (int32_t g = 0; g < ng; ++g) {
       group_meta m = quantize_group(src + (int64_t)t * src_row_stride + g * c->g_V, 1, c->g_V,
                                     c->b_V, codes + (int64_t)t * d + g * c->g_V, 1);
-      put_f16(Sp + 2 * ((int64_t)t * ng + g), m.S);
-      put_f16(Zp + 2 * ((int64_t)t * ng + g), m.Z);
+      put_f16(Sp + 2 * ((int64_t)g * N + t), m.S);
+      put_f16(Zp + 2 * ((int64_t)g * N + t), m.Z);
     }
   }
   memset(cb, 0, (size_t)N * d / 4);
   for (int32_t t = 0; t < N; ++t)
     for (int32_t ch = 0; ch < d; ++ch)
-      cb[((t / 16) * (d / 4) + ch / 4) * 16 + (t % 16)] |=
+      cb[((t / 8) * (d / 4) + ch / 4) * 8 + (t % 8)] |=
           (uint8_t)((codes[t * d + ch] & 3u) << (2 * (ch % 4)));
   free(codes);
   return 0;
@@ -407,11 +407,13 @@ int orc_unpack_v_page(const orc_cfg* c, const uint8_t* page, uint8_t* codes, uin
     for (int32_t t = 0; t < N; ++t)
       for (int32_t ch = 0; ch < d; ++ch)
         codes[t * d + ch] =
-            (uint8_t)((cb[((t / 16) * (d / 4) + ch / 4) * 16 + (t % 16)] >> (2 * (ch % 4))) & 3u);
-  for (int32_t i = 0; i < N * ng; ++i) {
-    if (S) S[i] = get_f16(Sp + 2 * i);
-    if (Z) Z[i] = get_f16(Zp + 2 * i);
-  }
+            (uint8_t)((cb[((t / 8) * (d / 4) + ch / 4) * 8 + (t % 8)] >> (2 * (ch % 4))) & 3u);
+  /* S, Z are returned per token, [N][d/g_V], from the group-major storage */
+  for (int32_t t = 0; t < N; ++t)
+    for (int32_t g = 0; g < ng; ++g) {
+      if (S) S[t * ng + g] = get_f16(Sp + 2 * ((int64_t)g * N + t));
+      if (Z) Z[t * ng + g] = get_f16(Zp + 2 * ((int64_t)g * N + t));
+    }
   return 0;
 }
 

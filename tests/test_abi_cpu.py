@@ -49,6 +49,7 @@ def _cfg(**kw):
     ({"b_H": 4, "b_L": 2}, L.PNMIX_E_UNSUPPORTED),
     ({"b_V": 4}, L.PNMIX_E_UNSUPPORTED),
     ({"g_V": 24}, L.PNMIX_E_INVALID),
+    ({"g_V": 16}, L.PNMIX_E_UNSUPPORTED),
     ({"N": 64}, L.PNMIX_E_UNSUPPORTED),
     ({"N_s": -1}, L.PNMIX_E_INVALID),
     ({"d": 32, "g_V": 32, "n_hi_pairs": 8, "pairing": 0, "H_q": 4, "H_kv": 2}, L.PNMIX_OK),

@@ -51,12 +51,13 @@ def test_golden_v_page(orc):
         src[t, 4:] = [t / 2] * 4 if t % 2 == 0 else [-3, 3, -2, 2]
     page = orc.quantize_v_page(cfg, src.view(np.uint16))
     codes = _hexbytes(vv["codes_hex"])
-    S = np.zeros((cfg.N, 2), np.uint16)
-    Z = np.zeros((cfg.N, 2), np.uint16)
+    # S and Z are stored group-major: [d/g_V][N]
+    S = np.zeros((2, cfg.N), np.uint16)
+    Z = np.zeros((2, cfg.N), np.uint16)
     zeven = _hexf16(vv["Z_f16_hex_group1_even_tokens"])
     for t in range(cfg.N):
-        S[t] = [0x3C00, 0x0000 if t % 2 == 0 else 0x4000]
-        Z[t] = [0x0000, zeven[t // 2] if t % 2 == 0 else 0xC200]
+        S[:, t] = [0x3C00, 0x0000 if t % 2 == 0 else 0x4000]
+        Z[:, t] = [0x0000, zeven[t // 2] if t % 2 == 0 else 0xC200]
     assert np.array_equal(page, np.concatenate([codes, S.reshape(-1).view(np.uint8),
                                                 Z.reshape(-1).view(np.uint8)]))
 

@@ -205,7 +205,8 @@ def pnmix_decode_attn(cfg, q, k_sink, v_sink, k_pages, v_pages, k_res, v_res, le
                       ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """q [B][H_q][d] fp16; sinks [B][H_kv][N_s][d]; pages [B][H_kv][max_pages][bytes] u8;
     residual [B][H_kv][N][d]; lens [B][4] int32 (sink_len, n_pages, res_len, 0);
-    mask [B][H_kv][words] -> out [B][H_q][d] f32."""
+    mask [B][H_kv][words] -> out [B][H_q][d] f32.  ws, when given, is a device byte buffer of
+    at least pnmix_decode_workspace_bytes(...) bytes that holds the split-K partials."""
     B = q.shape[0]
     max_pages = k_pages.shape[2]
     _expect(q, (B, cfg.H_q, cfg.d), _F16, "q")

@@ -62,6 +62,7 @@ struct DecodeArgs {
   const uint32_t* mask;
   float* part_o;   // [B*H_kv][splits][n_g][d]
   float* part_ml;  // [B*H_kv][splits][n_g][2]
+  float* out;      // [B][H_q][d]
   float qscale;    // sm_scale * log2(e)
   int H_q, H_kv, n_g, pairing, n_hi, n_sal, G, KG, g_V, NGV, N_s, max_pages, words;
   int64_t kpb, vpb;
@@ -348,32 +349,16 @@ __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, int64
   }
 }
 
-// The fp16 split of every (sequence, KV head): its partial is split index page_splits.
-template <int D, int NT>
-__global__ void __launch_bounds__(64) decode_fp16_kernel(DecodeArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  const int64_t bh = blockIdx.x;
-  const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
-  const pnmix_seq_len L = a.lens[b];
-  const int sink_len = min(max(L.sink_len, 0), a.N_s);
-  const int res_len = min(max(L.res_len, 0), kN);
-  const int64_t pbase = (bh * a.splits + a.page_splits) * a.n_g;
-  fp16_region<D, NT>(a, b, h, bh, pbase, sink_len, res_len, lds);
-}
-
 // ----------------------------------------------------------------------------- page split
 
 template <int D, int NT, int KG>
-__global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
+__device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t bh) {
   using S_ = Shape<D>;
   constexpr int KL = S_::KL, KHM = S_::KHM, TL = S_::TL, NM0 = S_::NM0, JL = S_::JL;
   constexpr int NH = 4 * NT;
   constexpr int UK = (NT * D + 63) / 64;  // LSB prep units per lane
-  extern __shared__ __align__(16) uint8_t lds[];
 
   const int lane = threadIdx.x;
-  const int split = blockIdx.x;
-  const int64_t bh = blockIdx.y;
   const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
   const int ng = a.n_g;
   const pnmix_seq_len L = a.lens[b];
@@ -848,63 +833,61 @@ __global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
   }
 }
 
-// --------------------------------------------------------------------------------- merge
+// ----------------------------------------------------------------------------------- merge
 
-// One workgroup per (sequence, query head): 256 threads find the maximum over the splits, put
-// each split's weight 2^(m_s - m) in LDS, then sum the weighted outputs with the splits spread
-// over 256 / d groups of threads and add the group sums in a fixed order (deterministic).
-__global__ void __launch_bounds__(256) decode_merge_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml,
-                                                           float* __restrict__ out, int H_q,
-                                                           int H_kv, int d, int splits) {
-  __shared__ float wts[1024];
-  __shared__ float red[256];
-  __shared__ float osum[256];
+// Second launch: one workgroup of 64 per (sequence, query head, 32-channel block).  m = max m_s,
+// l = sum 2^(m_s - m) l_s, o = sum 2^(m_s - m) o_s / l (log2 units); lanes own one split each for
+// the weights, then 32 channels x 2 split halves for the sums, added in a fixed order.
+__global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a, int d) {
+  __shared__ float wts[64];
+  __shared__ float half[64];
+  const int lane = threadIdx.x;
   const int bhq = blockIdx.x;  // b * H_q + hq
-  const int b = bhq / H_q;
-  const int hq = bhq % H_q;
-  const int ng = H_q / H_kv;
+  const int b = bhq / a.H_q, hq = bhq % a.H_q;
+  const int ng = a.n_g, S = a.splits;
   const int h = hq / ng, hh = hq % ng;
-  const int64_t bh = (int64_t)b * H_kv + h;
-  const int tid = threadIdx.x;
-  float m = -INFINITY;
-  for (int s = tid; s < splits; s += 256) m = fmaxf(m, part_ml[((bh * splits + s) * ng + hh) * 2]);
-  red[tid] = m;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
+  const int64_t bh = (int64_t)b * a.H_kv + h;
+  float m = -INFINITY, l = 0.0f;
+  if (lane < S) {
+    const int64_t pi = (bh * S + lane) * ng + hh;
+    m = a.part_ml[pi * 2];
+    l = a.part_ml[pi * 2 + 1];
   }
-  m = red[0];
+  const float M = group_max<64>(m);
+  const float w = (lane < S && m != -INFINITY && M != -INFINITY) ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+  const float L = group_sum<64>(w * l);
+  wts[lane] = w;
   __syncthreads();
-  float lsum = 0.0f;
-  for (int s = tid; s < splits; s += 256) {
-    const int64_t p = (bh * splits + s) * ng + hh;
-    const float ms = part_ml[p * 2];
-    const float wv = (m == -INFINITY || ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - m);
-    if (s < 1024) wts[s] = wv;
-    lsum += wv * part_ml[p * 2 + 1];
-  }
-  red[tid] = lsum;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = red[tid] + red[tid + o];
-    __syncthreads();
-  }
-  const float l = red[0];
-  const int ngrp = 256 / d;  // d in {32, 64, 128}
-  const int c = tid % d, grp = tid / d;
+  const int c = 32 * blockIdx.y + (lane & 31), part = lane >> 5;
   float o = 0.0f;
-  for (int s = grp; s < splits; s += ngrp) {
-    const float wv = s < 1024 ? wts[s] : 0.0f;
-    if (wv != 0.0f) o += wv * part_o[((bh * splits + s) * ng + hh) * d + c];
+  if (c < d) {
+#pragma unroll 8
+    for (int s = part; s < S; s += 2) {
+      const float ws = wts[s];
+      if (ws != 0.0f) o += ws * a.part_o[((bh * S + s) * ng + hh) * d + c];
+    }
   }
-  osum[tid] = o;
+  half[lane] = o;
   __syncthreads();
-  if (tid < d) {
-    float t = 0.0f;
-    for (int g = 0; g < ngrp; ++g) t += osum[g * d + tid];
-    out[(int64_t)bhq * d + tid] = l > 0.0f ? t / l : 0.0f;
+  if (lane < 32 && c < d) a.out[(int64_t)bhq * d + c] = L > 0.0f ? (half[lane] + half[lane + 32]) / L : 0.0f;
+}
+
+// One launch per decode call: blockIdx.x < page_splits walks packed pages, blockIdx.x ==
+// page_splits takes the fp16 sink and residual rows, concurrently with the pages.
+template <int D, int NT, int KG>
+__global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int split = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  if (split < a.page_splits) {
+    page_split<D, NT, KG>(a, lds, split, bh);
+  } else {
+    const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
+    const pnmix_seq_len L = a.lens[b];
+    const int sink_len = min(max(L.sink_len, 0), a.N_s);
+    const int res_len = min(max(L.res_len, 0), kN);
+    fp16_region<D, NT>(a, b, h, bh, (bh * a.splits + a.page_splits) * a.n_g, sink_len, res_len,
+                       lds);
   }
 }
 
@@ -940,7 +923,7 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   const long long target = 2048;
   int ps = (int)std::max<long long>(1, target / std::max<long long>(items, 1) - 1);
   ps = std::min(ps, std::max(max_pages, 1));
-  ps = std::min(ps, 1023);  // the merge kernel keeps at most 1024 split weights in LDS
+  ps = std::min(ps, 63);  // the merge gives each split one lane: at most 64 splits
   int pps = max_pages > 0 ? (max_pages + ps - 1) / ps : 1;
   ps = max_pages > 0 ? (max_pages + pps - 1) / pps : 0;
   p.page_splits = ps;
@@ -957,14 +940,12 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
 template <int D, int NT, int KG>
 static hipError_t launch_k(const DecodePlan& p, int B, const pnmix_cfg& c, const DecodeArgs& a,
                            hipStream_t stream) {
-  if (p.page_splits > 0) {
-    hipLaunchKernelGGL((decode_kernel<D, NT, KG>), dim3(p.page_splits, B * c.H_kv), dim3(64),
-                       lds_bytes(c), stream, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((decode_fp16_kernel<D, NT>), dim3(B * c.H_kv), dim3(64), lds_fp16_bytes(c),
-                     stream, a);
+  hipLaunchKernelGGL((decode_kernel<D, NT, KG>), dim3(p.splits, B * c.H_kv), dim3(64),
+                     p.lds_bytes, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(B * c.H_q, (c.d + 31) / 32), dim3(64), 0, stream, a,
+                     c.d);
   return hipGetLastError();
 }
 
@@ -1009,6 +990,7 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
   a.part_o = static_cast<float*>(ws);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                        ((per * c.d * sizeof(float) + 255) & ~(size_t)255));
+  a.out = out;
   a.qscale = sm_scale * kLog2e;
   a.H_q = c.H_q;
   a.H_kv = c.H_kv;
@@ -1035,10 +1017,7 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
     case 64: e = launch_d<64>(p, B, c, a, stream); break;
     default: e = launch_d<128>(p, B, c, a, stream); break;
   }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(B * c.H_q), dim3(256), 0, stream, a.part_o,
-                     a.part_ml, out, c.H_q, c.H_kv, c.d, p.splits);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace pnmix

@@ -160,7 +160,8 @@ pnmix_status pnmix_quantize_v_page(const pnmix_cfg* cfg, int32_t n_pages,
  *   lens    [B] pnmix_seq_len; mask [B][H_kv][mask_words] (the rows the pages were packed with)
  *   out     [B][H_q][d] fp32: softmax(q k^T * sm_scale) v over sinks, pages (k = S q + Z with the
  *           stored fp16 S, Z), residual; query head h' reads KV head floor(h'/n_g).
- *   ws      pnmix_decode_workspace_bytes(cfg, B, max_pages) bytes of device scratch.
+ *   ws      pnmix_decode_workspace_bytes(cfg, B, max_pages) bytes of device scratch (split-K
+ *           partials); calls that share a workspace must not overlap.
  * A sequence with no tokens gets out = 0.  Accuracy: max |out - float64 reference| <= 2e-3 on
  * the supported workloads (fp32 softmax; exact integer products of codes). */
 pnmix_status pnmix_decode_attn(const pnmix_cfg* cfg, int32_t B, int32_t max_pages,

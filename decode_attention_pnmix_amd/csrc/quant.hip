@@ -3,179 +3,345 @@
 // PN-Mix paper (arXiv 2610.19605) sec. 2, Eq. 2: b-bit asymmetric min-max group quantization;
 // keys grouped per channel along tokens, values per token along channels.  Reproduction notes
 // ("PN-Mix: Key-Cache Precision Allocation from RoPE Channel-Pair Norms"), Core equations:
-// Eq. 7 midpoint correction of 1-bit groups, zero scale plus original offset for constant
+// Eq. 7 midpoint correction of 1-bit groups, zero scale plus the original offset for constant
 // groups, H3/L1 packing.  Kernel-implementation appendix of the paper: LSB plane of every key
 // channel at 8 tokens per byte, upper-2-bit plane of salient channels at 4 tokens per byte,
 // values at 4 channels per byte.
 //
-// One workgroup per page job.  The page's N x d fp16 tile is staged in LDS with 16-byte loads
-// (each byte of the source read once), then each thread owns (channel, token group) items for
-// keys or (token, channel group) items for values: exact min/max, one IEEE divide and one IEEE
-// reciprocal per group, then per element sub, mul, round-half-even, clamp -- the reference
-// arithmetic, so codes and fp16 metadata are bit-identical to the oracle.
+// One workgroup of 2d threads per page; thread (octet k, block b) holds tokens 8k..8k+7 x
+// channels 8b..8b+7 of the N x d fp16 page in registers, read with one 16-byte load per token
+// straight from HBM (each source byte read once, no LDS copy of the tile).
+//   A. min / max of the thread's 8 x 8 values with packed fp16 min/max (exact), partials to LDS
+//      (keys: per channel over the 8 tokens; values: per token over the 8 channels).
+//   B. one thread per quantization group folds its partials, then takes the fp32 metadata
+//      path of Eq. 2 / Eq. 7 (one IEEE divide, one IEEE reciprocal) and stores S, Z; the
+//      group's (min, 1/s) go back through LDS.
+//   C. per element q = rne(clamp((x - min) * (1/s), 0, L)): the clamp bounds are integers, so
+//      clamping before rounding gives the same code as rounding first, and adding 2^23 to a
+//      value in [0, L] rounds it to the nearest even integer and leaves it in the low
+//      mantissa bits.  Codes are packed in registers and stored as whole 8- or 16-byte runs;
+//      the upper-bit plane is gathered in LDS by salient rank and copied out 16 bytes a lane.
+// Every float step is the reference arithmetic, so codes and fp16 metadata are bit-identical.
 #include "common.h"
 #include "kernels.h"
 
 namespace pnmix {
 
-constexpr int kQuantThreads = 256;
-constexpr int kMaxD = 128;
 constexpr int kN = 128;
+constexpr int kOctets = kN / 8;
+constexpr float kRound = 8388608.0f;  // 2^23
 
-// Copy one N x d fp16 page (row stride in elements) into LDS, 16 bytes per access when the
-// source is 16-byte aligned with a stride that keeps rows aligned, else 2 bytes per access.
-__device__ __forceinline__ void stage_page(uint16_t* tile, const uint16_t* src, int64_t stride,
-                                           int d) {
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t as_u(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
+  return as_u(__builtin_elementwise_min(as_h2(a), as_h2(b)));
+}
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+  return as_u(__builtin_elementwise_max(as_h2(a), as_h2(b)));
+}
+__device__ __forceinline__ float lo_f(uint32_t u) { return h2f((uint16_t)(u & 0xffffu)); }
+__device__ __forceinline__ float hi_f(uint32_t u) { return h2f((uint16_t)(u >> 16)); }
+// bytes of a and b: (a.b0, b.b0, a.b1... ) helpers via v_perm_b32 (selector bytes 0-3 = b,
+// 4-7 = a)
+__device__ __forceinline__ uint32_t perm(uint32_t a, uint32_t b, uint32_t sel) {
+  return __builtin_amdgcn_perm(a, b, sel);
+}
+// low bytes of four words -> one word (w0 in byte 0)
+__device__ __forceinline__ uint32_t gather_b0(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  const uint32_t p01 = perm(w1, w0, 0x0c0c0400u);  // [w0.b0, w1.b0, 0, 0]
+  const uint32_t p23 = perm(w3, w2, 0x0c0c0400u);
+  return perm(p23, p01, 0x05040100u);
+}
+
+// The 8 token rows 8k..8k+7, channels 8b..8b+7: x[j] = 8 fp16 of token 8k+j.
+__device__ __forceinline__ void load_block(uint4 (&x)[8], const uint16_t* src, int64_t stride,
+                                           int k, int b) {
   const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0) && ((stride & 7) == 0);
+  const uint16_t* p = src + (int64_t)(8 * k) * stride + 8 * b;
   if (vec) {
-    const int per_row = d / 8;
-    for (int i = threadIdx.x; i < kN * per_row; i += blockDim.x) {
-      const int t = i / per_row, c8 = i % per_row;
-      const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)t * stride + c8 * 8);
-      *reinterpret_cast<uint4*>(tile + t * d + c8 * 8) = v;
-    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const uint4*>(p + (int64_t)j * stride);
   } else {
-    for (int i = threadIdx.x; i < kN * d; i += blockDim.x) {
-      const int t = i / d, c = i % d;
-      tile[t * d + c] = src[(int64_t)t * stride + c];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t w[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        w[m] = (uint32_t)p[(int64_t)j * stride + 2 * m] |
+               ((uint32_t)p[(int64_t)j * stride + 2 * m + 1] << 16);
+      x[j] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
 
-struct GroupQ {
-  float mn, inv;
-  int L;
-  bool constant;
-  uint16_t S, Z;
-};
+__device__ __forceinline__ uint32_t word(const uint4& v, int m) {
+  return m == 0 ? v.x : m == 1 ? v.y : m == 2 ? v.z : v.w;
+}
 
-// Eq. 2 / Eq. 7 metadata of one group from its exact min and max.
-__device__ __forceinline__ GroupQ group_params(float mn, float mx, int bits) {
-  GroupQ g;
-  g.mn = canon(mn);
+// Eq. 2 / Eq. 7 metadata of one group with exact min mn and max mx; returns (mn, 1/s) with
+// 1/s = 0 for a constant group (all codes then come out 0).
+__device__ __forceinline__ float2 group_meta(float mn, float mx, int L, uint16_t& S,
+                                             uint16_t& Z) {
+  mn = canon(mn);
   mx = canon(mx);
-  g.L = (1 << bits) - 1;
-  g.constant = (mx == g.mn);
-  if (g.constant) {
-    g.inv = 0.0f;
-    g.S = 0;
-    g.Z = f2h(g.mn);
-    return g;
+  if (mx == mn) {
+    S = 0;
+    Z = f2h(mn);
+    return make_float2(mn, 0.0f);
   }
-  const float s = (mx - g.mn) / (float)g.L;
-  g.inv = 1.0f / s;
-  if (g.L == 1) {
-    const float s7 = (mx - g.mn) * 0.5f;
-    const float t3 = 3.0f * g.mn;
+  const float s = (mx - mn) / (float)L;
+  const float inv = 1.0f / s;
+  if (L == 1) {
+    const float s7 = (mx - mn) * 0.5f;
+    const float t3 = 3.0f * mn;
     const float z7 = (t3 + mx) * 0.25f;
-    g.S = f2h(s7);
-    g.Z = f2h(z7);
+    S = f2h(s7);
+    Z = f2h(z7);
   } else {
-    g.S = f2h(s);
-    g.Z = f2h(g.mn);
+    S = f2h(s);
+    Z = f2h(mn);
   }
-  return g;
+  return make_float2(mn, inv);
 }
 
-__device__ __forceinline__ uint32_t group_code(const GroupQ& g, float x) {
-  if (g.constant) return 0u;
-  float r = rintf((x - g.mn) * g.inv);
-  r = fminf(fmaxf(r, 0.0f), (float)g.L);
-  return (uint32_t)(int)r;
+// Code of one element as the float 2^23 + q (q in the low mantissa bits).
+__device__ __forceinline__ uint32_t code_bits(float x, float mn, float inv, float L) {
+  const float y = (x - mn) * inv;
+  return __float_as_uint(__builtin_amdgcn_fmed3f(y, 0.0f, L) + kRound);
 }
 
-__global__ void __launch_bounds__(kQuantThreads) quantize_k_kernel(const pnmix_page* __restrict__ jobs,
-                                                                   const uint32_t* __restrict__ mask,
-                                                                   int d, int pairing, int n_hi,
-                                                                   int G, int words) {
-  __shared__ __align__(16) uint16_t tile[kN * kMaxD];
+template <int D>
+__global__ void __launch_bounds__(2 * D) quantize_k_kernel(const pnmix_page* __restrict__ jobs,
+                                                          const uint32_t* __restrict__ mask,
+                                                          int pairing, int n_hi, int G,
+                                                          int words) {
+  constexpr int NB = D / 8;
+  __shared__ __align__(16) uint32_t part[kOctets * D];  // (min, max) fp16 per octet, channel
+  __shared__ __align__(16) float2 meta[(kN / 32) * D];  // (min, 1/s) per group, channel
+  __shared__ __align__(16) uint8_t hi_s[(kN / 4) * D];  // upper-bit plane staging
+  __shared__ __align__(8) int8_t rank_s[D];
+  const int tid = threadIdx.x, b = tid % NB, k = tid / NB;
   const pnmix_page job = jobs[blockIdx.x];
-  stage_page(tile, job.src, job.src_row_stride, d);
-  __syncthreads();
-  const uint32_t* mrow = mask + job.mask_row * words;
   const int n_sal = 2 * n_hi;
   uint8_t* lo = job.dst;
-  uint8_t* hi = lo + kN * d / 8;
+  uint8_t* hi = lo + kN * D / 8;
   uint16_t* S = reinterpret_cast<uint16_t*>(hi + kN * n_sal / 4);
-  uint16_t* Z = S + (kN / G) * d;
-  const int items = d * (kN / G);
-  for (int it = threadIdx.x; it < items; it += blockDim.x) {
-    const int c = it % d, g = it / d;
-    const int rank = salient_rank(mrow, c, d, pairing, n_hi);
-    const uint16_t* col = tile + g * G * d + c;
-    float mn = h2f(col[0]), mx = mn;
-    for (int t = 1; t < G; ++t) {
-      const float v = h2f(col[t * d]);
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
-    }
-    const GroupQ q = group_params(mn, mx, rank >= 0 ? 3 : 1);
-    for (int j = 0; j < G / 8; ++j) {
-      uint32_t lob = 0u, hib0 = 0u, hib1 = 0u;
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t code = group_code(q, h2f(col[(8 * j + k) * d]));
-        lob |= (code & 1u) << k;
-        if (k < 4)
-          hib0 |= (code >> 1) << (2 * k);
-        else
-          hib1 |= (code >> 1) << (2 * (k - 4));
+  uint16_t* Z = S + (kN / G) * D;
+
+  uint4 x[8];
+  load_block(x, job.src, job.src_row_stride, k, b);
+
+  // A: per channel min / max over the 8 tokens
+  {
+    uint32_t pm[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t mn = word(x[0], m), mx = mn;
+#pragma unroll
+      for (int j = 1; j < 8; ++j) {
+        mn = pk_min(mn, word(x[j], m));
+        mx = pk_max(mx, word(x[j], m));
       }
-      lo[(g * G / 8 + j) * d + c] = (uint8_t)lob;
-      if (rank >= 0) {
-        hi[(g * G / 4 + 2 * j) * n_sal + rank] = (uint8_t)hib0;
-        hi[(g * G / 4 + 2 * j + 1) * n_sal + rank] = (uint8_t)hib1;
-      }
+      pm[2 * m] = perm(mx, mn, 0x05040100u);      // channel 2m: (min.lo, max.lo)
+      pm[2 * m + 1] = perm(mx, mn, 0x07060302u);  // channel 2m+1: (min.hi, max.hi)
     }
-    S[g * d + c] = q.S;
-    Z[g * d + c] = q.Z;
+    uint4* dst = reinterpret_cast<uint4*>(part + k * D + 8 * b);
+    dst[0] = make_uint4(pm[0], pm[1], pm[2], pm[3]);
+    dst[1] = make_uint4(pm[4], pm[5], pm[6], pm[7]);
   }
+  const uint32_t* mrow = mask + job.mask_row * words;
+  if (tid < D) rank_s[tid] = (int8_t)salient_rank(mrow, tid, D, pairing, n_hi);
+  __syncthreads();
+
+  // B: one thread per (token group, channel)
+  const int og = G / 8;  // octets per group
+  for (int it = tid; it < (kN / G) * D; it += 2 * D) {
+    const int g = it / D, c = it % D;
+    float mn = lo_f(part[g * og * D + c]), mx = hi_f(part[g * og * D + c]);
+    for (int o = 1; o < og; ++o) {
+      const uint32_t v = part[(g * og + o) * D + c];
+      mn = fminf(mn, lo_f(v));
+      mx = fmaxf(mx, hi_f(v));
+    }
+    const int L = rank_s[c] >= 0 ? 7 : 1;
+    uint16_t s, z;
+    meta[g * D + c] = group_meta(mn, mx, L, s, z);
+    S[g * D + c] = s;
+    Z[g * D + c] = z;
+  }
+  __syncthreads();
+
+  // C: codes of the thread's 8 channels x 8 tokens
+  const int g = k / og;
+  float2 mt[8];
+  {
+    const float4* src = reinterpret_cast<const float4*>(meta + g * D + 8 * b);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = src[q];
+      mt[2 * q] = make_float2(v.x, v.y);
+      mt[2 * q + 1] = make_float2(v.z, v.w);
+    }
+  }
+  int8_t rk[8];
+  {
+    const uint2 r = *reinterpret_cast<const uint2*>(rank_s + 8 * b);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) rk[s] = (int8_t)(((s < 4 ? r.x : r.y) >> (8 * (s & 3))) & 0xff);
+  }
+  uint32_t lsb[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int m = s >> 1;
+    const float L = rk[s] >= 0 ? 7.0f : 1.0f;
+    uint32_t u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = word(x[j], m);
+      u[j] = code_bits((s & 1) ? hi_f(w) : lo_f(w), mt[s].x, mt[s].y, L);
+    }
+    // nibbles of tokens 0-3 and 4-7 in the low 16 bits (float exponent bits land >= bit 24)
+    uint32_t wl = u[3], wh = u[7];
+#pragma unroll
+    for (int j = 2; j >= 0; --j) {
+      wl = (wl << 4) | u[j];
+      wh = (wh << 4) | u[j + 4];
+    }
+    const uint32_t nib = perm(wh, wl, 0x05040100u);  // token j in bits 4j..4j+2
+    // LSB plane byte: bit j = code_j & 1
+    uint32_t t = nib & 0x11111111u;
+    t = (t | (t >> 3)) & 0x03030303u;
+    t = (t | (t >> 6)) & 0x000f000fu;
+    lsb[s] = t | (t >> 12);
+    if (rk[s] >= 0) {
+      // upper-bit plane: tokens 0-3 then 4-7, 2 bits each
+      uint32_t h = (nib >> 1) & 0x33333333u;
+      h = (h | (h >> 2)) & 0x0f0f0f0fu;
+      h = (h | (h >> 4));
+      hi_s[(2 * k) * n_sal + rk[s]] = (uint8_t)h;
+      hi_s[(2 * k + 1) * n_sal + rk[s]] = (uint8_t)(h >> 16);
+    }
+  }
+  {
+    const uint32_t w0 = gather_b0(lsb[0], lsb[1], lsb[2], lsb[3]);
+    const uint32_t w1 = gather_b0(lsb[4], lsb[5], lsb[6], lsb[7]);
+    *reinterpret_cast<uint2*>(lo + k * D + 8 * b) = make_uint2(w0, w1);
+  }
+  __syncthreads();
+  const int hi_chunks = (kN / 4) * n_sal / 16;
+  for (int i = tid; i < hi_chunks; i += 2 * D)
+    reinterpret_cast<uint4*>(hi)[i] = reinterpret_cast<const uint4*>(hi_s)[i];
 }
 
-__global__ void __launch_bounds__(kQuantThreads) quantize_v_kernel(const pnmix_page* __restrict__ jobs,
-                                                                   int d, int g_V) {
-  __shared__ __align__(16) uint16_t tile[kN * kMaxD];
+template <int D>
+__global__ void __launch_bounds__(2 * D) quantize_v_kernel(const pnmix_page* __restrict__ jobs,
+                                                          int g_V) {
+  constexpr int NB = D / 8;
+  __shared__ __align__(16) uint32_t part[kN * NB];  // (min, max) fp16 per token, block
+  __shared__ __align__(16) float2 meta[kN * 4];     // (min, 1/s) per token, group (<= 4)
+  const int tid = threadIdx.x, b = tid % NB, k = tid / NB;
   const pnmix_page job = jobs[blockIdx.x];
-  stage_page(tile, job.src, job.src_row_stride, d);
-  __syncthreads();
-  const int ng = d / g_V;
+  const int ng = D / g_V;
   uint8_t* codes = job.dst;
-  uint16_t* S = reinterpret_cast<uint16_t*>(codes + kN * d / 4);  // [ng][N]
+  uint16_t* S = reinterpret_cast<uint16_t*>(codes + kN * D / 4);  // [ng][N]
   uint16_t* Z = S + kN * ng;                                        // [ng][N]
-  for (int it = threadIdx.x; it < kN * ng; it += blockDim.x) {
-    const int gi = it % ng, t = it / ng;
-    const uint16_t* row = tile + t * d + gi * g_V;
-    float mn = h2f(row[0]), mx = mn;
-    for (int c = 1; c < g_V; ++c) {
-      const float v = h2f(row[c]);
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
-    }
-    const GroupQ q = group_params(mn, mx, 2);
-    for (int m = 0; m < g_V / 4; ++m) {
-      uint32_t byte = 0u;
-      for (int u = 0; u < 4; ++u) byte |= group_code(q, h2f(row[4 * m + u])) << (2 * u);
-      const int mcol = gi * g_V / 4 + m;
-      codes[((t / 8) * (d / 4) + mcol) * 8 + (t % 8)] = (uint8_t)byte;
-    }
-    S[gi * kN + t] = q.S;
-    Z[gi * kN + t] = q.Z;
+
+  uint4 x[8];
+  load_block(x, job.src, job.src_row_stride, k, b);
+
+  // A: per token min / max over the thread's 8 channels
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t mn2 = pk_min(pk_min(x[j].x, x[j].y), pk_min(x[j].z, x[j].w));
+    const uint32_t mx2 = pk_max(pk_max(x[j].x, x[j].y), pk_max(x[j].z, x[j].w));
+    const _Float16 mn = __builtin_elementwise_min(as_h2(mn2).x, as_h2(mn2).y);
+    const _Float16 mx = __builtin_elementwise_max(as_h2(mx2).x, as_h2(mx2).y);
+    part[(8 * k + j) * NB + b] = (uint32_t)__builtin_bit_cast(uint16_t, mn) |
+                                 ((uint32_t)__builtin_bit_cast(uint16_t, mx) << 16);
   }
+  __syncthreads();
+
+  // B: one thread per (token, channel group)
+  const int bg = g_V / 8;  // blocks per group
+  for (int it = tid; it < kN * ng; it += 2 * D) {
+    const int t = it % kN, gi = it / kN;
+    const uint32_t* pr = part + t * NB + gi * bg;
+    float mn = lo_f(pr[0]), mx = hi_f(pr[0]);
+    for (int o = 1; o < bg; ++o) {
+      mn = fminf(mn, lo_f(pr[o]));
+      mx = fmaxf(mx, hi_f(pr[o]));
+    }
+    uint16_t s, z;
+    meta[t * 4 + gi] = group_meta(mn, mx, 3, s, z);
+    S[gi * kN + t] = s;
+    Z[gi * kN + t] = z;
+  }
+  __syncthreads();
+
+  // C: two 4-channel columns x 8 tokens -> 16 contiguous bytes of [N/8][d/4][8]
+  const int gi = b / bg;
+  uint32_t byte[2][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float2 mt = meta[(8 * k + j) * 4 + gi];
+#pragma unroll
+    for (int col = 0; col < 2; ++col) {
+      const uint32_t w0 = col ? x[j].z : x[j].x, w1 = col ? x[j].w : x[j].y;
+      const uint32_t u0 = code_bits(lo_f(w0), mt.x, mt.y, 3.0f);
+      const uint32_t u1 = code_bits(hi_f(w0), mt.x, mt.y, 3.0f);
+      const uint32_t u2 = code_bits(lo_f(w1), mt.x, mt.y, 3.0f);
+      const uint32_t u3 = code_bits(hi_f(w1), mt.x, mt.y, 3.0f);
+      // channel u at bits 2u of the low byte (float exponent bits land >= bit 24)
+      byte[col][j] = (((((u3 << 2) | u2) << 2) | u1) << 2) | u0;
+    }
+  }
+  uint4 outv;
+  outv.x = gather_b0(byte[0][0], byte[0][1], byte[0][2], byte[0][3]);
+  outv.y = gather_b0(byte[0][4], byte[0][5], byte[0][6], byte[0][7]);
+  outv.z = gather_b0(byte[1][0], byte[1][1], byte[1][2], byte[1][3]);
+  outv.w = gather_b0(byte[1][4], byte[1][5], byte[1][6], byte[1][7]);
+  *reinterpret_cast<uint4*>(codes + (k * (D / 4) + 2 * b) * 8) = outv;
 }
 
 hipError_t launch_quantize_k(const pnmix_cfg& c, int n_pages, const pnmix_page* pages,
                              const uint32_t* mask, hipStream_t stream) {
   if (n_pages == 0) return hipSuccess;
   const int words = (c.d / 2 + 31) / 32;
-  hipLaunchKernelGGL(quantize_k_kernel, dim3(n_pages), dim3(kQuantThreads), 0, stream, pages,
-                     mask, c.d, c.pairing, c.n_hi_pairs, c.G, words);
+  switch (c.d) {
+    case 32:
+      hipLaunchKernelGGL(quantize_k_kernel<32>, dim3(n_pages), dim3(64), 0, stream, pages, mask,
+                         c.pairing, c.n_hi_pairs, c.G, words);
+      break;
+    case 64:
+      hipLaunchKernelGGL(quantize_k_kernel<64>, dim3(n_pages), dim3(128), 0, stream, pages,
+                         mask, c.pairing, c.n_hi_pairs, c.G, words);
+      break;
+    default:
+      hipLaunchKernelGGL(quantize_k_kernel<128>, dim3(n_pages), dim3(256), 0, stream, pages,
+                         mask, c.pairing, c.n_hi_pairs, c.G, words);
+      break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* pages,
                              hipStream_t stream) {
   if (n_pages == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_v_kernel, dim3(n_pages), dim3(kQuantThreads), 0, stream, pages,
-                     c.d, c.g_V);
+  switch (c.d) {
+    case 32:
+      hipLaunchKernelGGL(quantize_v_kernel<32>, dim3(n_pages), dim3(64), 0, stream, pages, c.g_V);
+      break;
+    case 64:
+      hipLaunchKernelGGL(quantize_v_kernel<64>, dim3(n_pages), dim3(128), 0, stream, pages,
+                         c.g_V);
+      break;
+    default:
+      hipLaunchKernelGGL(quantize_v_kernel<128>, dim3(n_pages), dim3(256), 0, stream, pages,
+                         c.g_V);
+      break;
+  }
   return hipGetLastError();
 }
 

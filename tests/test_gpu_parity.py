@@ -142,15 +142,16 @@ def test_quant_parity(name):
     _quant_compare(w, lc, oc, vp.reshape(n, w.N, w.d).contiguous(), mrow, sample, name + "/V")
 
 
-@pytest.mark.parametrize("G,d,pairing,r", [(128, 128, 1, 0.5), (64, 128, 1, 0.4),
-                                           (32, 64, 0, 0.25), (128, 32, 0, 1.0),
-                                           (64, 128, 0, 0.0)])
-def test_quant_adversarial_pages(G, d, pairing, r):
+@pytest.mark.parametrize("G,d,pairing,r,g_V", [(128, 128, 1, 0.5, 32), (64, 128, 1, 0.4, 128),
+                                               (32, 64, 0, 0.25, 16), (128, 32, 0, 1.0, 16),
+                                               (64, 128, 0, 0.0, 64), (32, 128, 1, 0.5, 32),
+                                               (64, 64, 1, 0.5, 64), (32, 32, 1, 0.0, 32)])
+def test_quant_adversarial_pages(G, d, pairing, r, g_V):
     """Constant channels and groups, signed zeros, +-65504, subnormals, exact midpoints and
-    random finite bit patterns."""
-    w = synth.Workload("adv", 1, 1, 8, 2, d, pairing, 1e4, 64, 512, r, G)
+    random finite bit patterns, over every supported token-group and value-group size."""
+    w = synth.Workload("adv", 1, 1, 8, 2, d, pairing, 1e4, 64, 512, r, G, g_V=g_V)
     lc, oc = cfgs(w)
-    say(f"[quant-adv] G={G} d={d} pairing={pairing} r={r}")
+    say(f"[quant-adv] G={G} d={d} pairing={pairing} r={r} g_V={g_V}")
     g = torch.Generator().manual_seed(G + d)
     n = 96
     x = torch.randn(n, 128, d, generator=g) * torch.exp(torch.randn(n, 1, d, generator=g) * 2)
@@ -178,6 +179,45 @@ def test_quant_adversarial_pages(G, d, pairing, r):
             masks[i, p // 32] |= 1 << (p % 32)
     masks = masks.to(torch.int32).cuda()
     _quant_compare(w, lc, oc, src, masks.contiguous(), np.arange(n), "adversarial")
+
+
+@pytest.mark.parametrize("pad,offset", [(8, 0), (3, 0), (0, 1), (136, 8), (0, 4)])
+def test_quant_strided_sources(pad, offset):
+    """Page rows read through a row stride of d + pad elements from a base offset by `offset`
+    elements: aligned strides take 16-byte loads, the others 2-byte loads; the packed pages
+    must not depend on which."""
+    w = synth.WORKLOADS["qwen3-8b-36L-b32-8k"]
+    lc, oc = cfgs(w)
+    say(f"[quant-stride] pad={pad} offset={offset}")
+    g = torch.Generator().manual_seed(pad * 7 + offset)
+    n, d = 24, w.d
+    stride = d + pad
+    flat = (torch.randn(offset + n * w.N * stride, generator=g) *
+            torch.exp(torch.randn(offset + n * w.N * stride, generator=g))).to(torch.float16)
+    flat_gpu = flat.cuda()
+    view = flat[offset:].view(n, w.N, stride)[:, :, :d].contiguous()
+    words = P.pnmix_mask_words(lc)
+    masks = torch.zeros(n, words, dtype=torch.int64)
+    for i in range(n):
+        for p in torch.randperm(d // 2, generator=g)[:w.n_hi_pairs].tolist():
+            masks[i, p // 32] |= 1 << (p % 32)
+    masks = masks.to(torch.int32).cuda()
+    kpb, vpb = P.pnmix_k_page_bytes(lc), P.pnmix_v_page_bytes(lc)
+    kd = torch.zeros(n, kpb, dtype=torch.uint8, device="cuda")
+    vd = torch.zeros(n, vpb, dtype=torch.uint8, device="cuda")
+    es = flat_gpu.element_size()
+    srcs = [flat_gpu.data_ptr() + (offset + i * w.N * stride) * es for i in range(n)]
+    kj = P.page_jobs(srcs, stride, [kd.data_ptr() + i * kpb for i in range(n)], range(n), "cuda")
+    vj = P.page_jobs(srcs, stride, [vd.data_ptr() + i * vpb for i in range(n)], range(n), "cuda")
+    P.pnmix_quantize_k_page(lc, kj, masks)
+    P.pnmix_quantize_v_page(lc, vj)
+    torch.cuda.synchronize()
+    sh = u16(view)
+    mh = masks.cpu().numpy().view(np.uint32)
+    kg, vg = kd.cpu().numpy(), vd.cpu().numpy()
+    for i in range(n):
+        assert np.array_equal(kg[i], oracle.quantize_k_page(oc, sh[i], mh[i])), f"K page {i}"
+        assert np.array_equal(vg[i], oracle.quantize_v_page(oc, sh[i])), f"V page {i}"
 
 
 # ----------------------------------------------------------------------------- decode attention

@@ -48,6 +48,7 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kN = 128;  // page and residual length
+constexpr int kMaxSplits = 256;  // split-K partitions per (sequence, KV head): one merge thread each
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeArgs {
@@ -167,6 +168,12 @@ __device__ __forceinline__ float sel4(const v4f& v, int i) {
 __device__ __forceinline__ uint32_t digits4(int x) {
   return ((uint32_t)x + 0x80808080u) ^ 0x80808080u;
 }
+// sum_d 256^d c[d] of four int32 digit partial sums, in fp32 (c[0] + 256 c[1] and
+// c[2] + 256 c[3] are formed exactly in int32 first: each |c[d]| < 2^22)
+__device__ __forceinline__ float combine4(const v4i& c) {
+  const int lo = c[0] + (c[1] << 8), hi = c[2] + (c[3] << 8);
+  return __builtin_fmaf((float)hi, 65536.0f, (float)lo);
+}
 // 4 x 4 byte transpose: out[d] byte i = byte d of y[i]
 __device__ __forceinline__ void transpose4(const uint32_t y[4], uint32_t out[4]) {
   const uint32_t t0 = __builtin_amdgcn_perm(y[1], y[0], 0x05010400u);
@@ -234,13 +241,14 @@ __device__ void write_empty_partial(const DecodeArgs& a, int64_t pbase) {
 
 // -------------------------------------------------------------- fp16 sink + residual split
 
-// One wave over the fp16 rows, 64 tokens per chunk (token order: sinks, then residual rows).
-// Every load of a chunk is issued at once: each lane's key row (one token per lane for the
+// One wave over the 64-token chunks chunk, chunk + n_chunk_splits, ... of the fp16 rows (token
+// order: sinks, then residual rows).  Every load of a chunk is issued at once: each lane's key row (one token per lane for the
 // logits) and the chunk's value rows, staged in LDS with coalesced 16-byte loads (one channel
 // pair per lane for p.V).  Logits go through LDS one head at a time to keep registers low.
 template <int D, int NT>
 __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, int64_t pbase,
-                            int sink_len, int res_len, uint8_t* lds) {
+                            int sink_len, int res_len, int chunk, int n_chunk_splits,
+                            uint8_t* lds) {
   constexpr int NH = 4 * NT;
   const int lane = threadIdx.x;
   const int ng = a.n_g;
@@ -262,13 +270,17 @@ __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, int64
     acc[i][0] = acc[i][1] = 0.0f;
   }
   const int T16 = sink_len + res_len;
+  if (64 * chunk >= T16) {
+    write_empty_partial<D>(a, pbase);
+    return;
+  }
   const uint16_t* ks = a.k_sink + bh * a.N_s * D;
   const uint16_t* vs = a.v_sink + bh * a.N_s * D;
   const uint16_t* kr = a.k_res + bh * kN * D;
   const uint16_t* vr = a.v_res + bh * kN * D;
   const bool chan = 2 * lane < D;
   constexpr int PER = D / 8;  // 16-byte pieces per row
-  for (int c0 = 0; c0 < T16; c0 += 64) {
+  for (int c0 = 64 * chunk; c0 < T16; c0 += 64 * n_chunk_splits) {
     const int nt = min(64, T16 - c0);
     // value rows of the chunk: piece i of the chunk is row i / PER, part i % PER
     v4u vpc[PER];
@@ -343,7 +355,7 @@ __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, int64
       a.part_o[(pbase + i) * D + 2 * lane + 1] = acc[i][1];
     }
     if (lane == 0) {
-      a.part_ml[(pbase + i) * 2 + 0] = T16 > 0 ? m[i] : -INFINITY;
+      a.part_ml[(pbase + i) * 2 + 0] = m[i];
       a.part_ml[(pbase + i) * 2 + 1] = l[i];
     }
   }
@@ -354,9 +366,12 @@ __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, int64
 template <int D, int NT, int KG>
 __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t bh) {
   using S_ = Shape<D>;
-  constexpr int KL = S_::KL, KHM = S_::KHM, TL = S_::TL, NM0 = S_::NM0, JL = S_::JL;
+  constexpr int KL = S_::KL, KHM = S_::KHM, TL = S_::TL, JL = S_::JL;
   constexpr int NH = 4 * NT;
-  constexpr int UK = (NT * D + 63) / 64;  // LSB prep units per lane
+  constexpr int UK = (NT * D + 63) / 64;   // LSB prep units per lane
+  constexpr int NTV = D / 16;              // p.V column tiles of 16 channels
+  constexpr int MW = D / 4 >= 16 ? 16 : 8; // value-byte columns per tile
+  constexpr int NMB = (D / 4) / MW;        // value-byte column blocks
 
   const int lane = threadIdx.x;
   const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
@@ -372,17 +387,19 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     return;
   }
 
-  // LDS: digit table T [KG][NT][16][TL] bytes, p buffer [NT][4][128] f32, key scales of the page
-  // [KG][D] fp16, bias [KG][NH] f32, salient channel of each rank [D] int16.
-  uint8_t* T = lds;
-  float* P = reinterpret_cast<float*>(lds + a.lds_T);
-  uint16_t* Sl = reinterpret_cast<uint16_t*>(P + NT * 4 * kN);
-  float* biasl = reinterpret_cast<float*>(Sl + 4 * D);
-  int16_t* sal = reinterpret_cast<int16_t*>(biasl + 4 * NH);
-
   const int G = a.G, n_sal = a.n_sal, NGV = a.NGV;
   const int KH = (n_sal + 63) / 64;
   const int JH = (n_sal + 3) / 4;  // 4-rank units per head of the upper-bit part
+
+  // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NT][NGV][16][N] bytes;
+  // key scales of the page [KG][D] fp16; bias [KG][NH] f32; salient channel of each rank [D]
+  // int16; head maxima [NH] f32.
+  uint8_t* T = lds;
+  uint8_t* W = lds + a.lds_T;
+  uint16_t* Sl = reinterpret_cast<uint16_t*>(W + NT * NGV * 16 * kN);
+  float* biasl = reinterpret_cast<float*>(Sl + 4 * D);
+  int16_t* sal = reinterpret_cast<int16_t*>(biasl + 4 * NH);
+  float* qm = reinterpret_cast<float*>(sal + D);
 
   // ---- once per split: clear the digit table, salient ranks, scaled queries
   for (int i = lane * 16; i < a.lds_T; i += 64 * 16) *reinterpret_cast<v4u*>(T + i) = v4u{0, 0, 0, 0};
@@ -410,22 +427,16 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     float mx = fmaxf(fmaxf(fabsf(qv[k][0]), fabsf(qv[k][1])), fmaxf(fabsf(qv[k][2]), fabsf(qv[k][3])));
     qmaxu[k] = group_max<(JL < 64 ? JL : 64)>(mx);
   }
+#pragma unroll
+  for (int k = 0; k < UK; ++k) {
+    const int u = lane + 64 * k;
+    if (u < NT * D && (u % JL) == 0) qm[u / JL] = qmaxu[k];
+  }
+  __syncthreads();
   // max |qt| of the head this lane has in the q.K output (head 4t + lane/16)
   float qmaxC[NT];
-  {
-    float* qm = P;  // scratch before P is used
-    if (lane < 64) {
 #pragma unroll
-      for (int k = 0; k < UK; ++k) {
-        const int u = lane + 64 * k;
-        if (u < NT * D && (u % JL) == 0) qm[u / JL] = qmaxu[k];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < NT; ++t) qmaxC[t] = qm[4 * t + lane / 16];
-    __syncthreads();
-  }
+  for (int t = 0; t < NT; ++t) qmaxC[t] = qm[4 * t + lane / 16];
   // upper-bit prep units: uh = lane + 64k -> head uh / JH, ranks 4 (uh % JH) + 0..3
   constexpr int UKH = (NT * 4 * (D / 4) + 63) / 64;
   int hc[UKH][4];
@@ -436,7 +447,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     const int uh = lane + 64 * k;
     const int hu = JH ? uh / JH : 0, jr = JH ? uh % JH : 0;
     const bool ok = JH && uh < NH * JH && hu < ng;
-    hqmax[k] = 0.0f;
+    hqmax[k] = (JH && uh < NH * JH) ? qm[hu] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * jr + i;
@@ -447,29 +458,12 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
                                : 0.0f;
     }
   }
-  // max|qt| of head hu for the upper-bit units: from the LSB units' head maxima via LDS
-  {
-    float* qm = P;
-#pragma unroll
-    for (int k = 0; k < UK; ++k) {
-      const int u = lane + 64 * k;
-      if (u < NT * D && (u % JL) == 0) qm[u / JL] = qmaxu[k];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < UKH; ++k) {
-      const int uh = lane + 64 * k;
-      const int hu = JH ? uh / JH : 0;
-      hqmax[k] = (JH && uh < NH * JH) ? qm[hu] : 0.0f;
-    }
-    __syncthreads();
-  }
 
-  // running softmax state of head 4t + lane/16; p.V accumulators [t][m0][u] in C layout
+  // running softmax state of head 4t + lane/16; p.V accumulators per 16-channel tile (C
+  // layout: column lane % 16), value-offset sums per group
   float m_run[NT], l_run[NT];
   float zacc[NT][4];
-  int k_run = 0;  // p.V operands carry p S 2^k_run (keeps w clear of the fp16 subnormal floor)
-  v4f acc[NT][NM0][4];
+  float acc[NT][NTV];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     m_run[t] = -INFINITY;
@@ -477,9 +471,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 #pragma unroll
     for (int g = 0; g < 4; ++g) zacc[t][g] = 0.0f;
 #pragma unroll
-    for (int m0 = 0; m0 < NM0; ++m0)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc[t][m0][u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int v = 0; v < NTV; ++v) acc[t][v] = 0.0f;
   }
 
   const int oct = lane & 15;  // octet of the q.K B operand (keys 8 oct + b)
@@ -488,6 +480,10 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   const int64_t page_base = bh * a.max_pages;
   const int sOff = kN * D / 8 + kN * n_sal / 4;      // K page: S after lo and hi planes
   const int zOff = sOff + 2 * KG * D;
+  // p.V: this lane's value-byte column within a tile block, and (for 8-column tiles) the
+  // shift that brings its field pair to bits 0-1 / 4-5
+  const int vcol = lane & (MW - 1);
+  const int vsh = MW == 16 ? 0 : 2 * ((lane & 15) >> 3);
 
   // Key side of one page in registers: this lane's packed codes (LSB rows and upper-bit rows
   // 2 oct, 2 oct + 1) and the scales of its prep units.  The next page's are loaded into them as
@@ -537,24 +533,20 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     const uint16_t* VS = reinterpret_cast<const uint16_t*>(vp + kN * D / 4);  // [NGV][N]
     const uint16_t* VZ = VS + NGV * kN;
 
-    // ---- value side of this page, issued now, consumed after q.K: scales of this lane's p.V
-    // rows (group gA, 8 keys of octet 4s + qb), offsets of its q.K keys (8 oct + b) per group,
-    // codes byte [octet][m][key] for m = 16 m0 + (lane & 15)
-    const int R = lane & 15, hlA = R >> 2, gA = R & 3;
+    // ---- value side of this page, issued now, consumed after q.K: scales and offsets of
+    // this lane's q.K keys (8 oct + b) per group; code bytes of its tile columns per K-step
     v4u sS[4], zZ[4];
-    uint2 cw[4][NM0];
+    v4u cv[NMB][2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      sS[s] = gA < NGV ? *reinterpret_cast<const v4u*>(VS + gA * kN + 8 * (4 * s + qb))
-                       : v4u{0, 0, 0, 0};
-      zZ[s] = s < NGV ? *reinterpret_cast<const v4u*>(VZ + s * kN + 8 * oct) : v4u{0, 0, 0, 0};
-#pragma unroll
-      for (int m0 = 0; m0 < NM0; ++m0) {
-        const int m = 16 * m0 + (lane & 15);
-        cw[s][m0] = m < D / 4 ? *reinterpret_cast<const uint2*>(vp + ((int64_t)(4 * s + qb) * (D / 4) + m) * 8)
-                              : make_uint2(0u, 0u);
-      }
+    for (int g = 0; g < 4; ++g) {
+      sS[g] = g < NGV ? *reinterpret_cast<const v4u*>(VS + g * kN + 8 * oct) : v4u{0, 0, 0, 0};
+      zZ[g] = g < NGV ? *reinterpret_cast<const v4u*>(VZ + g * kN + 8 * oct) : v4u{0, 0, 0, 0};
     }
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        cv[mb][ks] = load16(vp + (int64_t)(mb * MW + vcol) * kN + 64 * ks + 16 * qb);
 
     // ---- key scales: page maximum -> per-head fixed-point exponent
     uint32_t smax = 0u;
@@ -677,9 +669,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
             if (ks < KH) c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[kg][t][KL + ks], bH[ks], c, 0, 0, 0); \
           csel = (KG == 1 || kg == kg_lane) ? c : csel;                                        \
         }                                                                                      \
-        const float v = (((float)csel[3] * 256.0f + (float)csel[2]) * 256.0f +                 \
-                         (float)csel[1]) * 256.0f + (float)csel[0];                            \
-        lg[t][BB] = __builtin_fmaf(v, inv2s[t] * kInvSL[BB], bias[t]);                         \
+        lg[t][BB] = __builtin_fmaf(combine4(csel), inv2s[t] * kInvSL[BB], bias[t]);            \
       }                                                                                        \
     }
     PNMIX_QK_TILE(0) PNMIX_QK_TILE(1) PNMIX_QK_TILE(2) PNMIX_QK_TILE(3)
@@ -689,26 +679,34 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     // ---- the key side of this page is consumed: fetch the next page's
     if (pg + 1 < p1) load_k(pg + 1);
 
-    // ---- the page's power-of-two p.V operand scale 2^k: p S 2^k < 2^15 for every key, group
+    // ---- p.V fixed point: w = p S 2^sv with p <= 1 and S <= the page's largest value scale,
+    // so |w| < 2^30 and four balanced base-256 digits hold it exactly
     uint32_t svmax = 0u;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) svmax = max(svmax, max(sS[s][e] & 0xFFFFu, sS[s][e] >> 16));
+      for (int e = 0; e < 4; ++e) svmax = max(svmax, max(sS[g][e] & 0xFFFFu, sS[g][e] >> 16));
     svmax = wave_max_u32(svmax);
-    int k_page = 0;
+    int sv_e = 0;
     {
       const float Sv = (float)__builtin_bit_cast(_Float16, (uint16_t)svmax);
       if (Sv > 0.0f) {
         const int e = (int)((__builtin_bit_cast(uint32_t, Sv) >> 23) & 0xFF) - 127;
-        k_page = min(max(14 - e, 0), 64);
+        sv_e = min(max(29 - e, -126), 126);
       }
     }
-    if (pg == p0) k_run = k_page;
-    const float kscale = pow2i(k_page);
+    const float sv2 = pow2i(sv_e);
+    float sp[4][8];  // S 2^sv of this lane's keys per group
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sp[g][2 * e] = f16lo(sS[g][e]) * sv2;
+        sp[g][2 * e + 1] = f16hi(sS[g][e]) * sv2;
+      }
 
-    // ---- online softmax per head; p 2^k to LDS; value-offset term on the vector ALU
-    bool rescale = k_page != k_run;
+    // ---- online softmax per head, value-offset term on the vector ALU, digits of w to LDS
+    bool rescale = false;
     float alpha[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -727,9 +725,6 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         ps += p[bb];
       }
       l_run[t] = l_run[t] * alpha[t] + ps;
-      float* prow = P + (t * 4 + qb) * kN + 8 * oct;
-      *reinterpret_cast<v4f*>(prow) = v4f{p[0], p[1], p[2], p[3]} * kscale;
-      *reinterpret_cast<v4f*>(prow + 4) = v4f{p[4], p[5], p[6], p[7]} * kscale;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         if (g >= NGV) break;
@@ -741,70 +736,71 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
           s = __builtin_fmaf(p[2 * e + 1], f16hi(zz[e]), s);
         }
         zacc[t][g] = s;
+        uint32_t x[8], d0[4], d1[4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = digits4((int)(p[e] * sp[g][e]));
+        transpose4(x, d0);
+        transpose4(x + 4, d1);
+        uint8_t* row = W + ((t * NGV + g) * 16 + 4 * qb) * kN + 8 * oct;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) *reinterpret_cast<uint2*>(row + d * kN) = make_uint2(d0[d], d1[d]);
       }
     }
     if (__any(rescale)) {
-      const float kf = pow2i(k_page - k_run);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float f = alpha[t] * kf;
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int m0 = 0; m0 < NM0; ++m0)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) acc[t][m0][u] *= f;
-      }
+        for (int v = 0; v < NTV; ++v) acc[t][v] *= alpha[t];
     }
-    k_run = k_page;
-    __syncthreads();  // p visible
+    __syncthreads();  // the w digits are in LDS
 
-    // ---- p.V: A rows (head hl, value group g) = lane & 15, K block qb = 8 keys of octet 4s + qb
+    // ---- p.V: tile v = 16 channels of one value group; rows (head, digit), K = 64 keys
+    const float inv_sv = pow2i(-sv_e);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int octv = 4 * s + qb;
+    for (int v = 0; v < NTV; ++v) {
+      // MW = 16: tile (block mb, field u) = channels 16 mb + u d/4 + n;
+      // MW = 8:  tile tb = fields 2tb (n < 8) and 2tb + 1 (n >= 8) = channels 16 tb + n
+      const int mb = MW == 16 ? v % NMB : 0;
+      const int fu = MW == 16 ? v / NMB : v;
+      const int cbase = MW == 16 ? 16 * mb + fu * (D / 4) : 16 * v;
+      const int g = cbase / a.g_V;
+      v4i Bv[2];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float* prow = P + (t * 4 + hlA) * kN + 8 * octv;
-        const v4f pa = *reinterpret_cast<const v4f*>(prow);
-        const v4f pc = *reinterpret_cast<const v4f*>(prow + 4);
-        const float pe[8] = {pa[0], pa[1], pa[2], pa[3], pc[0], pc[1], pc[2], pc[3]};
-        float sw[8];
+      for (int ks = 0; ks < 2; ++ks) {
+        const v4u w = cv[mb][ks];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sw[2 * e] = f16lo(sS[s][e]);
-          sw[2 * e + 1] = f16hi(sS[s][e]);
-        }
-        float w[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = __builtin_fmaf(pe[e], sw[e], 0.0f);
-        // K element order (matches the codes below): (0,2), (1,3), (4,6), (5,7)
-        const uint32_t h02 = pk_rne(w[0], w[2]), h13 = pk_rne(w[1], w[3]);
-        const uint32_t h46 = pk_rne(w[4], w[6]), h57 = pk_rne(w[5], w[7]);
-        const uint32_t l02 = pk_rne(__builtin_fmaf(pe[0], sw[0], -f16lo(h02)), __builtin_fmaf(pe[2], sw[2], -f16hi(h02)));
-        const uint32_t l13 = pk_rne(__builtin_fmaf(pe[1], sw[1], -f16lo(h13)), __builtin_fmaf(pe[3], sw[3], -f16hi(h13)));
-        const uint32_t l46 = pk_rne(__builtin_fmaf(pe[4], sw[4], -f16lo(h46)), __builtin_fmaf(pe[6], sw[6], -f16hi(h46)));
-        const uint32_t l57 = pk_rne(__builtin_fmaf(pe[5], sw[5], -f16lo(h57)), __builtin_fmaf(pe[7], sw[7], -f16hi(h57)));
-        const v8h Ahi = __builtin_bit_cast(v8h, v4u{h02, h13, h46, h57});
-        const v8h Alo = __builtin_bit_cast(v8h, v4u{l02, l13, l46, l57});
-#pragma unroll
-        for (int m0 = 0; m0 < NM0; ++m0) {
-          const uint32_t w0 = cw[s][m0].x, w1 = cw[s][m0].y;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            // field u of every byte moved to bits 8..9 of its fp16 half: value code * 2^-16
-            const uint32_t M = 0x03000300u;
-            const v8h Bv = __builtin_bit_cast(
-                v8h, v4u{(w0 << (8 - 2 * u)) & M, (w0 >> (2 * u)) & M, (w1 << (8 - 2 * u)) & M,
-                         (w1 >> (2 * u)) & M});
-            acc[t][m0][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, acc[t][m0][u], 0, 0, 0);
-            acc[t][m0][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, acc[t][m0][u], 0, 0, 0);
+          uint32_t f;
+          if (MW == 16) {
+            f = fu == 0 ? (w[e] & 0x03030303u)
+              : fu == 1 ? (w[e] & 0x0C0C0C0Cu)
+              : fu == 2 ? (w[e] & 0x30303030u)
+                        : ((w[e] >> 2) & 0x30303030u);
+          } else {
+            const uint32_t ws = w[e] >> vsh;
+            f = fu == 0 ? (ws & 0x03030303u) : (ws & 0x30303030u);
           }
+          Bv[ks][e] = (int)f;
         }
       }
+      // field weight of the masked bytes: code * {1, 4, 16, 16}[u] (MW 16), {1, 16}[tb] (MW 8)
+      const float fw = MW == 16 ? (fu == 0 ? 1.0f : fu == 1 ? 0.25f : 0.0625f)
+                                : (fu == 0 ? 1.0f : 0.0625f);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint8_t* wrow = W + ((t * NGV + g) * 16 + (lane & 15)) * kN + 16 * qb;
+        const v4i A0 = *reinterpret_cast<const v4i*>(wrow);
+        const v4i A1 = *reinterpret_cast<const v4i*>(wrow + 64);
+        v4i c = v4i{0, 0, 0, 0};
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, Bv[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, Bv[1], c, 0, 0, 0);
+        acc[t][v] = __builtin_fmaf(combine4(c), inv_sv * fw, acc[t][v]);
+      }
     }
-    __syncthreads();  // P, T and Sl are rewritten by the next page
+    __syncthreads();  // T, W and Sl are rewritten by the next page
   }
 
-  // ---- partials of this split: head 4t + qb in both output layouts
+  // ---- partials of this split: head 4t + qb, channel of tile v for column lane % 16
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const float lt = row_sum16(l_run[t]);
@@ -814,17 +810,14 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     const int hh = 4 * t + qb;
     if (hh < ng) {
 #pragma unroll
-      for (int m0 = 0; m0 < NM0; ++m0)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = 4 * (16 * m0 + (lane & 15)) + u;
-          if (c < D) {
-            const int gi = c / a.g_V;
-            const float zsg = gi == 0 ? zs[0] : gi == 1 ? zs[1] : gi == 2 ? zs[2] : zs[3];
-            const float v = sel4(acc[t][m0][u], gi) * pow2i(16 - k_run) + zsg;
-            a.part_o[(pbase + hh) * D + c] = v;
-          }
-        }
+      for (int v = 0; v < NTV; ++v) {
+        const int mb = MW == 16 ? v % NMB : 0;
+        const int fu = MW == 16 ? v / NMB : v;
+        const int c = (MW == 16 ? 16 * mb + fu * (D / 4) : 16 * v) + (lane & 15);
+        const int gi = c / a.g_V;
+        const float zsg = gi == 0 ? zs[0] : gi == 1 ? zs[1] : gi == 2 ? zs[2] : zs[3];
+        a.part_o[(pbase + hh) * D + c] = acc[t][v] + zsg;
+      }
       if ((lane & 15) == 0) {
         a.part_ml[(pbase + hh) * 2 + 0] = m_run[t];
         a.part_ml[(pbase + hh) * 2 + 1] = lt;
@@ -835,45 +828,58 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 
 // ----------------------------------------------------------------------------------- merge
 
-// Second launch: one workgroup of 64 per (sequence, query head, 32-channel block).  m = max m_s,
-// l = sum 2^(m_s - m) l_s, o = sum 2^(m_s - m) o_s / l (log2 units); lanes own one split each for
-// the weights, then 32 channels x 2 split halves for the sums, added in a fixed order.
-__global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a, int d) {
-  __shared__ float wts[64];
-  __shared__ float half[64];
-  const int lane = threadIdx.x;
+// Second launch: one workgroup of 256 per (sequence, query head).  m = max m_s,
+// l = sum 2^(m_s - m) l_s, o = sum 2^(m_s - m) o_s / l (log2 units).  Thread s < S reads the
+// (m, l) of split s; then thread (split lane sl, channel quad cq) sums the splits sl, sl + SL, ...
+// of four channels with every load of the walk independent, and the SL lane sums are added in
+// a fixed order.
+template <int D>
+__global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
+  constexpr int Q = D / 4, SL = 256 / Q;
+  __shared__ float wts[256];
+  __shared__ float red[2][4];
+  __shared__ v4f psum[256];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bhq = blockIdx.x;  // b * H_q + hq
   const int b = bhq / a.H_q, hq = bhq % a.H_q;
   const int ng = a.n_g, S = a.splits;
   const int h = hq / ng, hh = hq % ng;
   const int64_t bh = (int64_t)b * a.H_kv + h;
   float m = -INFINITY, l = 0.0f;
-  if (lane < S) {
-    const int64_t pi = (bh * S + lane) * ng + hh;
+  if (tid < S) {
+    const int64_t pi = (bh * S + tid) * ng + hh;
     m = a.part_ml[pi * 2];
     l = a.part_ml[pi * 2 + 1];
   }
-  const float M = group_max<64>(m);
-  const float w = (lane < S && m != -INFINITY && M != -INFINITY) ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
-  const float L = group_sum<64>(w * l);
-  wts[lane] = w;
+  float M = group_max<64>(m);
+  if (lane == 0) red[0][wv] = M;
   __syncthreads();
-  const int c = 32 * blockIdx.y + (lane & 31), part = lane >> 5;
-  float o = 0.0f;
-  if (c < d) {
+  M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  const float w = (tid < S && m != -INFINITY && M != -INFINITY) ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+  const float Lw = group_sum<64>(w * l);
+  if (lane == 0) red[1][wv] = Lw;
+  wts[tid] = w;
+  __syncthreads();
+  const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  const int cq = tid % Q, sl = tid / Q;
+  v4f o = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const float* po = a.part_o + (bh * S * ng + hh) * D + 4 * cq;
 #pragma unroll 8
-    for (int s = part; s < S; s += 2) {
-      const float ws = wts[s];
-      if (ws != 0.0f) o += ws * a.part_o[((bh * S + s) * ng + hh) * d + c];
-    }
-  }
-  half[lane] = o;
+  for (int s = sl; s < S; s += SL)
+    o += wts[s] * *reinterpret_cast<const v4f*>(po + (int64_t)s * ng * D);
+  psum[tid] = o;
   __syncthreads();
-  if (lane < 32 && c < d) a.out[(int64_t)bhq * d + c] = L > 0.0f ? (half[lane] + half[lane + 32]) / L : 0.0f;
+  if (tid < Q) {
+    v4f r = psum[tid];
+#pragma unroll
+    for (int i = 1; i < SL; ++i) r += psum[i * Q + tid];
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    *reinterpret_cast<v4f*>(a.out + (int64_t)bhq * D + 4 * tid) = r * inv;
+  }
 }
 
-// One launch per decode call: blockIdx.x < page_splits walks packed pages, blockIdx.x ==
-// page_splits takes the fp16 sink and residual rows, concurrently with the pages.
+// One launch per decode call: blockIdx.x < page_splits walks packed pages, the remaining
+// splits take one 64-token chunk each of the fp16 sink and residual rows, concurrently.
 template <int D, int NT, int KG>
 __global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -886,8 +892,8 @@ __global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
     const pnmix_seq_len L = a.lens[b];
     const int sink_len = min(max(L.sink_len, 0), a.N_s);
     const int res_len = min(max(L.res_len, 0), kN);
-    fp16_region<D, NT>(a, b, h, bh, (bh * a.splits + a.page_splits) * a.n_g, sink_len, res_len,
-                       lds);
+    fp16_region<D, NT>(a, b, h, bh, (bh * a.splits + split) * a.n_g, sink_len, res_len,
+                       split - a.page_splits, a.splits - a.page_splits, lds);
   }
 }
 
@@ -907,7 +913,8 @@ static size_t lds_T_bytes(const pnmix_cfg& c) {
 
 static size_t lds_bytes(const pnmix_cfg& c) {
   const int NT = n_tiles(c);
-  return lds_T_bytes(c) + (size_t)NT * 4 * kN * 4 + 4 * c.d * 2 + 4 * 4 * NT * 4 + c.d * 2;
+  const size_t W = (size_t)NT * (c.d / c.g_V) * 16 * kN;
+  return lds_T_bytes(c) + W + 4 * c.d * 2 + 4 * 4 * NT * 4 + c.d * 2 + 4 * NT * 4;
 }
 
 static size_t lds_fp16_bytes(const pnmix_cfg& c) {
@@ -918,17 +925,19 @@ static size_t lds_fp16_bytes(const pnmix_cfg& c) {
 DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   DecodePlan p;
   const long long items = (long long)B * c.H_kv;
-  // about two resident waves per SIMD (256 CUs x 4 SIMDs), pages split evenly: one round of
-  // waves covers the grid, so no tail of late waves
+  // about two waves per SIMD (256 CUs x 4 SIMDs) over the pages, split evenly
   const long long target = 2048;
-  int ps = (int)std::max<long long>(1, target / std::max<long long>(items, 1) - 1);
+  // fp16 rows: one split per 64-token chunk when the batch is small, else one split walking
+  // all chunks (its latency then hides among the page splits)
+  const int n16 = items >= 128 ? 1 : (c.N_s + c.N + 63) / 64;
+  int ps = (int)std::max<long long>(1, (target + items - 1) / std::max<long long>(items, 1));
   ps = std::min(ps, std::max(max_pages, 1));
-  ps = std::min(ps, 63);  // the merge gives each split one lane: at most 64 splits
+  ps = std::min(ps, kMaxSplits - n16);
   int pps = max_pages > 0 ? (max_pages + ps - 1) / ps : 1;
   ps = max_pages > 0 ? (max_pages + pps - 1) / pps : 0;
   p.page_splits = ps;
   p.pages_per_split = pps;
-  p.splits = ps + 1;
+  p.splits = ps + n16;
   const int ng = c.H_q / c.H_kv;
   const size_t per = (size_t)items * p.splits * ng;
   const size_t o_bytes = (per * c.d * sizeof(float) + 255) & ~(size_t)255;
@@ -944,8 +953,7 @@ static hipError_t launch_k(const DecodePlan& p, int B, const pnmix_cfg& c, const
                      p.lds_bytes, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(B * c.H_q, (c.d + 31) / 32), dim3(64), 0, stream, a,
-                     c.d);
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(B * c.H_q), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@
 // Eq. 7 midpoint correction of 1-bit groups, zero scale plus the original offset for constant
 // groups, H3/L1 packing.  Kernel-implementation appendix of the paper: LSB plane of every key
 // channel at 8 tokens per byte, upper-2-bit plane of salient channels at 4 tokens per byte,
-// values at 4 channels per byte.
+// values at 4 channels per byte (here the channels j, j + d/4, j + d/2, j + 3d/4, so that one
+// 2-bit field of 16 consecutive bytes holds 16 consecutive channels of one value group).
 //
 // One workgroup of 2d threads per page; thread (octet k, block b) holds tokens 8k..8k+7 x
 // channels 8b..8b+7 of the N x d fp16 page in registers, read with one 16-byte load per token
@@ -19,8 +20,9 @@
 //   C. per element q = rne(clamp((x - min) * (1/s), 0, L)): the clamp bounds are integers, so
 //      clamping before rounding gives the same code as rounding first, and adding 2^23 to a
 //      value in [0, L] rounds it to the nearest even integer and leaves it in the low
-//      mantissa bits.  Codes are packed in registers and stored as whole 8- or 16-byte runs;
-//      the upper-bit plane is gathered in LDS by salient rank and copied out 16 bytes a lane.
+//      mantissa bits.  Key LSB bytes are packed in registers and stored as 8-byte runs; the
+//      upper-bit plane (by salient rank) and the value bytes (four fields from four threads)
+//      are gathered in LDS and copied out 16 bytes a lane.
 // Every float step is the reference arithmetic, so codes and fp16 metadata are bit-identical.
 #include "common.h"
 #include "kernels.h"
@@ -241,7 +243,9 @@ __global__ void __launch_bounds__(2 * D) quantize_v_kernel(const pnmix_page* __r
   constexpr int NB = D / 8;
   __shared__ __align__(16) uint32_t part[kN * NB];  // (min, max) fp16 per token, block
   __shared__ __align__(16) float2 meta[kN * 4];     // (min, 1/s) per token, group (<= 4)
+  __shared__ __align__(16) uint32_t cw[kN * D / 16]; // the page's code bytes [d/4][N]
   const int tid = threadIdx.x, b = tid % NB, k = tid / NB;
+  reinterpret_cast<uint4*>(cw)[tid] = make_uint4(0u, 0u, 0u, 0u);
   const pnmix_page job = jobs[blockIdx.x];
   const int ng = D / g_V;
   uint8_t* codes = job.dst;
@@ -280,29 +284,28 @@ __global__ void __launch_bounds__(2 * D) quantize_v_kernel(const pnmix_page* __r
   }
   __syncthreads();
 
-  // C: two 4-channel columns x 8 tokens -> 16 contiguous bytes of [N/8][d/4][8]
+  // C: codes of the thread's 8 channels x 8 tokens.  Byte [j][t] of the page holds channel
+  // j + u d/4 of token t in bits 2u..2u+1: the thread's channels share u and fill 8
+  // consecutive bytes j; the four fields of a byte come from four threads, OR-ed in LDS.
   const int gi = b / bg;
-  uint32_t byte[2][8];
+  const int u = (8 * b) / (D / 4), j0 = (8 * b) % (D / 4);
+  float2 mt[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float2 mt = meta[(8 * k + j) * 4 + gi];
+  for (int e = 0; e < 8; ++e) mt[e] = meta[(8 * k + e) * 4 + gi];
 #pragma unroll
-    for (int col = 0; col < 2; ++col) {
-      const uint32_t w0 = col ? x[j].z : x[j].x, w1 = col ? x[j].w : x[j].y;
-      const uint32_t u0 = code_bits(lo_f(w0), mt.x, mt.y, 3.0f);
-      const uint32_t u1 = code_bits(hi_f(w0), mt.x, mt.y, 3.0f);
-      const uint32_t u2 = code_bits(lo_f(w1), mt.x, mt.y, 3.0f);
-      const uint32_t u3 = code_bits(hi_f(w1), mt.x, mt.y, 3.0f);
-      // channel u at bits 2u of the low byte (float exponent bits land >= bit 24)
-      byte[col][j] = (((((u3 << 2) | u2) << 2) | u1) << 2) | u0;
+  for (int i = 0; i < 8; ++i) {
+    uint32_t cu[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = word(x[e], i >> 1);
+      cu[e] = code_bits((i & 1) ? hi_f(w) : lo_f(w), mt[e].x, mt[e].y, 3.0f);
     }
+    uint32_t* dst = cw + ((j0 + i) * kN + 8 * k) / 4;
+    atomicOr(dst, gather_b0(cu[0], cu[1], cu[2], cu[3]) << (2 * u));
+    atomicOr(dst + 1, gather_b0(cu[4], cu[5], cu[6], cu[7]) << (2 * u));
   }
-  uint4 outv;
-  outv.x = gather_b0(byte[0][0], byte[0][1], byte[0][2], byte[0][3]);
-  outv.y = gather_b0(byte[0][4], byte[0][5], byte[0][6], byte[0][7]);
-  outv.z = gather_b0(byte[1][0], byte[1][1], byte[1][2], byte[1][3]);
-  outv.w = gather_b0(byte[1][4], byte[1][5], byte[1][6], byte[1][7]);
-  *reinterpret_cast<uint4*>(codes + (k * (D / 4) + 2 * b) * 8) = outv;
+  __syncthreads();
+  reinterpret_cast<uint4*>(codes)[tid] = reinterpret_cast<const uint4*>(cw)[tid];
 }
 
 hipError_t launch_quantize_k(const pnmix_cfg& c, int n_pages, const pnmix_page* pages,

@@ -143,8 +143,9 @@ pnmix_status pnmix_quantize_k_page(const pnmix_cfg* cfg, int32_t n_pages,
 /* Value page quantization and packing ([PNMIX] sec. 2 and kernel-implementation appendix;
  * [SUMMARY]): per token and channel group of g_V channels, Eq. 2 at b_V = 2 bits with the
  * constant rule; stored S = h(s), Z = h(mn).  Layout:
- *   codes [N/8][d/4][8]  byte [j][m][k] = channels 4m..4m+3 of token 8j+k, channel 4m+u in
- *                        bits 2u..2u+1
+ *   codes [d/4][N]  byte [j][t] = 4 channels of token t a quarter of the head apart:
+ *                   channel j + u*d/4 in bits 2u..2u+1 (u = 0..3), so each 2-bit field of
+ *                   16 consecutive bytes j covers 16 consecutive channels (one value group)
  *   S [d/g_V][N] fp16, then Z [d/g_V][N] fp16 (group-major: one group's N tokens contiguous).
  * Bit-exact with the reference oracle. */
 pnmix_status pnmix_quantize_v_page(const pnmix_cfg* cfg, int32_t n_pages,

@@ -127,7 +127,7 @@ int64_t orc_k_page_bytes(const orc_cfg* c) {
          2 * 2 * (int64_t)(c->N / c->G) * c->d;
 }
 
-/* V page: codes [N/8][d/4][8] + S [d/g_V][N] + Z [d/g_V][N] (fp16) */
+/* V page: codes [d/4][N] + S [d/g_V][N] + Z [d/g_V][N] (fp16) */
 int64_t orc_v_page_bytes(const orc_cfg* c) {
   return (int64_t)c->N * c->d * c->b_V / 8 + 2 * 2 * (int64_t)c->N * (c->d / c->g_V);
 }
@@ -334,9 +334,10 @@ int orc_quantize_k_page(const orc_cfg* c, const uint16_t* src, int64_t src_row_s
 
 /* V page ([PNMIX] sec. 2 and kernel-implementation appendix; [SUMMARY]): values are
  * quantized per token over channel groups of g_V at b_V = 2 bits (Eq. 2, constant rule);
- * every 4 consecutive channels of one token share a byte, channel 4m + u in bits
- * 2u..2u+1.  Bytes are arranged [N/8][d/4][8]: byte [j][m][k] belongs to token 8j + k.
- * Then S[g][t], Z[g][t] as little-endian fp16 ([d/g_V][N] each, group-major). */
+ * 4 channels of one token share a byte.  This library's byte holds the channels a quarter
+ * of the head apart: byte [j][t] (j < d/4, bytes arranged [d/4][N]) carries channel
+ * j + u d/4 of token t in bits 2u..2u+1.  Then S[g][t], Z[g][t] as little-endian fp16
+ * ([d/g_V][N] each, group-major). */
 int orc_quantize_v_page(const orc_cfg* c, const uint16_t* src, int64_t src_row_stride,
                         uint8_t* dst) {
   if (orc_check_cfg(c) || !src || !dst) return 1;
@@ -357,8 +358,8 @@ int orc_quantize_v_page(const orc_cfg* c, const uint16_t* src, int64_t src_row_s
   memset(cb, 0, (size_t)N * d / 4);
   for (int32_t t = 0; t < N; ++t)
     for (int32_t ch = 0; ch < d; ++ch)
-      cb[((t / 8) * (d / 4) + ch / 4) * 8 + (t % 8)] |=
-          (uint8_t)((codes[t * d + ch] & 3u) << (2 * (ch % 4)));
+      cb[(int64_t)(ch % (d / 4)) * N + t] |=
+          (uint8_t)((codes[t * d + ch] & 3u) << (2 * (ch / (d / 4))));
   free(codes);
   return 0;
 }
@@ -407,7 +408,7 @@ int orc_unpack_v_page(const orc_cfg* c, const uint8_t* page, uint8_t* codes, uin
     for (int32_t t = 0; t < N; ++t)
       for (int32_t ch = 0; ch < d; ++ch)
         codes[t * d + ch] =
-            (uint8_t)((cb[((t / 8) * (d / 4) + ch / 4) * 8 + (t % 8)] >> (2 * (ch % 4))) & 3u);
+            (uint8_t)((cb[(int64_t)(ch % (d / 4)) * N + t] >> (2 * (ch / (d / 4)))) & 3u);
   /* S, Z are returned per token, [N][d/g_V], from the group-major storage */
   for (int32_t t = 0; t < N; ++t)
     for (int32_t g = 0; g < ng; ++g) {

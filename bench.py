@@ -44,6 +44,66 @@ def decode_bytes(cfg, lens, B, kpb, vpb):
     return B * (per_head * cfg.H_kv + 16)
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+DECODE_SRC = os.path.join(ROOT, "decode_attention_pnmix_amd", "csrc", "decode.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_MB = 256  # plain device copy that calibrates the HBM byte counters
+
+
+def _sha(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, lens):
+    """HBM bytes per decode call from the committed counter summary of this workload, or None
+    when there is none or the decode kernels changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"decode_attn_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("decode_src_sha256_16") != _sha(DECODE_SRC) or t.get("lens") != list(lens):
+        return None
+    return t["hbm_bytes_per_call"]
+
+
+def pmc_summary(fetch_dir, write_dir, workload, lens):
+    """Summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE): per
+    dispatch KiB of the decode kernels at the last decode call of the run, each scaled by the
+    ratio of the known bytes of the calibration copy to what the same counter reads for it."""
+    import csv
+    import glob
+
+    def rows(d):
+        out = []
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fn) as f:
+                out += list(csv.DictReader(f))
+        out.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return out
+
+    res = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rs = [r for r in rows(d) if r["Counter_Name"] == name]
+        copy = [float(r["Counter_Value"]) for r in rs
+                if "copybuffer" in r["Kernel_Name"].lower() or
+                ("elementwise" in r["Kernel_Name"] and "copy" in r["Kernel_Name"].lower())]
+        big = max(copy) * 1024.0  # the calibration copy is the largest copy of the run
+        factor = COPY_MB * 2**20 / big
+        dec = [r for r in rs if "decode_kernel" in r["Kernel_Name"]]
+        mrg = [r for r in rs if "decode_merge_kernel" in r["Kernel_Name"]]
+        k = float(dec[-1]["Counter_Value"]) * 1024.0 * factor
+        m = float(mrg[-1]["Counter_Value"]) * 1024.0 * factor
+        res[name] = {"copy_counter_bytes": big, "copy_factor": factor,
+                     "decode_kernel_bytes": k, "merge_kernel_bytes": m,
+                     "decode_kernel_name": dec[-1]["Kernel_Name"]}
+    total = sum(res[n]["decode_kernel_bytes"] + res[n]["merge_kernel_bytes"] for n in res)
+    return {"workload": workload, "lens": list(lens), "counters": res,
+            "hbm_bytes_per_call": total, "decode_src_sha256_16": _sha(DECODE_SRC)}
+
+
 def build_layer(w, cfg, layer, B, T0, max_pages, steps, dev, P, synth, torch):
     """Cache of one layer holding tokens [0, T0) and the inputs of `steps` decode steps."""
     npairs = w.d // 2
@@ -142,7 +202,17 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-reps", type=int, default=5)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"run one plain {COPY_MB} MiB device copy (HBM counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of this script and exit (no GPU)")
+    ap.add_argument("--lens", type=int, nargs=3, metavar=("SINK", "PAGES", "RES"),
+                    help="with --pmc-summary: the cache lengths of the profiled decode call")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload,
+                                     args.lens), indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence and KV head with no exchange between GPUs)",
@@ -242,22 +312,32 @@ def main():
     torch.cuda.synchronize()
     lens_now = (caches[0].sink_len, caches[0].n_pages, caches[0].res_len)
     qlast = [inputs[l][0][W + K - 1] for l in range(layers)]
+    # the layers' calls run back to back between one pair of events (per-call event pairs
+    # would add the event overhead to every call); the first repetition is a warm-up
     durs = []
-    for rep in range(args.roofline_reps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in caches]
+    for rep in range(args.roofline_reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         for layer, c in enumerate(caches):
-            ev[layer][0].record()
             c.attend(qlast[layer], outs[layer])
-            ev[layer][1].record()
+        e1.record()
         torch.cuda.synchronize()
         if rep:
-            durs += [a.elapsed_time(b) * 1e-3 for a, b in ev]
+            durs.append(e0.elapsed_time(e1) * 1e-3 / layers)
     call_s = float(np.mean(durs))
     call_bytes = decode_bytes(cfg, lens_now, w.B, kpb, vpb)
     achieved = call_bytes / call_s / 1e9
     _say(f"[bench] decode call: {call_bytes / 1e6:.2f} MB in {call_s * 1e6:.2f} us avg "
-         f"(median {np.median(durs) * 1e6:.2f}) -> {achieved:.0f} GB/s")
+         f"(min {np.min(durs) * 1e6:.2f}) -> {achieved:.0f} GB/s")
+    traffic = measured_traffic(w.name, lens_now)
+    _say(f"[bench] decode call lens (sink, pages, residual) = {lens_now}")
+    if args.copy_calibration:
+        src = torch.empty(COPY_MB * 2**20 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- page quantization: one bulk launch per kernel over every layer's residual buffers
     n_jobs = layers * w.B * w.H_kv
@@ -343,8 +423,9 @@ def main():
                    "b_V": w.b_V, "g_V": w.g_V, "N_s": w.N_s, "N": w.N,
                    "parallelism": "single GPU", "timed": "one HIP graph of K steps"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "pnmix_decode_attn (split kernel + merge kernel, one call)",
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "pnmix_decode_attn = decode_kernel (page and fp16 splits) + "
+                               "decode_merge_kernel, one call",
                      "bytes_per_call": call_bytes, "avg_call_us": call_s * 1e6},
         "page_quant": quant,
         "prefill_score": score,

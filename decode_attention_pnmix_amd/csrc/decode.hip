@@ -49,6 +49,7 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kN = 128;  // page and residual length
 constexpr int kMaxSplits = 256;  // split-K partitions per (sequence, KV head): one merge thread each
+constexpr int kWS = kN + 16;     // row stride of the p.V digit table (rows on distinct banks)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeArgs {
@@ -67,15 +68,17 @@ struct DecodeArgs {
   float qscale;    // sm_scale * log2(e)
   int H_q, H_kv, n_g, pairing, n_hi, n_sal, G, KG, g_V, NGV, N_s, max_pages, words;
   int64_t kpb, vpb;
-  int splits, page_splits, pps;
-  int lds_T;       // bytes of the digit table (KG * NT * 16 rows * TL)
+  int splits, page_splits;
+  int lds_T;       // bytes of the q.K digit table (KG * NT * 16 rows * TL)
 };
 
 template <int D>
 struct Shape {
   static constexpr int KL = (D + 63) / 64;   // 64-channel K-steps over the LSB plane
   static constexpr int KHM = KL;             // at most this many over the upper-bit plane
-  static constexpr int TL = 64 * (KL + KHM); // bytes per (head, digit) row of the digit table
+  // bytes per (head, digit) row of the q.K digit table: 64 per K-step, plus 16 so that the
+  // 16 rows of an A-operand read start on 16 different 4-bank groups
+  static constexpr int TL = 64 * (KL + KHM) + 16;
   static constexpr int NM0 = (D + 63) / 64;  // 16-quad column halves of the p.V product
   static constexpr int JL = D / 4;           // 4-channel units per head
 };
@@ -380,8 +383,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   const int n_pages = min(max(L.n_pages, 0), a.max_pages);
   const int64_t pbase = (bh * a.splits + split) * ng;
 
-  const int p0 = split * a.pps;
-  const int p1 = min(p0 + a.pps, n_pages);
+  // this sequence's pages split evenly over the page splits (sizes differ by at most one)
+  const int p0 = (int)((int64_t)split * n_pages / a.page_splits);
+  const int p1 = (int)((int64_t)(split + 1) * n_pages / a.page_splits);
   if (p0 >= p1) {
     write_empty_partial<D>(a, pbase);
     return;
@@ -391,12 +395,12 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   const int KH = (n_sal + 63) / 64;
   const int JH = (n_sal + 3) / 4;  // 4-rank units per head of the upper-bit part
 
-  // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NT][NGV][16][N] bytes;
+  // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NT][NGV][16][kWS] bytes;
   // key scales of the page [KG][D] fp16; bias [KG][NH] f32; salient channel of each rank [D]
   // int16; head maxima [NH] f32.
   uint8_t* T = lds;
   uint8_t* W = lds + a.lds_T;
-  uint16_t* Sl = reinterpret_cast<uint16_t*>(W + NT * NGV * 16 * kN);
+  uint16_t* Sl = reinterpret_cast<uint16_t*>(W + NT * NGV * 16 * kWS);
   float* biasl = reinterpret_cast<float*>(Sl + 4 * D);
   int16_t* sal = reinterpret_cast<int16_t*>(biasl + 4 * NH);
   float* qm = reinterpret_cast<float*>(sal + D);
@@ -741,9 +745,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         for (int e = 0; e < 8; ++e) x[e] = digits4((int)(p[e] * sp[g][e]));
         transpose4(x, d0);
         transpose4(x + 4, d1);
-        uint8_t* row = W + ((t * NGV + g) * 16 + 4 * qb) * kN + 8 * oct;
+        uint8_t* row = W + ((t * NGV + g) * 16 + 4 * qb) * kWS + 8 * oct;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) *reinterpret_cast<uint2*>(row + d * kN) = make_uint2(d0[d], d1[d]);
+        for (int d = 0; d < 4; ++d) *reinterpret_cast<uint2*>(row + d * kWS) = make_uint2(d0[d], d1[d]);
       }
     }
     if (__any(rescale)) {
@@ -788,7 +792,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
                                 : (fu == 0 ? 1.0f : 0.0625f);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint8_t* wrow = W + ((t * NGV + g) * 16 + (lane & 15)) * kN + 16 * qb;
+        const uint8_t* wrow = W + ((t * NGV + g) * 16 + (lane & 15)) * kWS + 16 * qb;
         const v4i A0 = *reinterpret_cast<const v4i*>(wrow);
         const v4i A1 = *reinterpret_cast<const v4i*>(wrow + 64);
         v4i c = v4i{0, 0, 0, 0};
@@ -907,13 +911,13 @@ static int n_tiles(const pnmix_cfg& c) {
 
 static size_t lds_T_bytes(const pnmix_cfg& c) {
   const int KL = (c.d + 63) / 64;
-  const int TL = 64 * 2 * KL;
+  const int TL = 64 * 2 * KL + 16;
   return (size_t)(c.N / c.G) * n_tiles(c) * 16 * TL;
 }
 
 static size_t lds_bytes(const pnmix_cfg& c) {
   const int NT = n_tiles(c);
-  const size_t W = (size_t)NT * (c.d / c.g_V) * 16 * kN;
+  const size_t W = (size_t)NT * (c.d / c.g_V) * 16 * kWS;
   return lds_T_bytes(c) + W + 4 * c.d * 2 + 4 * 4 * NT * 4 + c.d * 2 + 4 * NT * 4;
 }
 
@@ -922,27 +926,76 @@ static size_t lds_fp16_bytes(const pnmix_cfg& c) {
   return (size_t)4 * NT * c.d * 2 + 64 * 4 * NT * 4 + 64 * (size_t)c.d * 2;
 }
 
+// Waves of the split kernel that fit on the device at once: the runtime's occupancy for this
+// instantiation and LDS size, times the compute-unit count (defaults without a device).
+static int device_cus() {
+  static const int n = [] {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+        prop.multiProcessorCount <= 0)
+      return 256;
+    return prop.multiProcessorCount;
+  }();
+  return n;
+}
+
+template <int D, int NT, int KG>
+static int blocks_per_cu(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, NT, KG>, 64, lds) !=
+          hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 8;
+  }
+  return n;
+}
+
+template <int D>
+static int blocks_per_cu_d(const pnmix_cfg& c, size_t lds) {
+  const int kg = c.N / c.G;
+  switch (n_tiles(c)) {
+    case 1: return kg == 1 ? blocks_per_cu<D, 1, 1>(lds) : kg == 2 ? blocks_per_cu<D, 1, 2>(lds) : blocks_per_cu<D, 1, 4>(lds);
+    case 2: return kg == 1 ? blocks_per_cu<D, 2, 1>(lds) : kg == 2 ? blocks_per_cu<D, 2, 2>(lds) : blocks_per_cu<D, 2, 4>(lds);
+    default: return kg == 1 ? blocks_per_cu<D, 4, 1>(lds) : kg == 2 ? blocks_per_cu<D, 4, 2>(lds) : blocks_per_cu<D, 4, 4>(lds);
+  }
+}
+
 DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   DecodePlan p;
-  const long long items = (long long)B * c.H_kv;
-  // about two waves per SIMD (256 CUs x 4 SIMDs) over the pages, split evenly
-  const long long target = 2048;
+  const long long items = std::max<long long>((long long)B * c.H_kv, 1);
+  p.lds_bytes = std::max(lds_bytes(c), lds_fp16_bytes(c));
   // fp16 rows: one split per 64-token chunk when the batch is small, else one split walking
   // all chunks (its latency then hides among the page splits)
   const int n16 = items >= 128 ? 1 : (c.N_s + c.N + 63) / 64;
-  int ps = (int)std::max<long long>(1, (target + items - 1) / std::max<long long>(items, 1));
-  ps = std::min(ps, std::max(max_pages, 1));
-  ps = std::min(ps, kMaxSplits - n16);
-  int pps = max_pages > 0 ? (max_pages + ps - 1) / ps : 1;
-  ps = max_pages > 0 ? (max_pages + pps - 1) / pps : 0;
+  int bpc = 8;
+  switch (c.d) {
+    case 32: bpc = blocks_per_cu_d<32>(c, p.lds_bytes); break;
+    case 64: bpc = blocks_per_cu_d<64>(c, p.lds_bytes); break;
+    default: bpc = blocks_per_cu_d<128>(c, p.lds_bytes); break;
+  }
+  const long long resident = (long long)bpc * device_cus();
+  // page splits: fewest rounds of resident waves x pages per wave (+1 for the set-up)
+  int ps = 0;
+  if (max_pages > 0) {
+    long long best = -1;
+    const int ps_max = std::min(max_pages, kMaxSplits - n16);
+    for (int s = 1; s <= ps_max; ++s) {
+      const long long rounds = (items * (s + n16) + resident - 1) / resident;
+      const long long cost = rounds * ((max_pages + s - 1) / s + 1);
+      if (best < 0 || cost < best) {
+        best = cost;
+        ps = s;
+      }
+    }
+  }
   p.page_splits = ps;
-  p.pages_per_split = pps;
+  p.pages_per_split = ps > 0 ? (max_pages + ps - 1) / ps : 0;
   p.splits = ps + n16;
   const int ng = c.H_q / c.H_kv;
   const size_t per = (size_t)items * p.splits * ng;
   const size_t o_bytes = (per * c.d * sizeof(float) + 255) & ~(size_t)255;
   p.ws_bytes = o_bytes + ((per * 2 * sizeof(float) + 255) & ~(size_t)255);
-  p.lds_bytes = std::max(lds_bytes(c), lds_fp16_bytes(c));
   return p;
 }
 
@@ -1017,7 +1070,6 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
   a.vpb = (int64_t)pnmix_v_page_bytes(&c);
   a.splits = p.splits;
   a.page_splits = p.page_splits;
-  a.pps = p.pages_per_split;
   a.lds_T = (int)lds_T_bytes(c);
   hipError_t e;
   switch (c.d) {

@@ -21,7 +21,7 @@ hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* 
 struct DecodePlan {
   int splits;           // split-K partitions per (sequence, KV head): page splits + fp16 chunks
   int page_splits;      // partitions over the packed pages
-  int pages_per_split;  // contiguous pages per page partition
+  int pages_per_split;  // most pages of one page partition (a sequence's pages are split evenly)
   size_t ws_bytes;      // workspace for the partials
   size_t lds_bytes;     // dynamic LDS of the split kernel
 };

@@ -72,10 +72,10 @@ struct DecodeArgs {
   int lds_T;       // bytes of the q.K digit table (KG * NT * 16 rows * TL)
 };
 
-template <int D>
+template <int D, int KH>
 struct Shape {
   static constexpr int KL = (D + 63) / 64;   // 64-channel K-steps over the LSB plane
-  static constexpr int KHM = KL;             // at most this many over the upper-bit plane
+  static constexpr int KHM = KH;             // 64-rank K-steps over the upper-bit plane
   // bytes per (head, digit) row of the q.K digit table: 64 per K-step, plus 16 so that the
   // 16 rows of an A-operand read start on 16 different 4-bank groups
   static constexpr int TL = 64 * (KL + KHM) + 16;
@@ -143,6 +143,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   return max(x, (uint32_t)__shfl_xor((int)x, 32, 64));
 }
 
+__device__ __forceinline__ float wave_max_f(float x) {
+  x = fmaxf(x, dpp_c<0xB1>(x));
+  x = fmaxf(x, dpp_c<0x4E>(x));
+  x = fmaxf(x, dpp_c<0x124>(x));
+  x = fmaxf(x, dpp_c<0x128>(x));
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+
 __device__ __forceinline__ float f16lo(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
 }
@@ -176,6 +185,24 @@ __device__ __forceinline__ uint32_t digits4(int x) {
 __device__ __forceinline__ float combine4(const v4i& c) {
   const int lo = c[0] + (c[1] << 8), hi = c[2] + (c[3] << 8);
   return __builtin_fmaf((float)hi, 65536.0f, (float)lo);
+}
+// a * f16(low or high half of h) + c in one v_fma_mix_f32 (exact widening, one rounding)
+__device__ __forceinline__ float fma_mix_lo(float a, uint32_t h, float c) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(h), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float fma_mix_hi(float a, uint32_t h, float c) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(h), "v"(c));
+  return r;
+}
+typedef uint16_t v2u16 __attribute__((ext_vector_type(2)));
+// packed max of two pairs of non-negative fp16 values through their bit patterns (which order
+// like the values), without the NaN canonicalisation of a floating-point max
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2u16, a),
+                                                                __builtin_bit_cast(v2u16, b)));
 }
 // 4 x 4 byte transpose: out[d] byte i = byte d of y[i]
 __device__ __forceinline__ void transpose4(const uint32_t y[4], uint32_t out[4]) {
@@ -213,22 +240,30 @@ __device__ __forceinline__ uint32_t hi_field(uint32_t w) {
 }
 __device__ constexpr float kInvSL[8] = {1.0f, 0.5f, 0.25f, 0.125f, 0.0625f, 0.5f, 0.125f, 0.125f};
 
-__device__ __forceinline__ v4u load16(const uint8_t* p) {
-  return *reinterpret_cast<const v4u*>(p);
+// Buffer loads: one resource per (sequence, KV head) cache, a wave-uniform page offset in an
+// SGPR and loop-invariant lane offsets, so a page costs no per-lane address arithmetic.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+  const int n = (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
-
-// 16 bytes at an address that is only 2-byte aligned (upper-bit plane rows of odd length)
-__device__ __forceinline__ v4u load16_a2(const uint8_t* p) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const uint32_t* q = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
-  const uint32_t sh = (uint32_t)(a & 3);
+__device__ __forceinline__ v4u bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v[0], v[1]);
+}
+// 16 bytes at a 2-byte-aligned offset: five aligned dwords and a byte shift
+__device__ __forceinline__ v4u bload16_a2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const uint32_t a = voff & ~3u, sh = voff & 3u;
   uint32_t d[5];
 #pragma unroll
-  for (int i = 0; i < 5; ++i) d[i] = q[i];
-  v4u r;
+  for (int i = 0; i < 5; ++i) d[i] = __builtin_amdgcn_raw_buffer_load_b32(r, a + 4 * i, soff, 0);
+  v4u out;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = sh ? __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh) : d[i];
-  return r;
+  for (int i = 0; i < 4; ++i) out[i] = sh ? __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh) : d[i];
+  return out;
 }
 
 // ------------------------------------------------------------------------- partial writers
@@ -366,9 +401,9 @@ __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, int64
 
 // ----------------------------------------------------------------------------- page split
 
-template <int D, int NT, int KG>
+template <int D, int NT, int KG, int KH>
 __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t bh) {
-  using S_ = Shape<D>;
+  using S_ = Shape<D, KH>;
   constexpr int KL = S_::KL, KHM = S_::KHM, TL = S_::TL, JL = S_::JL;
   constexpr int NH = 4 * NT;
   constexpr int UK = (NT * D + 63) / 64;   // LSB prep units per lane
@@ -392,7 +427,6 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   }
 
   const int G = a.G, n_sal = a.n_sal, NGV = a.NGV;
-  const int KH = (n_sal + 63) / 64;
   const int JH = (n_sal + 3) / 4;  // 4-rank units per head of the upper-bit part
 
   // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NT][NGV][16][kWS] bytes;
@@ -494,26 +528,25 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // soon as the current page's q.K is done, so their latency hides behind softmax and p.V.
   v4u wL[KL], wH0[KHM], wH1[KHM];
   uint2 sv[UK][KG], zv[UK][KG];  // [k][kg] 4 fp16 of S and Z for the unit's channels
+  const rsrc_t krs = buf_rsrc(a.k_pages + page_base * a.kpb, (int64_t)a.max_pages * a.kpb);
+  const rsrc_t vrs = buf_rsrc(a.v_pages + page_base * a.vpb, (int64_t)a.max_pages * a.vpb);
   auto load_k = [&](int pgk) {
-    const uint8_t* kp = a.k_pages + (page_base + pgk) * a.kpb;
+    const uint32_t so = (uint32_t)(pgk * a.kpb);
 #pragma unroll
     for (int ks = 0; ks < KL; ++ks) {
       const int c0 = 64 * ks + 16 * qb;
-      wL[ks] = c0 < D ? load16(kp + oct * D + c0) : v4u{0, 0, 0, 0};
+      wL[ks] = c0 < D ? bload16(krs, oct * D + c0, so) : v4u{0, 0, 0, 0};
     }
 #pragma unroll
     for (int ks = 0; ks < KHM; ++ks) {
-      const int r0 = 64 * ks + 16 * qb;
-      wH0[ks] = wH1[ks] = v4u{0, 0, 0, 0};
-      if (ks < KH && r0 < n_sal) {
-        const uint8_t* hp = kp + kN * D / 8 + r0;
-        if ((n_sal & 15) == 0) {
-          wH0[ks] = *reinterpret_cast<const v4u*>(hp + (2 * oct) * n_sal);
-          wH1[ks] = *reinterpret_cast<const v4u*>(hp + (2 * oct + 1) * n_sal);
-        } else {
-          wH0[ks] = load16_a2(hp + (2 * oct) * n_sal);
-          wH1[ks] = load16_a2(hp + (2 * oct + 1) * n_sal);
-        }
+      // ranks past n_sal read other bytes of the page: their A columns are zero
+      const uint32_t h0 = kN * D / 8 + 64 * ks + 16 * qb + (2 * oct) * n_sal;
+      if ((n_sal & 15) == 0) {
+        wH0[ks] = bload16(krs, h0, so);
+        wH1[ks] = bload16(krs, h0 + n_sal, so);
+      } else {
+        wH0[ks] = bload16_a2(krs, h0, so);
+        wH1[ks] = bload16_a2(krs, h0 + n_sal, so);
       }
     }
 #pragma unroll
@@ -524,8 +557,8 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       for (int kg = 0; kg < KG; ++kg) {
         sv[k][kg] = zv[k][kg] = make_uint2(0u, 0u);
         if (u < NT * D) {
-          sv[k][kg] = *reinterpret_cast<const uint2*>(kp + sOff + 2 * (kg * D + 4 * j));
-          zv[k][kg] = *reinterpret_cast<const uint2*>(kp + zOff + 2 * (kg * D + 4 * j));
+          sv[k][kg] = bload8(krs, sOff + 2 * (kg * D + 4 * j), so);
+          zv[k][kg] = bload8(krs, zOff + 2 * (kg * D + 4 * j), so);
         }
       }
     }
@@ -533,9 +566,8 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   load_k(p0);
 
   for (int pg = p0; pg < p1; ++pg) {
-    const uint8_t* vp = a.v_pages + (page_base + pg) * a.vpb;
-    const uint16_t* VS = reinterpret_cast<const uint16_t*>(vp + kN * D / 4);  // [NGV][N]
-    const uint16_t* VZ = VS + NGV * kN;
+    const uint32_t vso = (uint32_t)(pg * a.vpb);
+    const uint32_t vS = kN * D / 4 + 2 * 8 * oct;  // S [NGV][N] fp16 after the codes, then Z
 
     // ---- value side of this page, issued now, consumed after q.K: scales and offsets of
     // this lane's q.K keys (8 oct + b) per group; code bytes of its tile columns per K-step
@@ -543,14 +575,17 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     v4u cv[NMB][2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      sS[g] = g < NGV ? *reinterpret_cast<const v4u*>(VS + g * kN + 8 * oct) : v4u{0, 0, 0, 0};
-      zZ[g] = g < NGV ? *reinterpret_cast<const v4u*>(VZ + g * kN + 8 * oct) : v4u{0, 0, 0, 0};
+      // groups past NGV repeat the last one: the page maximum is unchanged and the
+      // per-group loops stop at NGV
+      const int gc = min(g, NGV - 1);
+      sS[g] = bload16(vrs, vS + 2 * gc * kN, vso);
+      zZ[g] = bload16(vrs, vS + 2 * (NGV + gc) * kN, vso);
     }
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        cv[mb][ks] = load16(vp + (int64_t)(mb * MW + vcol) * kN + 64 * ks + 16 * qb);
+        cv[mb][ks] = bload16(vrs, (mb * MW + vcol) * kN + 64 * ks + 16 * qb, vso);
 
     // ---- key scales: page maximum -> per-head fixed-point exponent
     uint32_t smax = 0u;
@@ -560,12 +595,11 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       const int j = u % JL;
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
-        smax = max(smax, max(max(sv[k][kg].x & 0xFFFFu, sv[k][kg].x >> 16),
-                             max(sv[k][kg].y & 0xFFFFu, sv[k][kg].y >> 16)));
+        smax = pk_max_u16(smax, pk_max_u16(sv[k][kg].x, sv[k][kg].y));
         if (u < JL) *reinterpret_cast<uint2*>(Sl + kg * D + 4 * j) = sv[k][kg];
       }
     }
-    smax = wave_max_u32(smax);
+    smax = wave_max_u32(max(smax & 0xFFFFu, smax >> 16));
     const float Smax = (float)__builtin_bit_cast(_Float16, (uint16_t)smax);
     // 2^sigma with |qt S 2^sigma| < 2^30 for every channel of the head
     auto sigma_of = [&](float qmax) -> int {
@@ -670,7 +704,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
           _Pragma("unroll") for (int ks = 0; ks < KL; ++ks)                                    \
             c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[kg][t][ks], bL[ks], c, 0, 0, 0);       \
           _Pragma("unroll") for (int ks = 0; ks < KHM; ++ks)                                   \
-            if (ks < KH) c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[kg][t][KL + ks], bH[ks], c, 0, 0, 0); \
+            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[kg][t][KL + ks], bH[ks], c, 0, 0, 0);    \
           csel = (KG == 1 || kg == kg_lane) ? c : csel;                                        \
         }                                                                                      \
         lg[t][BB] = __builtin_fmaf(combine4(csel), inv2s[t] * kInvSL[BB], bias[t]);            \
@@ -684,30 +718,19 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     if (pg + 1 < p1) load_k(pg + 1);
 
     // ---- p.V fixed point: w = p S 2^sv with p <= 1 and S <= the page's largest value scale,
-    // so |w| < 2^30 and four balanced base-256 digits hold it exactly
-    uint32_t svmax = 0u;
+    // so 0 <= w < 2^30: four balanced base-256 digits hold its integer part exactly
+    uint32_t svm2 = 0u;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) svmax = max(svmax, max(sS[g][e] & 0xFFFFu, sS[g][e] >> 16));
-    svmax = wave_max_u32(svmax);
+      for (int e = 0; e < 4; ++e) svm2 = pk_max_u16(svm2, sS[g][e]);  // S >= 0: bit order
+    const float svmax = wave_max_f(fmaxf(f16lo(svm2), f16hi(svm2)));
     int sv_e = 0;
-    {
-      const float Sv = (float)__builtin_bit_cast(_Float16, (uint16_t)svmax);
-      if (Sv > 0.0f) {
-        const int e = (int)((__builtin_bit_cast(uint32_t, Sv) >> 23) & 0xFF) - 127;
-        sv_e = min(max(29 - e, -126), 126);
-      }
+    if (svmax > 0.0f) {
+      const int e = (int)((__builtin_bit_cast(uint32_t, svmax) >> 23) & 0xFF) - 127;
+      sv_e = min(max(29 - e, -126), 126);
     }
     const float sv2 = pow2i(sv_e);
-    float sp[4][8];  // S 2^sv of this lane's keys per group
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sp[g][2 * e] = f16lo(sS[g][e]) * sv2;
-        sp[g][2 * e + 1] = f16hi(sS[g][e]) * sv2;
-      }
 
     // ---- online softmax per head, value-offset term on the vector ALU, digits of w to LDS
     bool rescale = false;
@@ -722,32 +745,36 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       alpha[t] = __builtin_amdgcn_exp2f(m_run[t] - mn);
       rescale |= (alpha[t] != 1.0f);
       m_run[t] = mn;
-      float p[8], ps = 0.0f;
+      float p[8], pw[8], ps = 0.0f;
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
         p[bb] = __builtin_amdgcn_exp2f(lg[t][bb] - mn);
         ps += p[bb];
+        pw[bb] = p[bb] * sv2;
       }
       l_run[t] = l_run[t] * alpha[t] + ps;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         if (g >= NGV) break;
-        const v4u zz = zZ[g];
-        float s = zacc[t][g] * alpha[t];
+        const v4u zz = zZ[g], ss = sS[g];
+        float zs = zacc[t][g] * alpha[t];
+        uint32_t x[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s = __builtin_fmaf(p[2 * e], f16lo(zz[e]), s);
-          s = __builtin_fmaf(p[2 * e + 1], f16hi(zz[e]), s);
+          zs = fma_mix_lo(p[2 * e], zz[e], zs);
+          zs = fma_mix_hi(p[2 * e + 1], zz[e], zs);
+          // integer part of w plus the balanced-digit offset (the XOR follows the transpose)
+          x[2 * e] = (uint32_t)(int)fma_mix_lo(pw[2 * e], ss[e], 0.0f) + 0x80808080u;
+          x[2 * e + 1] = (uint32_t)(int)fma_mix_hi(pw[2 * e + 1], ss[e], 0.0f) + 0x80808080u;
         }
-        zacc[t][g] = s;
-        uint32_t x[8], d0[4], d1[4];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = digits4((int)(p[e] * sp[g][e]));
+        zacc[t][g] = zs;
+        uint32_t d0[4], d1[4];
         transpose4(x, d0);
         transpose4(x + 4, d1);
         uint8_t* row = W + ((t * NGV + g) * 16 + 4 * qb) * kWS + 8 * oct;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) *reinterpret_cast<uint2*>(row + d * kWS) = make_uint2(d0[d], d1[d]);
+        for (int d = 0; d < 4; ++d)
+          *reinterpret_cast<uint2*>(row + d * kWS) = make_uint2(d0[d] ^ 0x80808080u, d1[d] ^ 0x80808080u);
       }
     }
     if (__any(rescale)) {
@@ -884,13 +911,15 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
 
 // One launch per decode call: blockIdx.x < page_splits walks packed pages, the remaining
 // splits take one 64-token chunk each of the fp16 sink and residual rows, concurrently.
-template <int D, int NT, int KG>
-__global__ void __launch_bounds__(64) decode_kernel(DecodeArgs a) {
+// One head tile fits two waves per SIMD (256 registers); ask the compiler to stay there.
+template <int D, int NT, int KG, int KH>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 && KG == 1 ? 2 : 1)))
+decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int split = blockIdx.x;
   const int64_t bh = blockIdx.y;
   if (split < a.page_splits) {
-    page_split<D, NT, KG>(a, lds, split, bh);
+    page_split<D, NT, KG, KH>(a, lds, split, bh);
   } else {
     const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
     const pnmix_seq_len L = a.lens[b];
@@ -909,9 +938,13 @@ static int n_tiles(const pnmix_cfg& c) {
   return t == 3 ? 4 : t;
 }
 
+// 64-rank K-steps over the upper-bit plane: two only for d = 128 with more than 64 salient
+// channels
+static int hi_steps(const pnmix_cfg& c) { return (c.d == 128 && 2 * c.n_hi_pairs > 64) ? 2 : 1; }
+
 static size_t lds_T_bytes(const pnmix_cfg& c) {
   const int KL = (c.d + 63) / 64;
-  const int TL = 64 * 2 * KL + 16;
+  const int TL = 64 * (KL + hi_steps(c)) + 16;
   return (size_t)(c.N / c.G) * n_tiles(c) * 16 * TL;
 }
 
@@ -924,6 +957,39 @@ static size_t lds_bytes(const pnmix_cfg& c) {
 static size_t lds_fp16_bytes(const pnmix_cfg& c) {
   const int NT = n_tiles(c);
   return (size_t)4 * NT * c.d * 2 + 64 * 4 * NT * 4 + 64 * (size_t)c.d * 2;
+}
+
+// f.template run<D, NT, KG, KH>() for the split kernel instantiation of the configuration
+template <int D, int NT, int KG, class F>
+static auto dispatch_kh(const pnmix_cfg& c, const F& f) {
+  if constexpr (D == 128) {
+    if (hi_steps(c) == 2) return f.template run<D, NT, KG, 2>();
+  }
+  return f.template run<D, NT, KG, 1>();
+}
+template <int D, int NT, class F>
+static auto dispatch_kg(const pnmix_cfg& c, const F& f) {
+  switch (c.N / c.G) {
+    case 1: return dispatch_kh<D, NT, 1>(c, f);
+    case 2: return dispatch_kh<D, NT, 2>(c, f);
+    default: return dispatch_kh<D, NT, 4>(c, f);
+  }
+}
+template <int D, class F>
+static auto dispatch_nt(const pnmix_cfg& c, const F& f) {
+  switch (n_tiles(c)) {
+    case 1: return dispatch_kg<D, 1>(c, f);
+    case 2: return dispatch_kg<D, 2>(c, f);
+    default: return dispatch_kg<D, 4>(c, f);
+  }
+}
+template <class F>
+static auto dispatch(const pnmix_cfg& c, const F& f) {
+  switch (c.d) {
+    case 32: return dispatch_nt<32>(c, f);
+    case 64: return dispatch_nt<64>(c, f);
+    default: return dispatch_nt<128>(c, f);
+  }
 }
 
 // Waves of the split kernel that fit on the device at once: the runtime's occupancy for this
@@ -940,26 +1006,19 @@ static int device_cus() {
   return n;
 }
 
-template <int D, int NT, int KG>
-static int blocks_per_cu(size_t lds) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, NT, KG>, 64, lds) !=
-          hipSuccess || n <= 0) {
-    (void)hipGetLastError();
-    return 8;
+struct BlocksPerCu {
+  size_t lds;
+  template <int D, int NT, int KG, int KH>
+  int run() const {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, NT, KG, KH>, 64, lds) !=
+            hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      return 8;
+    }
+    return n;
   }
-  return n;
-}
-
-template <int D>
-static int blocks_per_cu_d(const pnmix_cfg& c, size_t lds) {
-  const int kg = c.N / c.G;
-  switch (n_tiles(c)) {
-    case 1: return kg == 1 ? blocks_per_cu<D, 1, 1>(lds) : kg == 2 ? blocks_per_cu<D, 1, 2>(lds) : blocks_per_cu<D, 1, 4>(lds);
-    case 2: return kg == 1 ? blocks_per_cu<D, 2, 1>(lds) : kg == 2 ? blocks_per_cu<D, 2, 2>(lds) : blocks_per_cu<D, 2, 4>(lds);
-    default: return kg == 1 ? blocks_per_cu<D, 4, 1>(lds) : kg == 2 ? blocks_per_cu<D, 4, 2>(lds) : blocks_per_cu<D, 4, 4>(lds);
-  }
-}
+};
 
 DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   DecodePlan p;
@@ -968,12 +1027,7 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   // fp16 rows: one split per 64-token chunk when the batch is small, else one split walking
   // all chunks (its latency then hides among the page splits)
   const int n16 = items >= 128 ? 1 : (c.N_s + c.N + 63) / 64;
-  int bpc = 8;
-  switch (c.d) {
-    case 32: bpc = blocks_per_cu_d<32>(c, p.lds_bytes); break;
-    case 64: bpc = blocks_per_cu_d<64>(c, p.lds_bytes); break;
-    default: bpc = blocks_per_cu_d<128>(c, p.lds_bytes); break;
-  }
+  const int bpc = dispatch(c, BlocksPerCu{p.lds_bytes});
   const long long resident = (long long)bpc * device_cus();
   // page splits: fewest rounds of resident waves x pages per wave (+1 for the set-up)
   int ps = 0;
@@ -999,36 +1053,22 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   return p;
 }
 
-template <int D, int NT, int KG>
-static hipError_t launch_k(const DecodePlan& p, int B, const pnmix_cfg& c, const DecodeArgs& a,
-                           hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, NT, KG>), dim3(p.splits, B * c.H_kv), dim3(64),
-                     p.lds_bytes, stream, a);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(B * c.H_q), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-template <int D, int NT>
-static hipError_t launch_t(const DecodePlan& p, int B, const pnmix_cfg& c, const DecodeArgs& a,
-                           hipStream_t stream) {
-  switch (c.N / c.G) {
-    case 1: return launch_k<D, NT, 1>(p, B, c, a, stream);
-    case 2: return launch_k<D, NT, 2>(p, B, c, a, stream);
-    default: return launch_k<D, NT, 4>(p, B, c, a, stream);
+struct Launch {
+  const DecodePlan& p;
+  int B;
+  const pnmix_cfg& c;
+  const DecodeArgs& a;
+  hipStream_t stream;
+  template <int D, int NT, int KG, int KH>
+  hipError_t run() const {
+    hipLaunchKernelGGL((decode_kernel<D, NT, KG, KH>), dim3(p.splits, B * c.H_kv), dim3(64),
+                       p.lds_bytes, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(B * c.H_q), dim3(256), 0, stream, a);
+    return hipGetLastError();
   }
-}
-
-template <int D>
-static hipError_t launch_d(const DecodePlan& p, int B, const pnmix_cfg& c, const DecodeArgs& a,
-                           hipStream_t stream) {
-  switch (n_tiles(c)) {
-    case 1: return launch_t<D, 1>(p, B, c, a, stream);
-    case 2: return launch_t<D, 2>(p, B, c, a, stream);
-    default: return launch_t<D, 4>(p, B, c, a, stream);
-  }
-}
+};
 
 hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_t* q,
                          const uint16_t* k_sink, const uint16_t* v_sink, const uint8_t* k_pages,
@@ -1071,13 +1111,7 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
   a.splits = p.splits;
   a.page_splits = p.page_splits;
   a.lds_T = (int)lds_T_bytes(c);
-  hipError_t e;
-  switch (c.d) {
-    case 32: e = launch_d<32>(p, B, c, a, stream); break;
-    case 64: e = launch_d<64>(p, B, c, a, stream); break;
-    default: e = launch_d<128>(p, B, c, a, stream); break;
-  }
-  return e;
+  return dispatch(c, Launch{p, B, c, a, stream});
 }
 
 }  // namespace pnmix

@@ -110,46 +110,65 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
 }
-// all-reduce over aligned groups of W lanes (W a power of two, 8 <= W <= 64): DPP inside a row
-// of 16, lane shuffles across rows
-template <int W>
-__device__ __forceinline__ float group_sum(float x) {
+// Across the four 16-lane rows: the row results are read into scalar registers (v_readlane)
+// and combined there, with no LDS round trip.  rowv(x, r) = x of row r (x uniform per row).
+__device__ __forceinline__ float rowv(float x, int r) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16 * r));
+}
+__device__ __forceinline__ float row_sum_all16(float x) {  // x: row all-reduced
   x = x + dpp_c<0xB1>(x);
   x = x + dpp_c<0x4E>(x);
-  if (W == 8) return x + __shfl_xor(x, 4, 64);
   x = x + dpp_c<0x124>(x);
-  x = x + dpp_c<0x128>(x);
-  if (W >= 32) x = x + __shfl_xor(x, 16, 64);
-  if (W >= 64) x = x + __shfl_xor(x, 32, 64);
-  return x;
+  return x + dpp_c<0x128>(x);
+}
+__device__ __forceinline__ float row_max_all16(float x) {
+  x = fmaxf(x, dpp_c<0xB1>(x));
+  x = fmaxf(x, dpp_c<0x4E>(x));
+  x = fmaxf(x, dpp_c<0x124>(x));
+  return fmaxf(x, dpp_c<0x128>(x));
+}
+
+// all-reduce over aligned groups of W lanes (W a power of two, 8 <= W <= 64)
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  if (W == 8) {
+    x = x + dpp_c<0xB1>(x);
+    x = x + dpp_c<0x4E>(x);
+    return x + dpp_c<0x141>(x);  // row_half_mirror: lane i and 7 - i of each 8
+  }
+  x = row_sum_all16(x);
+  if (W == 16) return x;
+  const float h0 = rowv(x, 0) + rowv(x, 1), h1 = rowv(x, 2) + rowv(x, 3);
+  if (W == 32) return threadIdx.x % 64 < 32 ? h0 : h1;
+  return h0 + h1;
 }
 template <int W>
 __device__ __forceinline__ float group_max(float x) {
-  x = fmaxf(x, dpp_c<0xB1>(x));
-  x = fmaxf(x, dpp_c<0x4E>(x));
-  if (W == 8) return fmaxf(x, __shfl_xor(x, 4, 64));
-  x = fmaxf(x, dpp_c<0x124>(x));
-  x = fmaxf(x, dpp_c<0x128>(x));
-  if (W >= 32) x = fmaxf(x, __shfl_xor(x, 16, 64));
-  if (W >= 64) x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+  if (W == 8) {
+    x = fmaxf(x, dpp_c<0xB1>(x));
+    x = fmaxf(x, dpp_c<0x4E>(x));
+    return fmaxf(x, dpp_c<0x141>(x));
+  }
+  x = row_max_all16(x);
+  if (W == 16) return x;
+  const float h0 = fmaxf(rowv(x, 0), rowv(x, 1)), h1 = fmaxf(rowv(x, 2), rowv(x, 3));
+  if (W == 32) return threadIdx.x % 64 < 32 ? h0 : h1;
+  return fmaxf(h0, h1);
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   x = max(x, dpp_u<0xB1>(x));
   x = max(x, dpp_u<0x4E>(x));
   x = max(x, dpp_u<0x124>(x));
   x = max(x, dpp_u<0x128>(x));
-  x = max(x, (uint32_t)__shfl_xor((int)x, 16, 64));
-  return max(x, (uint32_t)__shfl_xor((int)x, 32, 64));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
-
-__device__ __forceinline__ float wave_max_f(float x) {
-  x = fmaxf(x, dpp_c<0xB1>(x));
-  x = fmaxf(x, dpp_c<0x4E>(x));
-  x = fmaxf(x, dpp_c<0x124>(x));
-  x = fmaxf(x, dpp_c<0x128>(x));
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+// maximum over the wave of non-negative floats (their bit patterns order like the values)
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  return __builtin_bit_cast(float, wave_max_u32(__builtin_bit_cast(uint32_t, x)));
 }
 
 __device__ __forceinline__ float f16lo(uint32_t w) {
@@ -724,7 +743,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int e = 0; e < 4; ++e) svm2 = pk_max_u16(svm2, sS[g][e]);  // S >= 0: bit order
-    const float svmax = wave_max_f(fmaxf(f16lo(svm2), f16hi(svm2)));
+    const float svmax = wave_max_nonneg(fmaxf(f16lo(svm2), f16hi(svm2)));
     int sv_e = 0;
     if (svmax > 0.0f) {
       const int e = (int)((__builtin_bit_cast(uint32_t, svmax) >> 23) & 0xFF) - 127;

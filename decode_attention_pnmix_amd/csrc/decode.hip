@@ -51,6 +51,7 @@ constexpr int kN = 128;  // page and residual length
 constexpr int kMaxSplits = 256;  // split-K partitions per (sequence, KV head): one merge thread each
 constexpr int kWS = kN + 16;     // row stride of the p.V digit table (rows on distinct banks)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTwo23 = 8388608.0f;  // y + 2^23 rounds y in [0, 2^23) to an integer (RNE)
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -222,6 +223,24 @@ typedef uint16_t v2u16 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2u16, a),
                                                                 __builtin_bit_cast(v2u16, b)));
+}
+// sum_t x_t B_t from the p.V digit sums: c[0], c[1] of digits stored as u - 128, c[2] of the
+// top digit, c[3] = sum_t B_t from the ones row; every partial is exact in int32 and the
+// three terms are non-negative (no cancellation in fp32)
+__device__ __forceinline__ float combine_pv(const v4i& c) {
+  const int off = c[3] << 7;
+  const int lo = (c[0] + off) + ((c[1] + off) << 8);
+  return __builtin_fmaf((float)c[2], 65536.0f, (float)lo);
+}
+// bytes 0..2 of four words, transposed: out[d] byte i = byte d of y[i]
+__device__ __forceinline__ void transpose3(const uint32_t y[4], uint32_t out[3]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(y[1], y[0], 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(y[1], y[0], 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(y[3], y[2], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(y[3], y[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
 }
 // 4 x 4 byte transpose: out[d] byte i = byte d of y[i]
 __device__ __forceinline__ void transpose4(const uint32_t y[4], uint32_t out[4]) {
@@ -460,6 +479,12 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 
   // ---- once per split: clear the digit table, salient ranks, scaled queries
   for (int i = lane * 16; i < a.lds_T; i += 64 * 16) *reinterpret_cast<v4u*>(T + i) = v4u{0, 0, 0, 0};
+  // p.V digit rows (head, 3) are all ones: their sums are the column sums of the value codes
+  for (int i = lane; i < NT * NGV * 4 * (kN / 16); i += 64) {
+    const int r = i / (kN / 16), c16 = i % (kN / 16);
+    *reinterpret_cast<v4u*>(W + (4 * r + 3) * kWS + 16 * c16) =
+        v4u{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+  }
   const uint32_t* mrow = a.mask + bh * a.words;
   for (int c = lane; c < D; c += 64) sal[c] = -1;
   __syncthreads();
@@ -736,24 +761,20 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     // ---- the key side of this page is consumed: fetch the next page's
     if (pg + 1 < p1) load_k(pg + 1);
 
-    // ---- p.V fixed point: w = p S 2^sv with p <= 1 and S <= the page's largest value scale,
-    // so 0 <= w < 2^30: four balanced base-256 digits hold its integer part exactly
+    // ---- p.V fixed point, per head: x = rne(p S 2^sh) with 2^sh above the head's largest
+    // p on this page times the page's largest value scale, so 0 <= x < 2^23 (23 bits relative
+    // to the page's own largest term, whatever the running maximum of earlier pages)
     uint32_t svm2 = 0u;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int e = 0; e < 4; ++e) svm2 = pk_max_u16(svm2, sS[g][e]);  // S >= 0: bit order
     const float svmax = wave_max_nonneg(fmaxf(f16lo(svm2), f16hi(svm2)));
-    int sv_e = 0;
-    if (svmax > 0.0f) {
-      const int e = (int)((__builtin_bit_cast(uint32_t, svmax) >> 23) & 0xFF) - 127;
-      sv_e = min(max(29 - e, -126), 126);
-    }
-    const float sv2 = pow2i(sv_e);
 
     // ---- online softmax per head, value-offset term on the vector ALU, digits of w to LDS
     bool rescale = false;
     float alpha[NT];
+    int sh[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       float pm = lg[t][0];
@@ -764,6 +785,13 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       alpha[t] = __builtin_amdgcn_exp2f(m_run[t] - mn);
       rescale |= (alpha[t] != 1.0f);
       m_run[t] = mn;
+      {
+        const float top = __builtin_amdgcn_exp2f(pm - mn) * svmax;  // >= every w of this head
+        int e = 0;
+        if (top > 0.0f) e = (int)((__builtin_bit_cast(uint32_t, top) >> 23) & 0xFF) - 127;
+        sh[t] = min(max(22 - e, -126), 126);
+      }
+      const float sv2 = pow2i(sh[t]);
       float p[8], pw[8], ps = 0.0f;
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
@@ -782,18 +810,19 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         for (int e = 0; e < 4; ++e) {
           zs = fma_mix_lo(p[2 * e], zz[e], zs);
           zs = fma_mix_hi(p[2 * e + 1], zz[e], zs);
-          // integer part of w plus the balanced-digit offset (the XOR follows the transpose)
-          x[2 * e] = (uint32_t)(int)fma_mix_lo(pw[2 * e], ss[e], 0.0f) + 0x80808080u;
-          x[2 * e + 1] = (uint32_t)(int)fma_mix_hi(pw[2 * e + 1], ss[e], 0.0f) + 0x80808080u;
+          // 2^23 + x in the float's bits: x in bytes 0..2 (byte 2 < 128)
+          x[2 * e] = __builtin_bit_cast(uint32_t, fma_mix_lo(pw[2 * e], ss[e], kTwo23));
+          x[2 * e + 1] = __builtin_bit_cast(uint32_t, fma_mix_hi(pw[2 * e + 1], ss[e], kTwo23));
         }
         zacc[t][g] = zs;
-        uint32_t d0[4], d1[4];
-        transpose4(x, d0);
-        transpose4(x + 4, d1);
+        uint32_t d0[3], d1[3];
+        transpose3(x, d0);
+        transpose3(x + 4, d1);
+        // digit rows 0, 1 as int8 u - 128 (the ones row 3 restores the offset); row 2 as is
         uint8_t* row = W + ((t * NGV + g) * 16 + 4 * qb) * kWS + 8 * oct;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          *reinterpret_cast<uint2*>(row + d * kWS) = make_uint2(d0[d] ^ 0x80808080u, d1[d] ^ 0x80808080u);
+        *reinterpret_cast<uint2*>(row) = make_uint2(d0[0] ^ 0x80808080u, d1[0] ^ 0x80808080u);
+        *reinterpret_cast<uint2*>(row + kWS) = make_uint2(d0[1] ^ 0x80808080u, d1[1] ^ 0x80808080u);
+        *reinterpret_cast<uint2*>(row + 2 * kWS) = make_uint2(d0[2], d1[2]);
       }
     }
     if (__any(rescale)) {
@@ -805,7 +834,6 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     __syncthreads();  // the w digits are in LDS
 
     // ---- p.V: tile v = 16 channels of one value group; rows (head, digit), K = 64 keys
-    const float inv_sv = pow2i(-sv_e);
 #pragma unroll
     for (int v = 0; v < NTV; ++v) {
       // MW = 16: tile (block mb, field u) = channels 16 mb + u d/4 + n;
@@ -844,7 +872,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         v4i c = v4i{0, 0, 0, 0};
         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, Bv[0], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, Bv[1], c, 0, 0, 0);
-        acc[t][v] = __builtin_fmaf(combine4(c), inv_sv * fw, acc[t][v]);
+        acc[t][v] = __builtin_fmaf(combine_pv(c), pow2i(-sh[t]) * fw, acc[t][v]);
       }
     }
     __syncthreads();  // T, W and Sl are rewritten by the next page

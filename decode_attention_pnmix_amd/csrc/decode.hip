@@ -49,6 +49,7 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kN = 128;  // page and residual length
 constexpr int kMaxSplits = 256;  // split-K partitions per (sequence, KV head): one merge thread each
+constexpr int kMergeSplits = 136;  // the planner's cap: beyond it the merge costs more than it saves
 constexpr int kWS = kN + 16;     // row stride of the p.V digit table (rows on distinct banks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTwo23 = 8388608.0f;  // y + 2^23 rounds y in [0, 2^23) to an integer (RNE)
@@ -452,6 +453,17 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   const int lane = threadIdx.x;
   const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
   const int ng = a.n_g;
+  // the queries do not depend on the cache lengths: issue their loads first
+  // LSB prep units: unit u = lane + 64k -> head hu = u / JL (0..NH-1), channels 4 (u % JL) + 0..3
+  uint2 qq[UK];
+#pragma unroll
+  for (int k = 0; k < UK; ++k) {
+    const int u = lane + 64 * k;
+    const int hu = u / JL, j = u % JL;
+    const bool ok = u < NT * D && hu < ng;
+    qq[k] = ok ? *reinterpret_cast<const uint2*>(a.q + ((int64_t)b * a.H_q + (int64_t)h * ng + hu) * D + 4 * j)
+               : make_uint2(0u, 0u);
+  }
   const pnmix_seq_len L = a.lens[b];
   const int n_pages = min(max(L.n_pages, 0), a.max_pages);
   const int64_t pbase = (bh * a.splits + split) * ng;
@@ -469,13 +481,14 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 
   // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NT][NGV][16][kWS] bytes;
   // key scales of the page [KG][D] fp16; bias [KG][NH] f32; salient channel of each rank [D]
-  // int16; head maxima [NH] f32.
+  // int16; head maxima [NH] f32; scaled queries [NH][D] f32.
   uint8_t* T = lds;
   uint8_t* W = lds + a.lds_T;
   uint16_t* Sl = reinterpret_cast<uint16_t*>(W + NT * NGV * 16 * kWS);
   float* biasl = reinterpret_cast<float*>(Sl + 4 * D);
   int16_t* sal = reinterpret_cast<int16_t*>(biasl + 4 * NH);
   float* qm = reinterpret_cast<float*>(sal + D);
+  float* qs = qm + NH;
 
   // ---- once per split: clear the digit table, salient ranks, scaled queries
   for (int i = lane * 16; i < a.lds_T; i += 64 * 16) *reinterpret_cast<v4u*>(T + i) = v4u{0, 0, 0, 0};
@@ -492,22 +505,18 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     const int r = salient_rank(mrow, c, D, a.pairing, a.n_hi);
     if (r >= 0) sal[r] = (int16_t)c;
   }
-  // LSB prep units: unit u = lane + 64k -> head hu = u / JL (0..NH-1), channels 4 (u % JL) + 0..3
   float qv[UK][4];
   float qmaxu[UK];
 #pragma unroll
   for (int k = 0; k < UK; ++k) {
     const int u = lane + 64 * k;
-    const int hu = u / JL, j = u % JL;
-    const bool ok = u < NT * D && hu < ng;
-    uint2 qq = make_uint2(0u, 0u);
-    if (ok) qq = *reinterpret_cast<const uint2*>(a.q + ((int64_t)b * a.H_q + (int64_t)h * ng + hu) * D + 4 * j);
-    qv[k][0] = f16lo(qq.x) * a.qscale;
-    qv[k][1] = f16hi(qq.x) * a.qscale;
-    qv[k][2] = f16lo(qq.y) * a.qscale;
-    qv[k][3] = f16hi(qq.y) * a.qscale;
+    qv[k][0] = f16lo(qq[k].x) * a.qscale;
+    qv[k][1] = f16hi(qq[k].x) * a.qscale;
+    qv[k][2] = f16lo(qq[k].y) * a.qscale;
+    qv[k][3] = f16hi(qq[k].y) * a.qscale;
     float mx = fmaxf(fmaxf(fabsf(qv[k][0]), fabsf(qv[k][1])), fmaxf(fabsf(qv[k][2]), fabsf(qv[k][3])));
     qmaxu[k] = group_max<(JL < 64 ? JL : 64)>(mx);
+    if (u < NT * D) *reinterpret_cast<v4f*>(qs + 4 * u) = v4f{qv[k][0], qv[k][1], qv[k][2], qv[k][3]};
   }
 #pragma unroll
   for (int k = 0; k < UK; ++k) {
@@ -535,9 +544,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       const int r = 4 * jr + i;
       const int cs = (ok && r < n_sal) ? sal[r] : -1;
       hc[k][i] = (cs >= 0 && cs < D) ? cs : -1;  // a mask outside the contract stays in range
-      hq[k][i] = hc[k][i] >= 0 ? (float)__builtin_bit_cast(_Float16,
-                     a.q[((int64_t)b * a.H_q + (int64_t)h * ng + hu) * D + hc[k][i]]) * a.qscale
-                               : 0.0f;
+      hq[k][i] = hc[k][i] >= 0 ? qs[hu * D + hc[k][i]] : 0.0f;
     }
   }
 
@@ -998,7 +1005,8 @@ static size_t lds_T_bytes(const pnmix_cfg& c) {
 static size_t lds_bytes(const pnmix_cfg& c) {
   const int NT = n_tiles(c);
   const size_t W = (size_t)NT * (c.d / c.g_V) * 16 * kWS;
-  return lds_T_bytes(c) + W + 4 * c.d * 2 + 4 * 4 * NT * 4 + c.d * 2 + 4 * NT * 4;
+  return lds_T_bytes(c) + W + 4 * c.d * 2 + 4 * 4 * NT * 4 + c.d * 2 + 4 * NT * 4 +
+         (size_t)4 * NT * c.d * 4;
 }
 
 static size_t lds_fp16_bytes(const pnmix_cfg& c) {
@@ -1076,15 +1084,16 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   const int n16 = items >= 128 ? 1 : (c.N_s + c.N + 63) / 64;
   const int bpc = dispatch(c, BlocksPerCu{p.lds_bytes});
   const long long resident = (long long)bpc * device_cus();
-  // page splits: fewest rounds of resident waves x pages per wave (+1 for the set-up)
+  // page splits: fewest rounds of resident waves x pages per wave (+1 for the set-up); ties go
+  // to more splits, up to kMergeSplits in all (the merge reads every split of a head)
   int ps = 0;
   if (max_pages > 0) {
     long long best = -1;
-    const int ps_max = std::min(max_pages, kMaxSplits - n16);
+    const int ps_max = std::min(max_pages, kMergeSplits - n16);
     for (int s = 1; s <= ps_max; ++s) {
       const long long rounds = (items * (s + n16) + resident - 1) / resident;
       const long long cost = rounds * ((max_pages + s - 1) / s + 1);
-      if (best < 0 || cost < best) {
+      if (best < 0 || cost <= best) {
         best = cost;
         ps = s;
       }

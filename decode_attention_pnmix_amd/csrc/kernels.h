@@ -19,7 +19,7 @@ hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* 
                              hipStream_t stream);
 
 struct DecodePlan {
-  int splits;           // split-K partitions per (sequence, KV head): page splits + fp16 chunks
+  int splits;           // split-K partitions per (sequence, KV head): page + fp16 splits
   int page_splits;      // partitions over the packed pages
   int pages_per_split;  // most pages of one page partition (a sequence's pages are split evenly)
   size_t ws_bytes;      // workspace for the partials

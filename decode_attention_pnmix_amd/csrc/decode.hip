@@ -505,18 +505,16 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     const int r = salient_rank(mrow, c, D, a.pairing, a.n_hi);
     if (r >= 0) sal[r] = (int16_t)c;
   }
-  float qv[UK][4];
+  // scaled queries go to LDS (qs) and are read back per page; the registers keep only the
+  // per-unit head maxima
   float qmaxu[UK];
 #pragma unroll
   for (int k = 0; k < UK; ++k) {
     const int u = lane + 64 * k;
-    qv[k][0] = f16lo(qq[k].x) * a.qscale;
-    qv[k][1] = f16hi(qq[k].x) * a.qscale;
-    qv[k][2] = f16lo(qq[k].y) * a.qscale;
-    qv[k][3] = f16hi(qq[k].y) * a.qscale;
-    float mx = fmaxf(fmaxf(fabsf(qv[k][0]), fabsf(qv[k][1])), fmaxf(fabsf(qv[k][2]), fabsf(qv[k][3])));
+    const v4f q4 = v4f{f16lo(qq[k].x), f16hi(qq[k].x), f16lo(qq[k].y), f16hi(qq[k].y)} * a.qscale;
+    float mx = fmaxf(fmaxf(fabsf(q4[0]), fabsf(q4[1])), fmaxf(fabsf(q4[2]), fabsf(q4[3])));
     qmaxu[k] = group_max<(JL < 64 ? JL : 64)>(mx);
-    if (u < NT * D) *reinterpret_cast<v4f*>(qs + 4 * u) = v4f{qv[k][0], qv[k][1], qv[k][2], qv[k][3]};
+    if (u < NT * D) *reinterpret_cast<v4f*>(qs + 4 * u) = q4;
   }
 #pragma unroll
   for (int k = 0; k < UK; ++k) {
@@ -528,24 +526,14 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   float qmaxC[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) qmaxC[t] = qm[4 * t + lane / 16];
-  // upper-bit prep units: uh = lane + 64k -> head uh / JH, ranks 4 (uh % JH) + 0..3
+  // upper-bit prep units: uh = lane + 64k -> head uh / JH, ranks 4 (uh % JH) + 0..3; their
+  // channels (sal) and queries (qs) are read from LDS per page
   constexpr int UKH = (NT * 4 * (D / 4) + 63) / 64;
-  int hc[UKH][4];
-  float hq[UKH][4];
   float hqmax[UKH];
 #pragma unroll
   for (int k = 0; k < UKH; ++k) {
     const int uh = lane + 64 * k;
-    const int hu = JH ? uh / JH : 0, jr = JH ? uh % JH : 0;
-    const bool ok = JH && uh < NH * JH && hu < ng;
-    hqmax[k] = (JH && uh < NH * JH) ? qm[hu] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * jr + i;
-      const int cs = (ok && r < n_sal) ? sal[r] : -1;
-      hc[k][i] = (cs >= 0 && cs < D) ? cs : -1;  // a mask outside the contract stays in range
-      hq[k][i] = hc[k][i] >= 0 ? qs[hu * D + hc[k][i]] : 0.0f;
-    }
+    hqmax[k] = (JH && uh < NH * JH) ? qm[uh / JH] : 0.0f;
   }
 
   // running softmax state of head 4t + lane/16; p.V accumulators per 16-channel tile (C
@@ -578,7 +566,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // 2 oct, 2 oct + 1) and the scales of its prep units.  The next page's are loaded into them as
   // soon as the current page's q.K is done, so their latency hides behind softmax and p.V.
   v4u wL[KL], wH0[KHM], wH1[KHM];
-  uint2 sv[UK][KG], zv[UK][KG];  // [k][kg] 4 fp16 of S and Z for the unit's channels
+  // 4 fp16 of S and Z per key group for this lane's channels 4 j .. 4 j + 3, j = lane % JL
+  // (the same channels for every prep unit of the lane: 64 is a multiple of JL)
+  uint2 sv[KG], zv[KG];
   const rsrc_t krs = buf_rsrc(a.k_pages + page_base * a.kpb, (int64_t)a.max_pages * a.kpb);
   const rsrc_t vrs = buf_rsrc(a.v_pages + page_base * a.vpb, (int64_t)a.max_pages * a.vpb);
   auto load_k = [&](int pgk) {
@@ -601,17 +591,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       }
     }
 #pragma unroll
-    for (int k = 0; k < UK; ++k) {
-      const int u = lane + 64 * k;
-      const int j = u % JL;
-#pragma unroll
-      for (int kg = 0; kg < KG; ++kg) {
-        sv[k][kg] = zv[k][kg] = make_uint2(0u, 0u);
-        if (u < NT * D) {
-          sv[k][kg] = bload8(krs, sOff + 2 * (kg * D + 4 * j), so);
-          zv[k][kg] = bload8(krs, zOff + 2 * (kg * D + 4 * j), so);
-        }
-      }
+    for (int kg = 0; kg < KG; ++kg) {
+      sv[kg] = bload8(krs, sOff + 2 * (kg * D + 4 * (lane % JL)), so);
+      zv[kg] = bload8(krs, zOff + 2 * (kg * D + 4 * (lane % JL)), so);
     }
   };
   load_k(p0);
@@ -641,14 +623,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     // ---- key scales: page maximum -> per-head fixed-point exponent
     uint32_t smax = 0u;
 #pragma unroll
-    for (int k = 0; k < UK; ++k) {
-      const int u = lane + 64 * k;
-      const int j = u % JL;
-#pragma unroll
-      for (int kg = 0; kg < KG; ++kg) {
-        smax = pk_max_u16(smax, pk_max_u16(sv[k][kg].x, sv[k][kg].y));
-        if (u < JL) *reinterpret_cast<uint2*>(Sl + kg * D + 4 * j) = sv[k][kg];
-      }
+    for (int kg = 0; kg < KG; ++kg) {
+      smax = pk_max_u16(smax, pk_max_u16(sv[kg].x, sv[kg].y));
+      if (lane < JL) *reinterpret_cast<uint2*>(Sl + kg * D + 4 * lane) = sv[kg];
     }
     smax = wave_max_u32(max(smax & 0xFFFFu, smax >> 16));
     const float Smax = (float)__builtin_bit_cast(_Float16, (uint16_t)smax);
@@ -667,16 +644,17 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       const int hu = u / JL, j = u % JL;
       const bool ok = u < NT * D;
       const float sc = pow2i(sigma_of(qmaxu[k]));
+      const v4f qv = ok ? *reinterpret_cast<const v4f*>(qs + 4 * u) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
-        const float s4[4] = {f16lo(sv[k][kg].x), f16hi(sv[k][kg].x), f16lo(sv[k][kg].y), f16hi(sv[k][kg].y)};
-        const float z4[4] = {f16lo(zv[k][kg].x), f16hi(zv[k][kg].x), f16lo(zv[k][kg].y), f16hi(zv[k][kg].y)};
+        const float s4[4] = {f16lo(sv[kg].x), f16hi(sv[kg].x), f16lo(sv[kg].y), f16hi(sv[kg].y)};
+        const float z4[4] = {f16lo(zv[kg].x), f16hi(zv[kg].x), f16lo(zv[kg].y), f16hi(zv[kg].y)};
         uint32_t y[4], dg[4];
         float bz = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          y[i] = digits4((int)((qv[k][i] * sc) * s4[i]));
-          bz = __builtin_fmaf(qv[k][i], z4[i], bz);
+          y[i] = digits4((int)((qv[i] * sc) * s4[i]));
+          bz = __builtin_fmaf(qv[i], z4[i], bz);
         }
         transpose4(y, dg);
         bz = group_sum<(JL < 64 ? JL : 64)>(bz);
@@ -699,13 +677,21 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       const int hu = uh / JH, jr = uh % JH;
       const float sc = pow2i(sigma_of(hqmax[k]));
       const int t = hu / 4, hl = hu % 4;
+      int hc[4];
+      float hq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int cs = sal[4 * jr + i];  // -1 past n_sal
+        hc[i] = cs;
+        hq[i] = cs >= 0 ? qs[hu * D + cs] : 0.0f;
+      }
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
         uint32_t y[4], dg[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float s = hc[k][i] >= 0 ? (float)__builtin_bit_cast(_Float16, Sl[kg * D + hc[k][i]]) : 0.0f;
-          y[i] = digits4((int)((hq[k][i] * sc) * s));
+          const float s = hc[i] >= 0 ? (float)__builtin_bit_cast(_Float16, Sl[kg * D + hc[i]]) : 0.0f;
+          y[i] = digits4((int)((hq[i] * sc) * s));
         }
         transpose4(y, dg);
         uint8_t* row = T + ((kg * NT + t) * 16 + 4 * hl) * TL + 64 * KL + 4 * jr;
@@ -965,9 +951,11 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
 
 // One launch per decode call: blockIdx.x < page_splits walks packed pages, the remaining
 // splits take one 64-token chunk each of the fp16 sink and residual rows, concurrently.
-// One head tile fits two waves per SIMD (256 registers); ask the compiler to stay there.
+// Two waves per SIMD (at most 256 registers) where the compiler fits them without spills:
+// one head tile with at most two key groups, or two head tiles at d <= 64.
 template <int D, int NT, int KG, int KH>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 && KG == 1 ? 2 : 1)))
+__global__ void __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu((NT == 1 && KG <= 2) || (D <= 64 && NT == 2 && KG == 1) ? 2 : 1)))
 decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int split = blockIdx.x;

@@ -449,6 +449,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   constexpr int NTV = D / 16;              // p.V column tiles of 16 channels
   constexpr int MW = D / 4 >= 16 ? 16 : 8; // value-byte columns per tile
   constexpr int NMB = (D / 4) / MW;        // value-byte column blocks
+  constexpr bool kLate = NT >= 2;          // value loads after q.K, key prefetch after p.V
 
   const int lane = threadIdx.x;
   const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
@@ -606,19 +607,22 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     // this lane's q.K keys (8 oct + b) per group; code bytes of its tile columns per K-step
     v4u sS[4], zZ[4];
     v4u cv[NMB][2];
+    auto load_v = [&]() {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // groups past NGV repeat the last one: the page maximum is unchanged and the
-      // per-group loops stop at NGV
-      const int gc = min(g, NGV - 1);
-      sS[g] = bload16(vrs, vS + 2 * gc * kN, vso);
-      zZ[g] = bload16(vrs, vS + 2 * (NGV + gc) * kN, vso);
-    }
+      for (int g = 0; g < 4; ++g) {
+        // groups past NGV repeat the last one: the page maximum is unchanged and the
+        // per-group loops stop at NGV
+        const int gc = min(g, NGV - 1);
+        sS[g] = bload16(vrs, vS + 2 * gc * kN, vso);
+        zZ[g] = bload16(vrs, vS + 2 * (NGV + gc) * kN, vso);
+      }
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        cv[mb][ks] = bload16(vrs, (mb * MW + vcol) * kN + 64 * ks + 16 * qb, vso);
+        for (int ks = 0; ks < 2; ++ks)
+          cv[mb][ks] = bload16(vrs, (mb * MW + vcol) * kN + 64 * ks + 16 * qb, vso);
+    };
+    if constexpr (!kLate) load_v();
 
     // ---- key scales: page maximum -> per-head fixed-point exponent
     uint32_t smax = 0u;
@@ -751,8 +755,13 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     PNMIX_QK_TILE(4) PNMIX_QK_TILE(5) PNMIX_QK_TILE(6) PNMIX_QK_TILE(7)
 #undef PNMIX_QK_TILE
 
-    // ---- the key side of this page is consumed: fetch the next page's
-    if (pg + 1 < p1) load_k(pg + 1);
+    // ---- the key side of this page is consumed: fetch the next page's (with several head
+    // tiles: fetch the value side now and the next keys after p.V, to keep fewer registers live)
+    if constexpr (kLate) {
+      load_v();
+    } else {
+      if (pg + 1 < p1) load_k(pg + 1);
+    }
 
     // ---- p.V fixed point, per head: x = rne(p S 2^sh) with 2^sh above the head's largest
     // p on this page times the page's largest value scale, so 0 <= x < 2^23 (23 bits relative
@@ -868,6 +877,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         acc[t][v] = __builtin_fmaf(combine_pv(c), pow2i(-sh[t]) * fw, acc[t][v]);
       }
     }
+    if constexpr (kLate) {
+      if (pg + 1 < p1) load_k(pg + 1);
+    }
     __syncthreads();  // T, W and Sl are rewritten by the next page
   }
 
@@ -952,10 +964,11 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
 // One launch per decode call: blockIdx.x < page_splits walks packed pages, the remaining
 // splits take one 64-token chunk each of the fp16 sink and residual rows, concurrently.
 // Two waves per SIMD (at most 256 registers) where the compiler fits them without spills:
-// one head tile with at most two key groups, or two head tiles at d <= 64.
+// one head tile with at most two key groups, or two head tiles with one key group (and one
+// upper-bit K-step at d = 128).
 template <int D, int NT, int KG, int KH>
 __global__ void __launch_bounds__(64)
-__attribute__((amdgpu_waves_per_eu((NT == 1 && KG <= 2) || (D <= 64 && NT == 2 && KG == 1) ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu((NT == 1 && KG <= 2) || (NT == 2 && KG == 1 && (D <= 64 || KH == 1)) ? 2 : 1)))
 decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int split = blockIdx.x;

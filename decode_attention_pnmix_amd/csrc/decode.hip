@@ -70,8 +70,12 @@ struct DecodeArgs {
   float qscale;    // sm_scale * log2(e)
   int H_q, H_kv, n_g, pairing, n_hi, n_sal, G, KG, g_V, NGV, N_s, max_pages, words;
   int64_t kpb, vpb;
-  int splits, page_splits;
+  int splits;      // partials per (sequence, KV head): workgroups of the split kernel
+  int page_splits; // page splits per (sequence, KV head), then n16 fp16-row splits
+  int n16;
+  int nw;          // waves per workgroup, one split each
   int lds_T;       // bytes of the q.K digit table (KG * NT * 16 rows * TL)
+  int lds_wave;    // LDS bytes of one wave's slice
 };
 
 template <int D, int KH>
@@ -293,6 +297,29 @@ __device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t voff, uint32_t soff) 
   const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
   return make_uint2(v[0], v[1]);
 }
+// 16 bytes at any offset, in two steps so that no wait sits between them: the five aligned
+// dwords that cover them (bload20) and, where the bytes are consumed, the byte shift (align20)
+struct Raw20 {
+  uint32_t d[5];
+};
+__device__ __forceinline__ Raw20 bload20(rsrc_t r, uint32_t voff, uint32_t soff) {
+  Raw20 x;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) x.d[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (voff & ~3u) + 4 * i, soff, 0);
+  return x;
+}
+__device__ __forceinline__ v4u align20(const Raw20& x, uint32_t voff) {
+  const uint32_t sh = voff & 3u;
+  return v4u{__builtin_amdgcn_alignbyte(x.d[1], x.d[0], sh), __builtin_amdgcn_alignbyte(x.d[2], x.d[1], sh),
+             __builtin_amdgcn_alignbyte(x.d[3], x.d[2], sh), __builtin_amdgcn_alignbyte(x.d[4], x.d[3], sh)};
+}
+// Wave-uniform data that the kernel never writes (cache lengths, pair mask), read through the
+// constant address space so that it arrives by scalar loads, which a wait for vector loads
+// does not cover.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* kconst(const T* p) {
+  return (const __attribute__((address_space(4))) T*)p;
+}
 // 16 bytes at a 2-byte-aligned offset: five aligned dwords and a byte shift
 __device__ __forceinline__ v4u bload16_a2(rsrc_t r, uint32_t voff, uint32_t soff) {
   const uint32_t a = voff & ~3u, sh = voff & 3u;
@@ -307,141 +334,234 @@ __device__ __forceinline__ v4u bload16_a2(rsrc_t r, uint32_t voff, uint32_t soff
 
 // ------------------------------------------------------------------------- partial writers
 
-template <int D>
-__device__ void write_empty_partial(const DecodeArgs& a, int64_t pbase) {
-  for (int i = threadIdx.x; i < a.n_g * D; i += 64) a.part_o[pbase * D + i] = 0.0f;
-  if ((int)threadIdx.x < a.n_g) {
-    a.part_ml[(pbase + threadIdx.x) * 2 + 0] = -INFINITY;
-    a.part_ml[(pbase + threadIdx.x) * 2 + 1] = 0.0f;
+// LDS hand-off between the lanes of one wave.  Every wave owns its slice of LDS and the LDS unit
+// executes one wave's instructions in order, so waiting for the wave's own LDS operations plus a
+// compiler barrier orders them; no workgroup barrier is involved, and the waves of a workgroup
+// run their splits independently.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
+  __asm__ volatile("" ::: "memory");
+}
+
+// Where a split leaves its partial: o [n_g][d] and (m, l) [n_g][2], in the workspace (one wave
+// per workgroup) or in the wave's LDS slice for the workgroup's own merge.  Both are stored
+// through typed pointers (global or LDS instructions): a store through a generic pointer is a
+// FLAT instruction, and one in flight on any path makes the compiler wait for every load in
+// flight at the next use of a loaded value.
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) v4f lds_v4f;
+struct PartOut {
+  float* go;    // workspace o and (m, l), or
+  float* gml;
+  lds_f32* lo;  // the LDS slice's o and (m, l) when in_lds
+  lds_f32* lml;
+  bool in_lds;
+  __device__ __forceinline__ void o(int i, float v) const {
+    if (in_lds) lo[i] = v; else go[i] = v;
   }
+  __device__ __forceinline__ void o4(int i, const v4f& v) const {
+    if (in_lds) *reinterpret_cast<lds_v4f*>(lo + i) = v;
+    else *reinterpret_cast<v4f*>(go + i) = v;
+  }
+  __device__ __forceinline__ void ml(int hh, float m, float l) const {
+    if (in_lds) {
+      lml[2 * hh] = m;
+      lml[2 * hh + 1] = l;
+    } else {
+      gml[2 * hh] = m;
+      gml[2 * hh + 1] = l;
+    }
+  }
+};
+
+template <int D>
+__device__ void write_empty_partial(const DecodeArgs& a, const PartOut& po) {
+  const int lane = threadIdx.x & 63;
+  for (int i = lane; i < a.n_g * D; i += 64) po.o(i, 0.0f);
+  if (lane < a.n_g) po.ml(lane, -INFINITY, 0.0f);
 }
 
 // -------------------------------------------------------------- fp16 sink + residual split
 
 // One wave over the 64-token chunks chunk, chunk + n_chunk_splits, ... of the fp16 rows (token
-// order: sinks, then residual rows).  Every load of a chunk is issued at once: each lane's key row (one token per lane for the
-// logits) and the chunk's value rows, staged in LDS with coalesced 16-byte loads (one channel
-// pair per lane for p.V).  Logits go through LDS one head at a time to keep registers low.
-template <int D, int NT>
-__device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, int64_t pbase,
+// order: sinks, then residual rows), 32 tokens at a time on the fp16 matrix cores
+// (v_mfma_f32_16x16x32_f16, exact fp16 products, fp32 sums):
+// * logits transposed, S^T[token][head] = K q^T: the A operand is the key rows as loaded (16
+//   bytes of one token per lane), the B operand the queries (head = lane column);
+// * lane (g, n) of the S^T result holds head n for tokens 4g + r and 16 + 4g + r, r < 4.  With
+//   the 32 tokens of the reduction numbered in that order, this is the B operand of
+//   O^T = V^T P^T, so p never leaves its lane; it enters as fp16 hi + lo (two MFMAs, ~22 bits);
+// * V^T comes from LDS: 16-byte loads of 4 value rows are transposed with byte permutes into
+//   [channel][token] rows;
+// * every softmax quantity of head n lives in the lanes of column n: the maximum is taken over
+//   the lane's 8 tokens, then over the four lane groups.
+template <int D>
+__device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, const PartOut& po,
                             int sink_len, int res_len, int chunk, int n_chunk_splits,
                             uint8_t* lds) {
-  constexpr int NH = 4 * NT;
-  const int lane = threadIdx.x;
+  constexpr int KS = D / 32;         // 32-channel K-steps of S^T
+  constexpr int CT = D / 16;         // 16-channel tiles of O^T
+  constexpr int VS = 36;             // V^T row stride in halves: 32 tokens + 4 (bank spread)
+  constexpr int OC = D / 8;          // 8-channel pieces of a row
+  constexpr int VU = (8 * OC + 63) / 64;  // (4 tokens x 8 channels) staging units per lane
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
   const int ng = a.n_g;
-  uint32_t* q2 = reinterpret_cast<uint32_t*>(lds);                  // [NH][D/2] fp16 pairs
-  float* pb = reinterpret_cast<float*>(lds + NH * D * 2);           // [64][NH] logits, then p
-  uint16_t* vst = reinterpret_cast<uint16_t*>(pb + 64 * NH);        // [64][D] value rows
-  for (int i = lane; i < NH * D / 2; i += 64) {
-    const int hh = i / (D / 2), c2 = i % (D / 2);
-    q2[i] = hh < ng ? *reinterpret_cast<const uint32_t*>(
-                          a.q + ((int64_t)b * a.H_q + (int64_t)h * ng + hh) * D + 2 * c2)
-                    : 0u;
-  }
-  __syncthreads();
-  float m[NH], l[NH], acc[NH][2];
-#pragma unroll
-  for (int i = 0; i < NH; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.0f;
-    acc[i][0] = acc[i][1] = 0.0f;
-  }
+  uint16_t* vT = reinterpret_cast<uint16_t*>(lds);  // [D][VS]
   const int T16 = sink_len + res_len;
-  if (64 * chunk >= T16) {
-    write_empty_partial<D>(a, pbase);
-    return;
-  }
-  const uint16_t* ks = a.k_sink + bh * a.N_s * D;
-  const uint16_t* vs = a.v_sink + bh * a.N_s * D;
-  const uint16_t* kr = a.k_res + bh * kN * D;
-  const uint16_t* vr = a.v_res + bh * kN * D;
-  const bool chan = 2 * lane < D;
-  constexpr int PER = D / 8;  // 16-byte pieces per row
-  for (int c0 = 64 * chunk; c0 < T16; c0 += 64 * n_chunk_splits) {
-    const int nt = min(64, T16 - c0);
-    // value rows of the chunk: piece i of the chunk is row i / PER, part i % PER
-    v4u vpc[PER];
+  // No branches around loads (a wait would sit in each): the queries come by buffer loads
+  // (heads past n_g read as zero), and a token past the fp16 rows reads the last row instead,
+  // whose logit is then masked to -inf and whose p is 0 (finite values times 0).
+  const rsrc_t qrs = buf_rsrc(a.q + ((int64_t)b * a.H_q + (int64_t)h * ng) * D, (int64_t)ng * D * 2);
+  v4u qv[KS];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = lane + 64 * j;
-      const int tr = i / PER, part = i % PER;
-      const int t = c0 + tr;
-      const uint16_t* vrow = t < sink_len ? vs + (int64_t)t * D : vr + (int64_t)(t - sink_len) * D;
-      vpc[j] = tr < nt ? *reinterpret_cast<const v4u*>(vrow + 8 * part) : v4u{0, 0, 0, 0};
+  for (int ks = 0; ks < KS; ++ks) qv[ks] = bload16(qrs, (uint32_t)(2 * (n * D + 32 * ks + 8 * g)), 0u);
+  const uint16_t* k_s = a.k_sink + bh * a.N_s * D;
+  const uint16_t* v_s = a.v_sink + bh * a.N_s * D;
+  const uint16_t* k_r = a.k_res + bh * kN * D - (int64_t)sink_len * D;  // row t >= sink_len
+  const uint16_t* v_r = a.v_res + bh * kN * D - (int64_t)sink_len * D;
+  auto krow = [&](int t) { t = min(t, T16 - 1); return (t < sink_len ? k_s : k_r) + (int64_t)t * D; };
+  auto vrow = [&](int t) { t = min(t, T16 - 1); return (t < sink_len ? v_s : v_r) + (int64_t)t * D; };
+  float m = -INFINITY, l = 0.0f;  // l: this lane's tokens only, summed over lane groups at the end
+  v4f acc[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // 32-token pieces of this split's chunks; the loads of the next piece are issued before the
+  // current one is computed
+  auto s0_of = [&](int k) { return 64 * (chunk + (k >> 1) * n_chunk_splits) + 32 * (k & 1); };
+  auto load_piece = [&](int s0, v4u (&ka)[2][KS], v4u (&vr)[VU][4]) {
+    // key rows (A of S^T): tile tt holds tokens s0 + 16 tt + n, channels 32 ks + 8 g ...
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint16_t* row = krow(s0 + 16 * tt + n);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[tt][ks] = *reinterpret_cast<const v4u*>(row + 32 * ks + 8 * g);
     }
-    const int tok = c0 + lane;
-    const bool valid = lane < nt;
-    v4u krow[PER];
-    {
-      const uint16_t* row = tok < sink_len ? ks + (int64_t)tok * D : kr + (int64_t)(tok - sink_len) * D;
+    // value rows: unit u = tokens s0 + 4 (u / OC) + 0..3, channels 8 (u % OC) + 0..7
 #pragma unroll
-      for (int c8 = 0; c8 < PER; ++c8)
-        krow[c8] = valid ? *reinterpret_cast<const v4u*>(row + 8 * c8) : v4u{0, 0, 0, 0};
+    for (int j = 0; j < VU; ++j) {
+      const int u = lane + 64 * j;
+      const int tq = u / OC, oc = u % OC;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // (lanes past the units read a valid row; it is not stored)
+        vr[j][i] = *reinterpret_cast<const v4u*>(vrow(s0 + 4 * tq + i) + 8 * (oc % OC));
     }
+  };
+  // one 32-token piece: S^T, V^T to LDS, online softmax, O^T += V^T P^T
+  auto piece = [&](int s0, const v4u (&ka)[2][KS], const v4u (&vr)[VU][4]) {
+    v4f st[2];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) *reinterpret_cast<v4u*>(vst + 8 * (lane + 64 * j)) = vpc[j];
-#pragma unroll 1
-    for (int i = 0; i < NH; ++i) {
-      float sacc = 0.0f;
+    for (int tt = 0; tt < 2; ++tt) {
+      st[tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c8 = 0; c8 < PER; ++c8) {
-        const v4u qv = *reinterpret_cast<const v4u*>(q2 + i * (D / 2) + 4 * c8);
+      for (int ks = 0; ks < KS; ++ks)
+        st[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, ka[tt][ks]),
+                                                        __builtin_bit_cast(v8h, qv[ks]), st[tt], 0, 0, 0);
+    }
+    // V^T: channel 8 oc + c, tokens 4 tq .. 4 tq + 3 as one 8-byte row piece
+#pragma unroll
+    for (int j = 0; j < VU; ++j) {
+      const int u = lane + 64 * j;
+      if (u < 8 * OC) {
+        const int tq = u / OC, oc = u % OC;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sacc = __builtin_fmaf(f16lo(qv[e]), f16lo(krow[c8][e]), sacc);
-          sacc = __builtin_fmaf(f16hi(qv[e]), f16hi(krow[c8][e]), sacc);
+          const uint32_t w0 = vr[j][0][e], w1 = vr[j][1][e], w2 = vr[j][2][e], w3 = vr[j][3][e];
+          *reinterpret_cast<uint2*>(vT + (8 * oc + 2 * e) * VS + 4 * tq) =
+              make_uint2(__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u));
+          *reinterpret_cast<uint2*>(vT + (8 * oc + 2 * e + 1) * VS + 4 * tq) =
+              make_uint2(__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u));
         }
       }
-      pb[lane * NH + i] = valid ? sacc * a.qscale : -INFINITY;
     }
-    float alpha[NH];
+    // online softmax of head n over the 32 tokens (log2 units)
+    float sv[8];
+    float cm = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NH; ++i) {
-      const float lgi = pb[lane * NH + i];
-      const float cm = group_max<64>(lgi);
-      const float mn = fmaxf(m[i], cm);
-      alpha[i] = __builtin_amdgcn_exp2f(m[i] - mn);
-      m[i] = mn;
-      pb[lane * NH + i] = valid ? __builtin_amdgcn_exp2f(lgi - mn) : 0.0f;
+    for (int i = 0; i < 8; ++i) {
+      const int t = s0 + 16 * (i >> 2) + 4 * g + (i & 3);
+      sv[i] = t < T16 ? st[i >> 2][i & 3] * a.qscale : -INFINITY;
+      cm = fmaxf(cm, sv[i]);
     }
-    __syncthreads();  // p and the value rows are in LDS
+    cm = fmaxf(cm, __shfl_xor(cm, 16));
+    cm = fmaxf(cm, __shfl_xor(cm, 32));  // finite: token s0 is valid
+    const float mn = fmaxf(m, cm);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    float p[8], ps = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NH; ++i) {
-      acc[i][0] *= alpha[i];
-      acc[i][1] *= alpha[i];
-      l[i] *= alpha[i];
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(sv[i] - mn);
+      ps += p[i];
     }
-    for (int tt = 0; tt < nt; ++tt) {
-      const uint32_t vv = chan ? *reinterpret_cast<const uint32_t*>(vst + tt * D + 2 * lane) : 0u;
-      const float v0 = f16lo(vv), v1 = f16hi(vv);
+    l = l * alpha + ps;
 #pragma unroll
-      for (int i = 0; i < NH; ++i) {
-        const float p = pb[tt * NH + i];
-        acc[i][0] = __builtin_fmaf(p, v0, acc[i][0]);
-        acc[i][1] = __builtin_fmaf(p, v1, acc[i][1]);
-        l[i] += p;
-      }
+    for (int ct = 0; ct < CT; ++ct) acc[ct] *= alpha;
+    v4u phi, plo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      phi[e] = pk_rne(p[2 * e], p[2 * e + 1]);
+      plo[e] = pk_rne(p[2 * e] - f16lo(phi[e]), p[2 * e + 1] - f16hi(phi[e]));
     }
-    __syncthreads();  // LDS is reused by the next chunk
+    wave_sync();  // V^T is in LDS
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const uint16_t* vrow = vT + (16 * ct + n) * VS;
+      const uint2 x0 = *reinterpret_cast<const uint2*>(vrow + 4 * g);
+      const uint2 x1 = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
+      const v8h va = __builtin_bit_cast(v8h, v4u{x0.x, x0.y, x1.x, x1.y});
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, __builtin_bit_cast(v8h, phi), acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, __builtin_bit_cast(v8h, plo), acc[ct], 0, 0, 0);
+    }
+    wave_sync();  // V^T is rewritten by the next 32 tokens
+  };
+  // two register sets, each loaded one piece ahead of its use (no copies between them)
+  v4u ka0[2][KS], vr0[VU][4], ka1[2][KS], vr1[VU][4];
+  if (s0_of(0) < T16) {
+    load_piece(s0_of(0), ka0, vr0);
+    // (the next piece is loaded unconditionally, rows clamped to the last one: no load sits
+    // under a branch)
+    for (int k = 0;; k += 2) {
+      load_piece(s0_of(k + 1), ka1, vr1);
+      piece(s0_of(k), ka0, vr0);
+      if (s0_of(k + 1) >= T16) break;
+      load_piece(s0_of(k + 2), ka0, vr0);
+      piece(s0_of(k + 1), ka1, vr1);
+      if (s0_of(k + 2) >= T16) break;
+    }
   }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (n < ng) {
+    // O^T: lane (g, n) holds channels 16 ct + 4 g + r of head n
 #pragma unroll
-  for (int i = 0; i < NH; ++i) {
-    if (i >= ng) break;
-    if (chan) {
-      a.part_o[(pbase + i) * D + 2 * lane] = acc[i][0];
-      a.part_o[(pbase + i) * D + 2 * lane + 1] = acc[i][1];
-    }
-    if (lane == 0) {
-      a.part_ml[(pbase + i) * 2 + 0] = m[i];
-      a.part_ml[(pbase + i) * 2 + 1] = l[i];
-    }
+    for (int ct = 0; ct < CT; ++ct)
+      po.o4(n * D + 16 * ct + 4 * g, acc[ct]);
+    if (g == 0) po.ml(n, m, l);
   }
 }
 
 // ----------------------------------------------------------------------------- page split
 
+// Rank of channel c among the salient channels (-1 if not salient) from the first two words of
+// the pair mask held in registers (d <= 128: at most 64 pairs).  Same ranking as the packer:
+// ascending pair index; adjacent pairs interleave their two channels, half-split pairs list the
+// first halves, then the second halves.
+__device__ __forceinline__ int salient_rank2(uint32_t w0, uint32_t w1, int c, int d, int pairing,
+                                             int n_hi) {
+  const int p = pair_of_channel(c, d, pairing);
+  const uint64_t mk = (uint64_t)w0 | ((uint64_t)w1 << 32);
+  if (!((mk >> p) & 1u)) return -1;
+  const int below = __popcll(mk & ((1ull << p) - 1ull));
+  const int r = pairing == PNMIX_PAIRS_ADJACENT ? 2 * below + (c & 1)
+                                                : (c < d / 2 ? below : n_hi + below);
+  return r < 2 * n_hi ? r : -1;
+}
+
 template <int D, int NT, int KG, int KH>
-__device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t bh) {
+__device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t bh,
+                           const PartOut& po) {
   using S_ = Shape<D, KH>;
   constexpr int KL = S_::KL, KHM = S_::KHM, TL = S_::TL, JL = S_::JL;
   constexpr int NH = 4 * NT;
@@ -451,33 +571,101 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   constexpr int NMB = (D / 4) / MW;        // value-byte column blocks
   constexpr bool kLate = NT >= 2;          // value loads after q.K, key prefetch after p.V
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
   const int ng = a.n_g;
-  // the queries do not depend on the cache lengths: issue their loads first
+  const int G = a.G, n_sal = a.n_sal, NGV = a.NGV;
+  // The queries and the first page do not depend on the cache lengths: their loads go first,
+  // the queries ahead of the page (a wait for them must not wait for the page).
   // LSB prep units: unit u = lane + 64k -> head hu = u / JL (0..NH-1), channels 4 (u % JL) + 0..3
+  // (buffer loads: heads past the group's n_g read as zero, with no branch to wait in)
+  const rsrc_t qrs = buf_rsrc(a.q + ((int64_t)b * a.H_q + (int64_t)h * ng) * D, (int64_t)ng * D * 2);
   uint2 qq[UK];
 #pragma unroll
   for (int k = 0; k < UK; ++k) {
     const int u = lane + 64 * k;
-    const int hu = u / JL, j = u % JL;
-    const bool ok = u < NT * D && hu < ng;
-    qq[k] = ok ? *reinterpret_cast<const uint2*>(a.q + ((int64_t)b * a.H_q + (int64_t)h * ng + hu) * D + 4 * j)
-               : make_uint2(0u, 0u);
+    qq[k] = bload8(qrs, (uint32_t)(2 * 4 * u), 0u);  // head u / JL, channels 4 (u % JL) + 0..3
   }
-  const pnmix_seq_len L = a.lens[b];
-  const int n_pages = min(max(L.n_pages, 0), a.max_pages);
-  const int64_t pbase = (bh * a.splits + split) * ng;
+  const int oct = lane & 15;  // octet of the q.K B operand (keys 8 oct + b)
+  const int qb = lane >> 4;   // K block (16 channels / 8 keys) of this lane
+  const int kg_lane = (8 * oct) / G;  // key group of this lane's keys
+  const int64_t page_base = bh * a.max_pages;
+  const int sOff = kN * D / 8 + kN * n_sal / 4;      // K page: S after lo and hi planes
+  const int zOff = sOff + 2 * KG * D;
+  // p.V: this lane's value-byte column within a tile block, and (for 8-column tiles) the
+  // shift that brings its field pair to bits 0-1 / 4-5
+  const int vcol = lane & (MW - 1);
+  const int vsh = MW == 16 ? 0 : 2 * ((lane & 15) >> 3);
 
-  // this sequence's pages split evenly over the page splits (sizes differ by at most one)
-  const int p0 = (int)((int64_t)split * n_pages / a.page_splits);
-  const int p1 = (int)((int64_t)(split + 1) * n_pages / a.page_splits);
-  if (p0 >= p1) {
-    write_empty_partial<D>(a, pbase);
-    return;
-  }
+  // Key side of one page in registers: this lane's packed codes (LSB rows and upper-bit rows
+  // 2 oct, 2 oct + 1) and the scales of its prep units.  The next page's are loaded into them as
+  // soon as the current page's q.K is done, so their latency hides behind softmax and p.V.
+  v4u wL[KL];
+  Raw20 hr0[KHM], hr1[KHM];  // upper-bit rows as loaded (any byte alignment)
+  // 4 fp16 of S and Z per key group for this lane's channels 4 j .. 4 j + 3, j = lane % JL
+  // (the same channels for every prep unit of the lane: 64 is a multiple of JL)
+  uint2 sv[KG], zv[KG];
+  const rsrc_t krs = buf_rsrc(a.k_pages + page_base * a.kpb, (int64_t)a.max_pages * a.kpb);
+  const rsrc_t vrs = buf_rsrc(a.v_pages + page_base * a.vpb, (int64_t)a.max_pages * a.vpb);
+  // The next page's loads are issued whether or not there is a next page, through a resource
+  // of zero bytes when there is none (every lane reads zero, nothing is fetched): a load under
+  // a branch would make the compiler wait, on the path that issued it, for everything in flight
+  // wherever an older load's data is used after the branch rejoins.
+  const rsrc_t nul = buf_rsrc(a.k_pages, 0);
+  auto load_k = [&](int pgk, rsrc_t krs) {
+    const uint32_t so = (uint32_t)(pgk * a.kpb);
+#pragma unroll
+    for (int ks = 0; ks < KL; ++ks) {
+      const int c0 = 64 * ks + 16 * qb;
+      wL[ks] = c0 < D ? bload16(krs, oct * D + c0, so) : v4u{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KHM; ++ks) {
+      // ranks past n_sal read other bytes of the page: their A columns are zero
+      const uint32_t h0 = kN * D / 8 + 64 * ks + 16 * qb + (2 * oct) * n_sal;
+      hr0[ks] = bload20(krs, h0, so);
+      hr1[ks] = bload20(krs, h0 + n_sal, so);
+    }
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) {
+      sv[kg] = bload8(krs, sOff + 2 * (kg * D + 4 * (lane % JL)), so);
+      zv[kg] = bload8(krs, zOff + 2 * (kg * D + 4 * (lane % JL)), so);
+    }
+  };
+  // Value side of one page: scales and offsets of this lane's q.K keys (8 oct + b) per group;
+  // code bytes of its p.V tile columns per K-step.
+  const uint32_t vS = kN * D / 4 + 2 * 8 * oct;  // S [NGV][N] fp16 after the codes, then Z
+  v4u sS[4], zZ[4];
+  v4u cv[NMB][2];
+  auto load_v = [&](int pgv, rsrc_t vrs) {
+    const uint32_t vso = (uint32_t)(pgv * a.vpb);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // groups past NGV repeat the last one: the page maximum is unchanged and the per-group
+      // loops stop at NGV
+      const int gc = min(g, NGV - 1);
+      sS[g] = bload16(vrs, vS + 2 * gc * kN, vso);
+      zZ[g] = bload16(vrs, vS + 2 * (NGV + gc) * kN, vso);
+    }
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        cv[mb][ks] = bload16(vrs, (mb * MW + vcol) * kN + 64 * ks + 16 * qb, vso);
+  };
+  // Pages of this split: split, split + page_splits, ...  (a split past the last page drops
+  // the loads of its first one)
+  const int step = a.page_splits, p0 = split;
+  load_k(p0, krs);
+  if constexpr (!kLate) load_v(p0, vrs);
 
-  const int G = a.G, n_sal = a.n_sal, NGV = a.NGV;
+  const auto mrow = kconst(a.mask + bh * a.words);
+  const uint32_t mw0 = mrow[0], mw1 = a.words > 1 ? mrow[1] : 0u;
+  const int n_pages = min(max(kconst(&a.lens[b].n_pages)[0], 0), a.max_pages);
+  // A split past the last page runs its set-up and no page: its partial is m = -inf, l = 0,
+  // o = 0.  (No early exit: a branch that stores its partial early would force waits for all
+  // loads in flight at the point where it rejoins.)
+
   const int JH = (n_sal + 3) / 4;  // 4-rank units per head of the upper-bit part
 
   // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NT][NGV][16][kWS] bytes;
@@ -499,11 +687,10 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     *reinterpret_cast<v4u*>(W + (4 * r + 3) * kWS + 16 * c16) =
         v4u{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
   }
-  const uint32_t* mrow = a.mask + bh * a.words;
   for (int c = lane; c < D; c += 64) sal[c] = -1;
-  __syncthreads();
+  wave_sync();
   for (int c = lane; c < D; c += 64) {
-    const int r = salient_rank(mrow, c, D, a.pairing, a.n_hi);
+    const int r = salient_rank2(mw0, mw1, c, D, a.pairing, a.n_hi);
     if (r >= 0) sal[r] = (int16_t)c;
   }
   // scaled queries go to LDS (qs) and are read back per page; the registers keep only the
@@ -522,7 +709,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     const int u = lane + 64 * k;
     if (u < NT * D && (u % JL) == 0) qm[u / JL] = qmaxu[k];
   }
-  __syncthreads();
+  wave_sync();
   // max |qt| of the head this lane has in the q.K output (head 4t + lane/16)
   float qmaxC[NT];
 #pragma unroll
@@ -552,77 +739,8 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     for (int v = 0; v < NTV; ++v) acc[t][v] = 0.0f;
   }
 
-  const int oct = lane & 15;  // octet of the q.K B operand (keys 8 oct + b)
-  const int qb = lane >> 4;   // K block (16 channels / 8 keys) of this lane
-  const int kg_lane = (8 * oct) / G;  // key group of this lane's keys
-  const int64_t page_base = bh * a.max_pages;
-  const int sOff = kN * D / 8 + kN * n_sal / 4;      // K page: S after lo and hi planes
-  const int zOff = sOff + 2 * KG * D;
-  // p.V: this lane's value-byte column within a tile block, and (for 8-column tiles) the
-  // shift that brings its field pair to bits 0-1 / 4-5
-  const int vcol = lane & (MW - 1);
-  const int vsh = MW == 16 ? 0 : 2 * ((lane & 15) >> 3);
-
-  // Key side of one page in registers: this lane's packed codes (LSB rows and upper-bit rows
-  // 2 oct, 2 oct + 1) and the scales of its prep units.  The next page's are loaded into them as
-  // soon as the current page's q.K is done, so their latency hides behind softmax and p.V.
-  v4u wL[KL], wH0[KHM], wH1[KHM];
-  // 4 fp16 of S and Z per key group for this lane's channels 4 j .. 4 j + 3, j = lane % JL
-  // (the same channels for every prep unit of the lane: 64 is a multiple of JL)
-  uint2 sv[KG], zv[KG];
-  const rsrc_t krs = buf_rsrc(a.k_pages + page_base * a.kpb, (int64_t)a.max_pages * a.kpb);
-  const rsrc_t vrs = buf_rsrc(a.v_pages + page_base * a.vpb, (int64_t)a.max_pages * a.vpb);
-  auto load_k = [&](int pgk) {
-    const uint32_t so = (uint32_t)(pgk * a.kpb);
-#pragma unroll
-    for (int ks = 0; ks < KL; ++ks) {
-      const int c0 = 64 * ks + 16 * qb;
-      wL[ks] = c0 < D ? bload16(krs, oct * D + c0, so) : v4u{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int ks = 0; ks < KHM; ++ks) {
-      // ranks past n_sal read other bytes of the page: their A columns are zero
-      const uint32_t h0 = kN * D / 8 + 64 * ks + 16 * qb + (2 * oct) * n_sal;
-      if ((n_sal & 15) == 0) {
-        wH0[ks] = bload16(krs, h0, so);
-        wH1[ks] = bload16(krs, h0 + n_sal, so);
-      } else {
-        wH0[ks] = bload16_a2(krs, h0, so);
-        wH1[ks] = bload16_a2(krs, h0 + n_sal, so);
-      }
-    }
-#pragma unroll
-    for (int kg = 0; kg < KG; ++kg) {
-      sv[kg] = bload8(krs, sOff + 2 * (kg * D + 4 * (lane % JL)), so);
-      zv[kg] = bload8(krs, zOff + 2 * (kg * D + 4 * (lane % JL)), so);
-    }
-  };
-  load_k(p0);
-
-  for (int pg = p0; pg < p1; ++pg) {
-    const uint32_t vso = (uint32_t)(pg * a.vpb);
-    const uint32_t vS = kN * D / 4 + 2 * 8 * oct;  // S [NGV][N] fp16 after the codes, then Z
-
-    // ---- value side of this page, issued now, consumed after q.K: scales and offsets of
-    // this lane's q.K keys (8 oct + b) per group; code bytes of its tile columns per K-step
-    v4u sS[4], zZ[4];
-    v4u cv[NMB][2];
-    auto load_v = [&]() {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // groups past NGV repeat the last one: the page maximum is unchanged and the
-        // per-group loops stop at NGV
-        const int gc = min(g, NGV - 1);
-        sS[g] = bload16(vrs, vS + 2 * gc * kN, vso);
-        zZ[g] = bload16(vrs, vS + 2 * (NGV + gc) * kN, vso);
-      }
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          cv[mb][ks] = bload16(vrs, (mb * MW + vcol) * kN + 64 * ks + 16 * qb, vso);
-    };
-    if constexpr (!kLate) load_v();
+  for (int pg = p0; pg < n_pages; pg += step) {
+    const bool more = pg + step < n_pages;
 
     // ---- key scales: page maximum -> per-head fixed-point exponent
     uint32_t smax = 0u;
@@ -671,7 +789,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         }
       }
     }
-    __syncthreads();  // Sl and the LSB digits are in LDS
+    wave_sync();  // Sl and the LSB digits are in LDS
 
     // ---- digit table, upper-bit part: ranks of salient channels, code weight 2 is in sH
 #pragma unroll
@@ -703,7 +821,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         for (int d = 0; d < 4; ++d) *reinterpret_cast<uint32_t*>(row + d * TL) = dg[d];
       }
     }
-    __syncthreads();
+    wave_sync();
 
     // ---- A operands (digit rows) of every tile and key group
     v4i A[KG][NT][KL + KHM];
@@ -724,6 +842,13 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     }
 
     // ---- q.K: tile b holds keys 8 oct + b; the lane's q.K output head is 4t + qb
+    v4u wH0[KHM], wH1[KHM];
+#pragma unroll
+    for (int ks = 0; ks < KHM; ++ks) {
+      const uint32_t h0 = 64 * ks + 16 * qb + (2 * oct) * n_sal;  // alignment as loaded
+      wH0[ks] = align20(hr0[ks], h0);
+      wH1[ks] = align20(hr1[ks], h0 + n_sal);
+    }
     float lg[NT][8];
 #define PNMIX_QK_TILE(BB)                                                                      \
     {                                                                                          \
@@ -758,9 +883,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     // ---- the key side of this page is consumed: fetch the next page's (with several head
     // tiles: fetch the value side now and the next keys after p.V, to keep fewer registers live)
     if constexpr (kLate) {
-      load_v();
+      load_v(pg, vrs);
     } else {
-      if (pg + 1 < p1) load_k(pg + 1);
+      load_k(more ? pg + step : 0, more ? krs : nul);
     }
 
     // ---- p.V fixed point, per head: x = rne(p S 2^sh) with 2^sh above the head's largest
@@ -833,7 +958,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 #pragma unroll
         for (int v = 0; v < NTV; ++v) acc[t][v] *= alpha[t];
     }
-    __syncthreads();  // the w digits are in LDS
+    wave_sync();  // the w digits are in LDS
 
     // ---- p.V: tile v = 16 channels of one value group; rows (head, digit), K = 64 keys
 #pragma unroll
@@ -878,9 +1003,11 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       }
     }
     if constexpr (kLate) {
-      if (pg + 1 < p1) load_k(pg + 1);
+      load_k(more ? pg + step : 0, more ? krs : nul);
+    } else {
+      load_v(more ? pg + step : 0, more ? vrs : nul);
     }
-    __syncthreads();  // T, W and Sl are rewritten by the next page
+    wave_sync();  // T, W and Sl are rewritten by the next page (and by the partial)
   }
 
   // ---- partials of this split: head 4t + qb, channel of tile v for column lane % 16
@@ -899,11 +1026,10 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         const int c = (MW == 16 ? 16 * mb + fu * (D / 4) : 16 * v) + (lane & 15);
         const int gi = c / a.g_V;
         const float zsg = gi == 0 ? zs[0] : gi == 1 ? zs[1] : gi == 2 ? zs[2] : zs[3];
-        a.part_o[(pbase + hh) * D + c] = acc[t][v] + zsg;
+        po.o(hh * D + c, acc[t][v] + zsg);
       }
       if ((lane & 15) == 0) {
-        a.part_ml[(pbase + hh) * 2 + 0] = m_run[t];
-        a.part_ml[(pbase + hh) * 2 + 1] = lt;
+        po.ml(hh, m_run[t], lt);
       }
     }
   }
@@ -961,27 +1087,69 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   }
 }
 
-// One launch per decode call: blockIdx.x < page_splits walks packed pages, the remaining
-// splits take one 64-token chunk each of the fp16 sink and residual rows, concurrently.
+// Waves per workgroup the split kernel is compiled for: eight for the instantiations that run
+// two waves per SIMD, four (one per SIMD) otherwise.
+template <int D, int NT, int KG, int KH>
+struct KernelWaves {
+  static constexpr bool two = (NT == 1 && KG <= 2) || (NT == 2 && KG == 1 && (D <= 64 || KH == 1));
+  static constexpr int max_nw = two ? 8 : 4;
+};
+
+// One launch per decode call.  Wave w of workgroup x takes split x nw + w of its (sequence, KV
+// head): the first page_splits walk packed pages, the next ones take one 64-token chunk each of
+// the fp16 sink and residual rows, any further ones are empty.  With one wave per workgroup the
+// split writes its partial to the workspace; with nw > 1 the waves leave their partials in
+// their LDS slices and the workgroup merges them into one partial (same log-sum-exp rule as
+// the merge kernel), so the merge kernel reads nw times fewer.
 // Two waves per SIMD (at most 256 registers) where the compiler fits them without spills:
 // one head tile with at most two key groups, or two head tiles with one key group (and one
 // upper-bit K-step at d = 128).
 template <int D, int NT, int KG, int KH>
-__global__ void __launch_bounds__(64)
-__attribute__((amdgpu_waves_per_eu((NT == 1 && KG <= 2) || (NT == 2 && KG == 1 && (D <= 64 || KH == 1)) ? 2 : 1)))
+__global__ void __launch_bounds__((64 * KernelWaves<D, NT, KG, KH>::max_nw))
+__attribute__((amdgpu_waves_per_eu((KernelWaves<D, NT, KG, KH>::two ? 2 : 1))))
 decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int split = blockIdx.x;
+  const int nw = a.nw;
+  const int wv = nw > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
+  const int split = (int)blockIdx.x * nw + wv;
   const int64_t bh = blockIdx.y;
+  const int ng = a.n_g;
+  uint8_t* wl = lds + (size_t)wv * a.lds_wave;
+  const int64_t pbase = (bh * a.splits + split) * ng;  // nw == 1
+  lds_f32* const st = (lds_f32*)(wl);
+  const PartOut po{a.part_o + pbase * D, a.part_ml + pbase * 2, st, st + ng * D, nw > 1};
   if (split < a.page_splits) {
-    page_split<D, NT, KG, KH>(a, lds, split, bh);
-  } else {
+    page_split<D, NT, KG, KH>(a, wl, split, bh, po);
+  } else if (split < a.page_splits + a.n16) {
     const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
-    const pnmix_seq_len L = a.lens[b];
-    const int sink_len = min(max(L.sink_len, 0), a.N_s);
-    const int res_len = min(max(L.res_len, 0), kN);
-    fp16_region<D, NT>(a, b, h, bh, (bh * a.splits + split) * a.n_g, sink_len, res_len,
-                       split - a.page_splits, a.splits - a.page_splits, lds);
+    const int sink_len = min(max(kconst(&a.lens[b].sink_len)[0], 0), a.N_s);
+    const int res_len = min(max(kconst(&a.lens[b].res_len)[0], 0), kN);
+    fp16_region<D>(a, b, h, bh, po, sink_len, res_len, split - a.page_splits, a.n16, wl);
+  } else {
+    write_empty_partial<D>(a, po);
+  }
+  if (nw == 1) return;
+  __syncthreads();  // every wave's partial is in its LDS slice
+  const int64_t pb = (bh * a.splits + blockIdx.x) * ng;
+  const int nthr = 64 * nw;
+  for (int i = threadIdx.x; i < ng * (D + 1); i += nthr) {
+    const int hh = i < ng * D ? i / D : i - ng * D;
+    float M = -INFINITY;
+    for (int w = 0; w < nw; ++w)
+      M = fmaxf(M, reinterpret_cast<const float*>(lds + (size_t)w * a.lds_wave)[ng * D + 2 * hh]);
+    float r = 0.0f;
+    for (int w = 0; w < nw; ++w) {
+      const float* st = reinterpret_cast<const float*>(lds + (size_t)w * a.lds_wave);
+      const float mw = st[ng * D + 2 * hh];
+      const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      r = __builtin_fmaf(f, i < ng * D ? st[i] : st[ng * D + 2 * hh + 1], r);
+    }
+    if (i < ng * D) {
+      a.part_o[pb * D + i] = r;
+    } else {
+      a.part_ml[(pb + hh) * 2 + 0] = M;
+      a.part_ml[(pb + hh) * 2 + 1] = r;
+    }
   }
 }
 
@@ -1011,8 +1179,15 @@ static size_t lds_bytes(const pnmix_cfg& c) {
 }
 
 static size_t lds_fp16_bytes(const pnmix_cfg& c) {
-  const int NT = n_tiles(c);
-  return (size_t)4 * NT * c.d * 2 + 64 * 4 * NT * 4 + 64 * (size_t)c.d * 2;
+  return (size_t)c.d * 36 * 2;  // V^T [d][32 tokens + 4] halves
+}
+
+// LDS slice of one wave: the larger of the page and fp16 layouts, and at least the partial the
+// wave leaves there for its workgroup's merge
+static size_t lds_wave_bytes(const pnmix_cfg& c) {
+  const size_t ng = (size_t)(c.H_q / c.H_kv);
+  const size_t b = std::max(std::max(lds_bytes(c), lds_fp16_bytes(c)), ng * (c.d + 2) * 4);
+  return (b + 15) & ~(size_t)15;
 }
 
 // f.template run<D, NT, KG, KH>() for the split kernel instantiation of the configuration
@@ -1048,61 +1223,101 @@ static auto dispatch(const pnmix_cfg& c, const F& f) {
   }
 }
 
-// Waves of the split kernel that fit on the device at once: the runtime's occupancy for this
-// instantiation and LDS size, times the compute-unit count (defaults without a device).
-static int device_cus() {
-  static const int n = [] {
+// Device limits (defaults without a device): compute units, dynamic LDS per workgroup.
+static const hipDeviceProp_t* device_prop() {
+  static hipDeviceProp_t prop;
+  static const bool ok = [] {
     int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
-        prop.multiProcessorCount <= 0)
-      return 256;
-    return prop.multiProcessorCount;
+    return hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess;
   }();
-  return n;
+  return ok ? &prop : nullptr;
+}
+static int device_cus() {
+  const hipDeviceProp_t* p = device_prop();
+  return p && p->multiProcessorCount > 0 ? p->multiProcessorCount : 256;
+}
+static size_t device_lds_per_block() {
+  const hipDeviceProp_t* p = device_prop();
+  return p && p->sharedMemPerBlock > 0 ? p->sharedMemPerBlock : 65536;
 }
 
+struct MaxWaves {
+  template <int D, int NT, int KG, int KH>
+  int run() const {
+    return KernelWaves<D, NT, KG, KH>::max_nw;
+  }
+};
+
+// dynamic LDS above 64 KiB has to be allowed per kernel
+template <int D, int NT, int KG, int KH>
+static hipError_t allow_lds(size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, NT, KG, KH>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// Workgroups of the split kernel resident per compute unit (the runtime's occupancy for this
+// instantiation, block size and LDS size).
 struct BlocksPerCu {
   size_t lds;
+  int threads;
   template <int D, int NT, int KG, int KH>
   int run() const {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, NT, KG, KH>, 64, lds) !=
-            hipSuccess || n <= 0) {
+    if (allow_lds<D, NT, KG, KH>(lds) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, NT, KG, KH>, threads,
+                                                     lds) != hipSuccess ||
+        n <= 0) {
       (void)hipGetLastError();
-      return 8;
+      return std::max(1, 8 / (threads / 64));
     }
     return n;
   }
 };
 
+// Split plan.  Large batches (>= 128 (sequence, KV head) items): one wave per workgroup, one
+// fp16 split walking all 64-token chunks.  Small batches: workgroups of nw waves (as many as
+// the instantiation and the LDS allow) merge their waves' partials on chip, and the number of
+// fp16 splits is searched too.  Cost = rounds of resident workgroups x (pages per split + 1 for
+// the set-up), the fp16 splits' chunks counting half a page each; ties go to more page splits.
+// At most kMergeSplits partials per (sequence, KV head) (the merge reads every one).
 DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   DecodePlan p;
   const long long items = std::max<long long>((long long)B * c.H_kv, 1);
-  p.lds_bytes = std::max(lds_bytes(c), lds_fp16_bytes(c));
-  // fp16 rows: one split per 64-token chunk when the batch is small, else one split walking
-  // all chunks (its latency then hides among the page splits)
-  const int n16 = items >= 128 ? 1 : (c.N_s + c.N + 63) / 64;
-  const int bpc = dispatch(c, BlocksPerCu{p.lds_bytes});
-  const long long resident = (long long)bpc * device_cus();
-  // page splits: fewest rounds of resident waves x pages per wave (+1 for the set-up); ties go
-  // to more splits, up to kMergeSplits in all (the merge reads every split of a head)
-  int ps = 0;
+  p.lds_wave = lds_wave_bytes(c);
+  const int chunks = (c.N_s + c.N + 63) / 64;
+  int nw = 1;
+  if (items < 128) {
+    nw = dispatch(c, MaxWaves{});
+    while (nw > 1 && (size_t)nw * p.lds_wave > device_lds_per_block()) nw /= 2;
+  }
+  p.nw = nw;
+  p.lds_bytes = (size_t)nw * p.lds_wave;
+  const int bpc = dispatch(c, BlocksPerCu{p.lds_bytes, 64 * nw});
+  const long long resident = (long long)bpc * device_cus();  // workgroups
+  int ps = 0, n16 = nw == 1 ? (items >= 128 ? 1 : chunks) : 1;
   if (max_pages > 0) {
     long long best = -1;
-    const int ps_max = std::min(max_pages, kMergeSplits - n16);
-    for (int s = 1; s <= ps_max; ++s) {
-      const long long rounds = (items * (s + n16) + resident - 1) / resident;
-      const long long cost = rounds * ((max_pages + s - 1) / s + 1);
-      if (best < 0 || cost <= best) {
-        best = cost;
-        ps = s;
+    const int n16_lo = n16, n16_hi = nw == 1 ? n16 : chunks;
+    for (int f = n16_lo; f <= n16_hi; ++f) {
+      const int f16 = nw == 1 ? 0 : (chunks + f - 1) / f;  // half pages
+      const int ps_max = std::min(max_pages, kMergeSplits * nw - f);
+      for (int s = 1; s <= ps_max; ++s) {
+        const long long wg = (s + f + nw - 1) / nw;
+        const long long rounds = (items * wg + resident - 1) / resident;
+        const long long cost = rounds * (std::max<long long>(2LL * ((max_pages + s - 1) / s), f16) + 2);
+        if (best < 0 || cost < best || (cost == best && s > ps)) {
+          best = cost;
+          ps = s;
+          n16 = f;
+        }
       }
     }
   }
   p.page_splits = ps;
+  p.n16 = n16;
   p.pages_per_split = ps > 0 ? (max_pages + ps - 1) / ps : 0;
-  p.splits = ps + n16;
+  p.splits = (ps + n16 + nw - 1) / nw;
   const int ng = c.H_q / c.H_kv;
   const size_t per = (size_t)items * p.splits * ng;
   const size_t o_bytes = (per * c.d * sizeof(float) + 255) & ~(size_t)255;
@@ -1118,8 +1333,10 @@ struct Launch {
   hipStream_t stream;
   template <int D, int NT, int KG, int KH>
   hipError_t run() const {
-    hipLaunchKernelGGL((decode_kernel<D, NT, KG, KH>), dim3(p.splits, B * c.H_kv), dim3(64),
-                       p.lds_bytes, stream, a);
+    const hipError_t la = allow_lds<D, NT, KG, KH>(p.lds_bytes);
+    if (la != hipSuccess) return la;
+    hipLaunchKernelGGL((decode_kernel<D, NT, KG, KH>), dim3(p.splits, B * c.H_kv),
+                       dim3(64 * p.nw), p.lds_bytes, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(B * c.H_q), dim3(256), 0, stream, a);
@@ -1167,7 +1384,10 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
   a.vpb = (int64_t)pnmix_v_page_bytes(&c);
   a.splits = p.splits;
   a.page_splits = p.page_splits;
+  a.n16 = p.n16;
+  a.nw = p.nw;
   a.lds_T = (int)lds_T_bytes(c);
+  a.lds_wave = (int)p.lds_wave;
   return dispatch(c, Launch{p, B, c, a, stream});
 }
 

@@ -19,11 +19,14 @@ hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* 
                              hipStream_t stream);
 
 struct DecodePlan {
-  int splits;           // split-K partitions per (sequence, KV head): page + fp16 splits
-  int page_splits;      // partitions over the packed pages
-  int pages_per_split;  // most pages of one page partition (a sequence's pages are split evenly)
+  int splits;           // partials per (sequence, KV head): workgroups of the split kernel
+  int page_splits;      // waves over the packed pages, per (sequence, KV head)
+  int n16;              // waves over the fp16 sink and residual rows, per (sequence, KV head)
+  int nw;               // waves per workgroup (their partials are merged on chip)
+  int pages_per_split;  // most pages of one page wave (a sequence's pages are split evenly)
   size_t ws_bytes;      // workspace for the partials
-  size_t lds_bytes;     // dynamic LDS of the split kernel
+  size_t lds_wave;      // LDS slice of one wave
+  size_t lds_bytes;     // dynamic LDS of one workgroup
 };
 DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages);
 hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_t* q,

@@ -161,9 +161,9 @@ pnmix_status pnmix_decode_attn(const pnmix_cfg* c, int32_t B, int32_t max_pages,
     return fail(PNMIX_E_INVALID, "k_pages and v_pages must be non-NULL when max_pages > 0");
   if (!std::isfinite(sm_scale)) return fail(PNMIX_E_INVALID, "sm_scale is not finite");
   const pnmix::DecodePlan plan = pnmix::decode_plan(*c, B, max_pages);
-  if (plan.lds_bytes > 65536)
+  if (plan.lds_wave > 65536)
     return fail(PNMIX_E_UNSUPPORTED, "n_g = %d with G = %d needs %zu bytes of LDS (> 64 KiB)",
-                c->H_q / c->H_kv, c->G, plan.lds_bytes);
+                c->H_q / c->H_kv, c->G, plan.lds_wave);
   const size_t need = plan.ws_bytes;
   if (ws_bytes < need)
     return fail(PNMIX_E_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);

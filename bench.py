@@ -312,14 +312,19 @@ def main():
     torch.cuda.synchronize()
     lens_now = (caches[0].sink_len, caches[0].n_pages, caches[0].res_len)
     qlast = [inputs[l][0][W + K - 1] for l in range(layers)]
-    # the layers' calls run back to back between one pair of events (per-call event pairs
-    # would add the event overhead to every call); the first repetition is a warm-up
+    # the layers' calls are captured once in a HIP graph and replayed back to back between one
+    # pair of events on the launch stream, so host launch overhead stays out of the per-call
+    # time; the first replay is a warm-up
+    call_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(call_graph):
+        for layer, c in enumerate(caches):
+            c.attend(qlast[layer], outs[layer])
+    torch.cuda.synchronize()
     durs = []
     for rep in range(args.roofline_reps + 1):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for layer, c in enumerate(caches):
-            c.attend(qlast[layer], outs[layer])
+        call_graph.replay()
         e1.record()
         torch.cuda.synchronize()
         if rep:

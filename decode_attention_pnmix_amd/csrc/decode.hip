@@ -1037,53 +1037,68 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 
 // ----------------------------------------------------------------------------------- merge
 
-// Second launch: one workgroup of 256 per (sequence, query head).  m = max m_s,
-// l = sum 2^(m_s - m) l_s, o = sum 2^(m_s - m) o_s / l (log2 units).  Thread s < S reads the
-// (m, l) of split s; then thread (split lane sl, channel quad cq) sums the splits sl, sl + SL, ...
-// of four channels with every load of the walk independent, and the SL lane sums are added in
-// a fixed order.
+// Second launch: one workgroup of 256 per (sequence, query head).  out = sum_s 2^(m_s - m) o_s /
+// sum_s 2^(m_s - m) l_s with m = max_s m_s (log2 units).  Thread (split lane sl, channel quad cq)
+// loads (m, l, o) of its splits sl, sl + SL, ... in one round (up to kMergeChunk at a time) and
+// folds them in ascending order with the online rule (m, l, o) <- (m', l 2^(m - m') +
+// l_s 2^(m_s - m'), same for o), m' = max(m, m_s); the SL lane results are folded the same way,
+// in ascending sl, through LDS.  A sequence with no tokens (every m_s = -inf) gets out = 0.
+constexpr int kMergeChunk = 8;
+struct MergeAcc {
+  float m, l;
+  v4f o;
+  __device__ __forceinline__ void fold(float ms, float ls, const v4f& os) {
+    if (ms == -INFINITY) return;  // an empty split
+    const float mn = fmaxf(m, ms);
+    const float a = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    const float w = __builtin_amdgcn_exp2f(ms - mn);
+    l = __builtin_fmaf(w, ls, l * a);
+    o = o * a + w * os;
+    m = mn;
+  }
+};
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   constexpr int Q = D / 4, SL = 256 / Q;
-  __shared__ float wts[256];
-  __shared__ float red[2][4];
-  __shared__ v4f psum[256];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ v4f red_o[256];
+  __shared__ float red_m[256], red_l[256];
+  const int tid = threadIdx.x;
   const int bhq = blockIdx.x;  // b * H_q + hq
   const int b = bhq / a.H_q, hq = bhq % a.H_q;
   const int ng = a.n_g, S = a.splits;
   const int h = hq / ng, hh = hq % ng;
   const int64_t bh = (int64_t)b * a.H_kv + h;
-  float m = -INFINITY, l = 0.0f;
-  if (tid < S) {
-    const int64_t pi = (bh * S + tid) * ng + hh;
-    m = a.part_ml[pi * 2];
-    l = a.part_ml[pi * 2 + 1];
-  }
-  float M = group_max<64>(m);
-  if (lane == 0) red[0][wv] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  const float w = (tid < S && m != -INFINITY && M != -INFINITY) ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
-  const float Lw = group_sum<64>(w * l);
-  if (lane == 0) red[1][wv] = Lw;
-  wts[tid] = w;
-  __syncthreads();
-  const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
   const int cq = tid % Q, sl = tid / Q;
-  v4f o = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  const float* po = a.part_o + (bh * S * ng + hh) * D + 4 * cq;
-#pragma unroll 8
-  for (int s = sl; s < S; s += SL)
-    o += wts[s] * *reinterpret_cast<const v4f*>(po + (int64_t)s * ng * D);
-  psum[tid] = o;
+  // partial r = (split s, head hh) of this (sequence, KV head); loads past the last split read
+  // zero (buffer bounds) and are not folded
+  const rsrc_t mlr = buf_rsrc(a.part_ml + bh * S * ng * 2, (int64_t)S * ng * 2 * 4);
+  const rsrc_t por = buf_rsrc(a.part_o + bh * S * ng * D, (int64_t)S * ng * D * 4);
+  MergeAcc acc{-INFINITY, 0.0f, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int s0 = sl; s0 < S; s0 += kMergeChunk * SL) {
+    v4u ob[kMergeChunk];
+    uint32_t mb[kMergeChunk], lb[kMergeChunk];
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      const int r = (s0 + j * SL) * ng + hh;
+      ob[j] = bload16(por, (uint32_t)(4 * (r * D + 4 * cq)), 0u);
+      mb[j] = __builtin_amdgcn_raw_buffer_load_b32(mlr, (uint32_t)(8 * r), 0u, 0);
+      lb[j] = __builtin_amdgcn_raw_buffer_load_b32(mlr, (uint32_t)(8 * r + 4), 0u, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j)
+      if (s0 + j * SL < S)
+        acc.fold(__builtin_bit_cast(float, mb[j]), __builtin_bit_cast(float, lb[j]),
+                 __builtin_bit_cast(v4f, ob[j]));
+  }
+  red_o[tid] = acc.o;
+  red_m[tid] = acc.m;
+  red_l[tid] = acc.l;
   __syncthreads();
   if (tid < Q) {
-    v4f r = psum[tid];
-#pragma unroll
-    for (int i = 1; i < SL; ++i) r += psum[i * Q + tid];
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    *reinterpret_cast<v4f*>(a.out + (int64_t)bhq * D + 4 * tid) = r * inv;
+#pragma unroll 4
+    for (int g = 1; g < SL; ++g) acc.fold(red_m[g * Q + tid], red_l[g * Q + tid], red_o[g * Q + tid]);
+    const float inv = acc.l > 0.0f ? 1.0f / acc.l : 0.0f;
+    *reinterpret_cast<v4f*>(a.out + (int64_t)bhq * D + 4 * tid) = acc.o * inv;
   }
 }
 

@@ -91,11 +91,14 @@ struct Shape {
 
 // ---------------------------------------------------------------------------- small helpers
 
-// lanes outside the pattern keep their own value (bound_ctrl off, full row and bank masks)
+// Lane permutations inside a 16-lane row.  Every pattern used here (quad_perm, row_ror,
+// row_half_mirror) reads a valid lane for every lane, so bound_ctrl never applies; setting it
+// lets the compiler fold the move into the consuming add or integer max (one instruction per
+// step).
 template <int CTRL>
 __device__ __forceinline__ float dpp_c(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-      __builtin_bit_cast(int, x), __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, true));
 }
 // all-reduce over the 16 lanes of a row (lanes 16r .. 16r+15)
 __device__ __forceinline__ float row_max16(float x) {
@@ -114,7 +117,7 @@ __device__ __forceinline__ float row_sum16(float x) {
 }
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
 }
 // Across the four 16-lane rows: the row results are read into scalar registers (v_readlane)
 // and combined there, with no LDS round trip.  rowv(x, r) = x of row r (x uniform per row).

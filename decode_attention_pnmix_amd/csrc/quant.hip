@@ -113,6 +113,23 @@ __device__ __forceinline__ uint32_t code_bits(float x, float mn, float inv, floa
   const float y = (x - mn) * inv;
   return __float_as_uint(__builtin_amdgcn_fmed3f(y, 0.0f, L) + kRound);
 }
+// f16(low or high half of w) - mn in one v_fma_mix_f32 (w widened exactly, times 1, plus -mn:
+// the single rounding of the fp32 subtraction), then the rest of code_bits.
+__device__ __forceinline__ float sub_lo(uint32_t w, float nmn) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(nmn));
+  return r;
+}
+__device__ __forceinline__ float sub_hi(uint32_t w, float nmn) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(nmn));
+  return r;
+}
+__device__ __forceinline__ uint32_t code_bits_h(uint32_t w, bool high, float nmn, float inv,
+                                                float L) {
+  const float y = (high ? sub_hi(w, nmn) : sub_lo(w, nmn)) * inv;
+  return __float_as_uint(__builtin_amdgcn_fmed3f(y, 0.0f, L) + kRound);
+}
 
 template <int D>
 __global__ void __launch_bounds__(2 * D) quantize_k_kernel(const pnmix_page* __restrict__ jobs,
@@ -201,8 +218,7 @@ __global__ void __launch_bounds__(2 * D) quantize_k_kernel(const pnmix_page* __r
     uint32_t u[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t w = word(x[j], m);
-      u[j] = code_bits((s & 1) ? hi_f(w) : lo_f(w), mt[s].x, mt[s].y, L);
+      u[j] = code_bits_h(word(x[j], m), (s & 1) != 0, -mt[s].x, mt[s].y, L);
     }
     // nibbles of tokens 0-3 and 4-7 in the low 16 bits (float exponent bits land >= bit 24)
     uint32_t wl = u[3], wh = u[7];
@@ -292,17 +308,41 @@ __global__ void __launch_bounds__(2 * D) quantize_v_kernel(const pnmix_page* __r
   float2 mt[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) mt[e] = meta[(8 * k + e) * 4 + gi];
+  if constexpr (D == 128) {
+    // The four threads of a byte column (same k, u = 0..3) are lanes 4 apart in one 16-lane row:
+    // two DPP rotations of the row OR their fields in registers, and lane u then writes the
+    // column bytes of i = 2u, 2u + 1 with plain LDS stores (no atomics).
+    uint2 mine[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t cu[8];
+    for (int i = 0; i < 8; ++i) {
+      uint32_t cu[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w = word(x[e], i >> 1);
-      cu[e] = code_bits((i & 1) ? hi_f(w) : lo_f(w), mt[e].x, mt[e].y, 3.0f);
+      for (int e = 0; e < 8; ++e) {
+        cu[e] = code_bits_h(word(x[e], i >> 1), (i & 1) != 0, -mt[e].x, mt[e].y, 3.0f);
+      }
+      uint32_t w0 = gather_b0(cu[0], cu[1], cu[2], cu[3]) << (2 * u);
+      uint32_t w1 = gather_b0(cu[4], cu[5], cu[6], cu[7]) << (2 * u);
+      w0 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w0, 0x124, 0xF, 0xF, true);  // row_ror:4
+      w1 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w1, 0x124, 0xF, 0xF, true);
+      w0 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w0, 0x128, 0xF, 0xF, true);  // row_ror:8
+      w1 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w1, 0x128, 0xF, 0xF, true);
+      if ((i >> 1) == u) mine[i & 1] = make_uint2(w0, w1);
     }
-    uint32_t* dst = cw + ((j0 + i) * kN + 8 * k) / 4;
-    atomicOr(dst, gather_b0(cu[0], cu[1], cu[2], cu[3]) << (2 * u));
-    atomicOr(dst + 1, gather_b0(cu[4], cu[5], cu[6], cu[7]) << (2 * u));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<uint2*>(cw + ((j0 + 2 * u + h) * kN + 8 * k) / 4) = mine[h];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t cu[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cu[e] = code_bits_h(word(x[e], i >> 1), (i & 1) != 0, -mt[e].x, mt[e].y, 3.0f);
+      }
+      uint32_t* dst = cw + ((j0 + i) * kN + 8 * k) / 4;
+      atomicOr(dst, gather_b0(cu[0], cu[1], cu[2], cu[3]) << (2 * u));
+      atomicOr(dst + 1, gather_b0(cu[4], cu[5], cu[6], cu[7]) << (2 * u));
+    }
   }
   __syncthreads();
   reinterpret_cast<uint4*>(codes)[tid] = reinterpret_cast<const uint4*>(cw)[tid];

@@ -572,7 +572,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   constexpr int NTV = D / 16;              // p.V column tiles of 16 channels
   constexpr int MW = D / 4 >= 16 ? 16 : 8; // value-byte columns per tile
   constexpr int NMB = (D / 4) / MW;        // value-byte column blocks
-  constexpr bool kLate = NT >= 2;          // value loads after q.K, key prefetch after p.V
+  // value loads after q.K and key prefetch after p.V, only where prefetching both sides a page
+  // ahead would spill (the 8-head tiles with one or two key groups fit it in registers)
+  constexpr bool kLate = NT >= 4 || (NT == 2 && KG >= 4);
 
   const int lane = threadIdx.x & 63;
   const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);

@@ -148,8 +148,13 @@ def cpu_baseline(w, sample, seconds, threads):
                     N_s=w.N_s, N=w.N)
     sm = float(np.float32(1.0 / math.sqrt(w.d)))
     prepared = []
+    t_score = t_quant = 0.0
+    score_bytes = quant_bytes = 0
     for (qp_b, k_b, v_b, qd_b, T) in sample:
+        t0 = time.perf_counter()
         _, _, _, mask = oracle.score_prefill(oc, qp_b, k_b[:, :w.P])
+        t_score += time.perf_counter() - t0
+        score_bytes += (w.H_q + w.H_kv) * w.P * w.d * 2
         s = min(T, w.N_s)
         n_pages = (T - s) // w.N
         kp = np.zeros((w.H_kv, max(n_pages, 1), oracle.k_page_bytes(oc)), np.uint8)
@@ -161,7 +166,11 @@ def cpu_baseline(w, sample, seconds, threads):
             kp[h, p] = oracle.quantize_k_page(oc, k_b[h, s + p * w.N:s + (p + 1) * w.N], mask[h])
             vp[h, p] = oracle.quantize_v_page(oc, v_b[h, s + p * w.N:s + (p + 1) * w.N])
 
+        t0 = time.perf_counter()
         oracle.parallel_map(qj, jobs, threads)
+        t_quant += time.perf_counter() - t0
+        quant_bytes += len(jobs) * (2 * w.N * w.d * 2 + oracle.k_page_bytes(oc) +
+                                    oracle.v_page_bytes(oc))
         a = s + n_pages * w.N
         ks = np.zeros((w.H_kv, w.N_s, w.d), np.uint16)
         vs = np.zeros_like(ks)
@@ -184,11 +193,21 @@ def cpu_baseline(w, sample, seconds, threads):
     t0 = time.perf_counter()
     work = sum(oracle.parallel_map(run, range(n_items), threads))
     el = time.perf_counter() - t0
+    n_pg = quant_bytes // (2 * w.N * w.d * 2 + oracle.k_page_bytes(oc) + oracle.v_page_bytes(oc))
     return {"value": work / el, "unit": "KV token-heads/s", "cores": threads, "kind": "oracle",
             "sample": (f"float64 decode attention (the oracle's dequantize-then-softmax) of "
                        f"{n_items} sequence-layers drawn from {len(prepared)} sampled sequences "
                        f"(T={sample[0][4]}, {w.H_kv} KV heads, {w.H_q} query heads), "
-                       f"{el:.1f} s wall on {threads} threads; page quantization excluded")}
+                       f"{el:.1f} s wall on {threads} threads; page quantization and prefill "
+                       f"score timed separately below"),
+            "page_quant": {"value": quant_bytes / max(t_quant, 1e-9) / 1e9, "unit": "GB/s",
+                           "cores": threads, "kind": "oracle",
+                           "sample": f"{n_pg} K+V page pairs of the sampled sequences, "
+                                     f"{t_quant:.2f} s wall"},
+            "prefill_score": {"value": score_bytes / max(t_score, 1e-9) / 1e9, "unit": "GB/s",
+                              "cores": 1, "kind": "oracle",
+                              "sample": f"P={w.P} prompt, {len(prepared)} sequence(s), "
+                                        f"{t_score:.3f} s wall (single-threaded)"}}
 
 
 def main():

@@ -671,17 +671,12 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // o = 0.  (No early exit: a branch that stores its partial early would force waits for all
   // loads in flight at the point where it rejoins.)
 
-  const int JH = (n_sal + 3) / 4;  // 4-rank units per head of the upper-bit part
-
   // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NT][NGV][16][kWS] bytes;
-  // key scales of the page [KG][D] fp16; bias [KG][NH] f32; salient channel of each rank [D]
-  // int16; head maxima [NH] f32; scaled queries [NH][D] f32.
+  // bias [KG][NH] f32; head maxima [NH] f32; scaled queries [NH][D] f32.
   uint8_t* T = lds;
   uint8_t* W = lds + a.lds_T;
-  uint16_t* Sl = reinterpret_cast<uint16_t*>(W + NT * NGV * 16 * kWS);
-  float* biasl = reinterpret_cast<float*>(Sl + 4 * D);
-  int16_t* sal = reinterpret_cast<int16_t*>(biasl + 4 * NH);
-  float* qm = reinterpret_cast<float*>(sal + D);
+  float* biasl = reinterpret_cast<float*>(W + NT * NGV * 16 * kWS);
+  float* qm = biasl + 4 * NH;
   float* qs = qm + NH;
 
   // ---- once per split: clear the digit table, salient ranks, scaled queries
@@ -692,11 +687,25 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     *reinterpret_cast<v4u*>(W + (4 * r + 3) * kWS + 16 * c16) =
         v4u{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
   }
-  for (int c = lane; c < D; c += 64) sal[c] = -1;
-  wave_sync();
-  for (int c = lane; c < D; c += 64) {
-    const int r = salient_rank2(mw0, mw1, c, D, a.pairing, a.n_hi);
-    if (r >= 0) sal[r] = (int16_t)c;
+  // Upper-bit digit rows: the digits of a salient channel are the same words as its LSB digits
+  // (same qt S product), placed at the channel's salient rank.  Each LSB prep unit scatters the
+  // digit bytes of its salient channels there; hoff[k] holds, for the unit's 4 channels, the
+  // byte offset (within one key group's table) of digit row 0 at that rank, two to a word, or
+  // a padding column of rows 0..3 (never read by the A loads) for a channel that is not salient.
+  uint32_t hoff[UK][2];
+#pragma unroll
+  for (int k = 0; k < UK; ++k) {
+    const int u = lane + 64 * k;
+    const int hu = u / JL, j = u % JL;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = u < NT * D ? salient_rank2(mw0, mw1, 4 * j + i, D, a.pairing, a.n_hi) : -1;
+      o[i] = r >= 0 ? (uint32_t)(((hu / 4) * 16 + 4 * (hu % 4)) * TL + 64 * KL + r)
+                    : (uint32_t)(64 * (KL + KHM));
+    }
+    hoff[k][0] = o[0] | (o[1] << 16);
+    hoff[k][1] = o[2] | (o[3] << 16);
   }
   // scaled queries go to LDS (qs) and are read back per page; the registers keep only the
   // per-unit head maxima
@@ -719,15 +728,6 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   float qmaxC[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) qmaxC[t] = qm[4 * t + lane / 16];
-  // upper-bit prep units: uh = lane + 64k -> head uh / JH, ranks 4 (uh % JH) + 0..3; their
-  // channels (sal) and queries (qs) are read from LDS per page
-  constexpr int UKH = (NT * 4 * (D / 4) + 63) / 64;
-  float hqmax[UKH];
-#pragma unroll
-  for (int k = 0; k < UKH; ++k) {
-    const int uh = lane + 64 * k;
-    hqmax[k] = (JH && uh < NH * JH) ? qm[uh / JH] : 0.0f;
-  }
 
   // running softmax state of head 4t + lane/16; p.V accumulators per 16-channel tile (C
   // layout: column lane % 16), value-offset sums per group
@@ -752,7 +752,6 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
       smax = pk_max_u16(smax, pk_max_u16(sv[kg].x, sv[kg].y));
-      if (lane < JL) *reinterpret_cast<uint2*>(Sl + kg * D + 4 * lane) = sv[kg];
     }
     smax = wave_max_u32(max(smax & 0xFFFFu, smax >> 16));
     const float Smax = (float)__builtin_bit_cast(_Float16, (uint16_t)smax);
@@ -792,41 +791,19 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
           for (int d = 0; d < 4; ++d) *reinterpret_cast<uint32_t*>(row + d * TL) = dg[d];
           if (j == 0) biasl[kg * NH + hu] = bz;
         }
-      }
-    }
-    wave_sync();  // Sl and the LSB digits are in LDS
-
-    // ---- digit table, upper-bit part: ranks of salient channels, code weight 2 is in sH
-#pragma unroll
-    for (int k = 0; k < UKH; ++k) {
-      const int uh = lane + 64 * k;
-      if (!(JH && uh < NH * JH)) continue;
-      const int hu = uh / JH, jr = uh % JH;
-      const float sc = pow2i(sigma_of(hqmax[k]));
-      const int t = hu / 4, hl = hu % 4;
-      int hc[4];
-      float hq[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int cs = sal[4 * jr + i];  // -1 past n_sal
-        hc[i] = cs;
-        hq[i] = cs >= 0 ? qs[hu * D + cs] : 0.0f;
-      }
-#pragma unroll
-      for (int kg = 0; kg < KG; ++kg) {
-        uint32_t y[4], dg[4];
+        // the same digit words at the salient ranks of the upper-bit rows
+        uint8_t* tb = T + kg * NT * 16 * TL;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float s = hc[i] >= 0 ? (float)__builtin_bit_cast(_Float16, Sl[kg * D + hc[i]]) : 0.0f;
-          y[i] = digits4((int)((hq[i] * sc) * s));
+          uint8_t* p = tb + ((hoff[k][i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+          p[0] = (uint8_t)y[i];
+          p[TL] = (uint8_t)(y[i] >> 8);
+          p[2 * TL] = (uint8_t)(y[i] >> 16);
+          p[3 * TL] = (uint8_t)(y[i] >> 24);
         }
-        transpose4(y, dg);
-        uint8_t* row = T + ((kg * NT + t) * 16 + 4 * hl) * TL + 64 * KL + 4 * jr;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) *reinterpret_cast<uint32_t*>(row + d * TL) = dg[d];
       }
     }
-    wave_sync();
+    wave_sync();  // the LSB and upper-bit digits are in LDS
 
     // ---- A operands (digit rows) of every tile and key group
     v4i A[KG][NT][KL + KHM];
@@ -1194,8 +1171,7 @@ static size_t lds_T_bytes(const pnmix_cfg& c) {
 static size_t lds_bytes(const pnmix_cfg& c) {
   const int NT = n_tiles(c);
   const size_t W = (size_t)NT * (c.d / c.g_V) * 16 * kWS;
-  return lds_T_bytes(c) + W + 4 * c.d * 2 + 4 * 4 * NT * 4 + c.d * 2 + 4 * NT * 4 +
-         (size_t)4 * NT * c.d * 4;
+  return lds_T_bytes(c) + W + 4 * 4 * NT * 4 + 4 * NT * 4 + (size_t)4 * NT * c.d * 4;
 }
 
 static size_t lds_fp16_bytes(const pnmix_cfg& c) {

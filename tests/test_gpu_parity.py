@@ -384,3 +384,45 @@ def test_online_fill_equals_bulk_fill():
     assert torch.equal(c.v_pages[:, :, :c.n_pages], bulk.v_pages[:, :, :bulk.n_pages])
     assert torch.equal(c.k_sink, bulk.k_sink)
     assert torch.equal(c.k_res[:, :, :c.res_len], bulk.k_res[:, :, :bulk.res_len])
+
+
+# ------------------------------------------------------------ decode kernel instantiations
+
+# Small shapes that reach every split-kernel variant the supported configurations select:
+# head tiles (4-head tiles: 1, 2, and 4 for up to 16 heads, a partly empty second tile for
+# 6 heads), key groups per page (G = 128, 64, 32), one or two upper-bit K-steps (r > 0.5 gives
+# more than 64 salient channels at d = 128), d in {32, 64, 128}, and both launch shapes
+# (workgroups of several waves merged on chip for fewer than 128 (sequence, KV head) items,
+# one wave per workgroup otherwise).  T = 466 holds sinks, three pages and 50 residual rows.
+INST_CASES = [
+    # id, H_q, H_kv, d, pairing, r, G, g_V, B
+    ("ng8-G64", 16, 2, 128, 1, 0.5, 64, 32, 2),
+    ("ng8-G64-B64", 16, 2, 128, 1, 0.5, 64, 32, 64),
+    ("ng4-r075", 8, 2, 128, 1, 0.75, 128, 32, 2),
+    ("ng8-r075", 16, 2, 128, 1, 0.75, 128, 32, 2),
+    ("ng16", 32, 2, 128, 1, 0.5, 128, 32, 2),
+    ("ng6-G32", 12, 2, 128, 0, 0.5, 32, 32, 2),
+    ("d64-ng8", 16, 2, 64, 0, 0.5, 128, 32, 2),
+    ("d32-ng12", 24, 2, 32, 0, 0.25, 64, 16, 2),
+    ("ng4-B64", 8, 2, 128, 1, 0.5, 128, 32, 64),
+]
+
+
+@pytest.mark.parametrize("case", INST_CASES, ids=[c[0] for c in INST_CASES])
+def test_decode_instantiations(case):
+    name, H_q, H_kv, d, pairing, r, G, g_V, B = case
+    T = 32 + 3 * 128 + 50
+    w = synth.Workload(name, 1, B, H_q, H_kv, d, pairing, 1e4, 64, T, r, G, g_V=g_V)
+    lc, oc = cfgs(w)
+    say(f"[decode-inst] {name} B={B} splits={P.pnmix_decode_splits(lc, B, w.n_pages)}")
+    qp, k, v, qd = layer_inputs(w, 3, B, T)
+    cache = fill_cache_bulk(w, lc, qp, k, v, T)
+    out = cache.attend(qd)
+    torch.cuda.synchronize()
+    out_h = out.cpu().numpy()
+    for b in sorted({0, B // 2, B - 1}):
+        ref = oracle_decode(w, oc, u16(qp[b]), u16(k[b]), u16(v[b]), u16(qd[b]), T,
+                            sm_scale(d))
+        err = np.abs(out_h[b] - ref).max()
+        say(f"   b={b} max|err|={err:.3e}")
+        assert err <= ATOL, (name, b, err)

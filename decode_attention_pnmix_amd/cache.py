@@ -101,6 +101,44 @@ class PNMixLayerCache:
         self.sink_len, self.n_pages, self.res_len = s, n_full, rest
         self._sync_lens()
 
+    def load_context(self, q_prompt: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+        """A cache holding a whole context at once: the mask is scored on the first P tokens
+        (q_prompt [B][H_q][P][d] against k[:, :, :P]), then k, v [B][H_kv][T][d] are placed as
+        sinks, full pages (bulk quantization) and an fp16 residual of the remaining rows.  The
+        result equals filling the cache one decode step at a time after a P-token prefill
+        whenever every page boundary was crossed by a flush."""
+        cfg = self.cfg
+        P, T = q_prompt.shape[2], k.shape[2]
+        if not (k.is_contiguous() and v.is_contiguous()):
+            raise ValueError("keys and values must be contiguous [B][H_kv][T][d]")
+        if P > T:
+            raise ValueError("the prompt is longer than the context")
+        self.sigma, mask = L.pnmix_score_prefill(cfg, q_prompt, k[:, :, :P].contiguous())
+        self.mask.copy_(mask)
+        self.n_score_calls += 1
+        s = min(T, cfg.N_s)
+        n_full = (T - s) // cfg.N
+        if n_full > self.max_pages:
+            raise ValueError("context exceeds the cache capacity")
+        self.k_sink.zero_()
+        self.v_sink.zero_()
+        self.k_sink[:, :, :s] = k[:, :, :s]
+        self.v_sink[:, :, :s] = v[:, :, :s]
+        if n_full:
+            kj, _ = self.page_jobs(k, s, 0, n_full)
+            _, vj = self.page_jobs(v, s, 0, n_full)
+            L.pnmix_quantize_k_page(cfg, kj, self.mask)
+            L.pnmix_quantize_v_page(cfg, vj)
+            torch.cuda.current_stream().synchronize()  # jobs reference k, v
+        a = s + n_full * cfg.N
+        rest = T - a
+        self.k_res.zero_()
+        self.v_res.zero_()
+        self.k_res[:, :, :rest] = k[:, :, a:]
+        self.v_res[:, :, :rest] = v[:, :, a:]
+        self.sink_len, self.n_pages, self.res_len = s, n_full, rest
+        self._sync_lens()
+
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor):
         """k_new, v_new [B][H_kv][d]: the decode step's key and value, placed by the library
         (sink row while the sinks are filling, else the next residual row)."""

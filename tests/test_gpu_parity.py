@@ -391,7 +391,8 @@ def test_online_fill_equals_bulk_fill():
 # Small shapes that reach every split-kernel variant the supported configurations select:
 # head tiles (4-head tiles: 1, 2, and 4 for up to 16 heads, a partly empty second tile for
 # 6 heads), key groups per page (G = 128, 64, 32), one or two upper-bit K-steps (r > 0.5 gives
-# more than 64 salient channels at d = 128), d in {32, 64, 128}, and both launch shapes
+# more than 64 salient channels at d = 128; r = 0 and r = 1 are the all-1-bit and all-3-bit key
+# caches), d in {32, 64, 128}, and both launch shapes
 # (workgroups of several waves merged on chip for fewer than 128 (sequence, KV head) items,
 # one wave per workgroup otherwise).  T = 466 holds sinks, three pages and 50 residual rows.
 INST_CASES = [
@@ -405,6 +406,9 @@ INST_CASES = [
     ("d64-ng8", 16, 2, 64, 0, 0.5, 128, 32, 2),
     ("d32-ng12", 24, 2, 32, 0, 0.25, 64, 16, 2),
     ("ng4-B64", 8, 2, 128, 1, 0.5, 128, 32, 64),
+    ("ng4-r0", 8, 2, 128, 1, 0.0, 128, 32, 2),
+    ("ng4-r1", 8, 2, 128, 1, 1.0, 128, 32, 2),
+    ("tinyshape-r0", 4, 2, 32, 0, 0.0, 128, 32, 1),
 ]
 
 

@@ -5,11 +5,11 @@
 // floor(r d/2) pairs of each KV head form a bit mask stored once (Korean summary page,
 // "무엇과 다른가": B x L x H_kv x d/2 bits).
 //
-// Two passes.  Pass 1 gives each (sequence, head, 64-token chunk) one wave; lane i owns RoPE
-// pair i and adds its pair norms over the chunk in ascending token order, reading one token row
-// per step (coalesced: adjacent pairs are one dword per lane, split-half pairs two halves).
-// Pass 2 gives each (sequence, KV head) one workgroup: its waves add the chunk sums of one head
-// each in ascending chunk order, divide by P, then wave 0 forms sigma, ranks the pairs through
+// Two passes.  Pass 1 gives each (sequence, head, 64-token chunk) one wave; the wave stages 32
+// token rows at a time in LDS with 16-byte loads, and lane i owns RoPE pair i and adds its pair
+// norms over the chunk in ascending token order.  Pass 2 gives each (sequence, KV head) one
+// workgroup: its waves add the chunk sums of one head each in ascending chunk order (the loads
+// go out 32 chunks at a time), divide by P, then wave 0 forms sigma, ranks the pairs through
 // LDS and writes the mask with a wave ballot.  The summation order is fixed, so sigma and the
 // mask are bit-identical to the reference oracle.
 #include "common.h"
@@ -19,11 +19,14 @@ namespace pnmix {
 
 constexpr int kChunk = 64;
 
+constexpr int kSub = 32;  // tokens staged in LDS at a time
+
 __global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           float* __restrict__ chunk_sums,
                                                           int H_q, int H_kv, int d, int pairing,
                                                           int P, int n_chunks) {
+  __shared__ __align__(16) uint16_t tile[kSub * 128];  // kSub token rows of up to 128 fp16
   const int chunk = blockIdx.x;
   const int seq_head = blockIdx.y;  // b * (H_q + H_kv) + head
   const int H = H_q + H_kv;
@@ -31,23 +34,42 @@ __global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __rest
   const int head = seq_head % H;
   const int np = d / 2;
   const int i = threadIdx.x;
-  if (i >= np) return;
   const uint16_t* src = head < H_q ? q + ((int64_t)b * H_q + head) * P * d
                                    : k + ((int64_t)b * H_kv + (head - H_q)) * P * d;
   const int c0 = pairing == PNMIX_PAIRS_ADJACENT ? 2 * i : i;
   const int c1 = pairing == PNMIX_PAIRS_ADJACENT ? 2 * i + 1 : i + np;
   const int t0 = chunk * kChunk;
   const int t1 = min(t0 + kChunk, P);
+  // The wave copies kSub token rows at a time into LDS with 16-byte loads (the rows of a
+  // (sequence, head) are contiguous; d * 2 bytes is a multiple of 16), or with 2-byte loads when
+  // the rows are not 16-byte aligned; then lane i adds the norms of pair i over those tokens in
+  // ascending order, as before.
+  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
   float s = 0.0f;
+  for (int ts = t0; ts < t1; ts += kSub) {
+    const int rows = min(kSub, t1 - ts);
+    const uint16_t* g = src + (int64_t)ts * d;
+    if (vec) {
+      const int n16 = rows * d / 8;
+      for (int x = i; x < n16; x += 64)
+        reinterpret_cast<uint4*>(tile)[x] = reinterpret_cast<const uint4*>(g)[x];
+    } else {
+      for (int x = i; x < rows * d; x += 64) tile[x] = g[x];
+    }
+    __syncthreads();
+    if (i < np) {
 #pragma unroll 8
-  for (int t = t0; t < t1; ++t) {
-    const float x = h2f(src[(int64_t)t * d + c0]);
-    const float y = h2f(src[(int64_t)t * d + c1]);
-    const float a = x * x;
-    const float bb = y * y;
-    s = s + sqrtf(a + bb);
+      for (int t = 0; t < rows; ++t) {
+        const float x = h2f(tile[t * d + c0]);
+        const float y = h2f(tile[t * d + c1]);
+        const float a = x * x;
+        const float bb = y * y;
+        s = s + sqrtf(a + bb);
+      }
+    }
+    __syncthreads();  // the tile is refilled
   }
-  chunk_sums[((int64_t)seq_head * n_chunks + chunk) * np + i] = s;
+  if (i < np) chunk_sums[((int64_t)seq_head * n_chunks + chunk) * np + i] = s;
 }
 
 __global__ void __launch_bounds__(256) score_select_kernel(const float* __restrict__ chunk_sums,
@@ -69,8 +91,16 @@ __global__ void __launch_bounds__(256) score_select_kernel(const float* __restri
     const int head = r < ng ? h * ng + r : H_q + h;
     if (lane < np) {
       const float* cs = chunk_sums + ((int64_t)(seq * H + head) * n_chunks) * np + lane;
+      // the adds stay in ascending chunk order; the loads go out 32 at a time
       float s = 0.0f;
-      for (int c = 0; c < n_chunks; ++c) s = s + cs[(int64_t)c * np];
+      for (int c0 = 0; c0 < n_chunks; c0 += 32) {
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] = c0 + j < n_chunks ? cs[(int64_t)(c0 + j) * np] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+          if (c0 + j < n_chunks) s = s + v[j];
+      }
       means[r][lane] = s / (float)P;
     }
   }

@@ -352,32 +352,44 @@ def test_decode_split_count_does_not_change_results():
 
 # ------------------------------------------------------------------------ online vs bulk fill
 
-def test_online_fill_equals_bulk_fill():
-    """Prefill P = 64, then one decode step at a time up to 512 cached tokens (attend, then
-    quantize when the residual buffer is full): every packed page equals bulk quantization of
-    the same tokens, and outputs match the oracle along the way."""
-    w = synth.WORKLOADS["tiny"]
+ONLINE_CASES = {
+    "tiny": (synth.WORKLOADS["tiny"], {65, 159, 160, 161, 288, 289, 512}),
+    # d = 128 split-half pairs, 4 query heads per KV head, G = 64, B = 2, P = 141: page flushes
+    # at 160, 288 and 416 cached tokens
+    "d128-G64": (synth.Workload("online-d128", 1, 2, 16, 4, 128, 1, 1e6, 141, 436, 0.5, 64),
+                 {142, 159, 160, 161, 288, 289, 416, 417, 436}),
+}
+
+
+@pytest.mark.parametrize("name", list(ONLINE_CASES))
+def test_online_fill_equals_bulk_fill(name):
+    """Prefill P tokens, then one decode step at a time (attend, then quantize when the residual
+    buffer is full): every packed page equals bulk quantization of the same tokens, and outputs
+    match the oracle along the way."""
+    w, checks = ONLINE_CASES[name]
     lc, oc = cfgs(w)
     T = w.T
-    qp, k, v, _ = layer_inputs(w, 0, 1, T)
+    max_pages = (T - w.N_s) // w.N + 1
+    qp, k, v, _ = layer_inputs(w, 0, w.B, T)
     npairs = w.d // 2
     sq = synth.pair_scales(w.H_q, npairs, w.sigma_ln, "cuda", w.name, 0, "q")
-    c = P.PNMixLayerCache(lc, 1, 4)
+    c = P.PNMixLayerCache(lc, w.B, max_pages)
     c.prefill(qp, k[:, :, :w.P].contiguous(), v[:, :, :w.P].contiguous())
     assert c.n_score_calls == 1
     mask0 = c.mask.clone()
-    checks = {w.P + 1, 159, 160, 161, 288, 289, T}
+    say(f"[online] {name} B={w.B} P={w.P} T={T}")
     for t in range(w.P, T):
-        qt = synth.rope_tokens(sq, 1, torch.tensor([t], device="cuda"), w.d, w.pairing,
+        qt = synth.rope_tokens(sq, w.B, torch.tensor([t], device="cuda"), w.d, w.pairing,
                                w.rope_base, "cuda", w.name, 0, "qstep", t)[:, :, 0].contiguous()
         o = c.step(qt, k[:, :, t].contiguous(), v[:, :, t].contiguous())
         if t + 1 in checks:
             torch.cuda.synchronize()
-            ref = oracle_decode(w, oc, u16(qp[0]), u16(k[0]), u16(v[0]), u16(qt[0]), t + 1,
-                                sm_scale(w.d), online=True)
-            assert np.abs(o[0].cpu().numpy() - ref).max() <= ATOL, t + 1
+            for b in range(w.B):
+                ref = oracle_decode(w, oc, u16(qp[b]), u16(k[b]), u16(v[b]), u16(qt[b]), t + 1,
+                                    sm_scale(w.d), online=True)
+                assert np.abs(o[b].cpu().numpy() - ref).max() <= ATOL, (t + 1, b)
     assert c.n_score_calls == 1 and torch.equal(c.mask, mask0)  # mask fixed after prefill
-    bulk = fill_cache_bulk(w, lc, qp, k, v, T, max_pages=4)
+    bulk = fill_cache_bulk(w, lc, qp, k, v, T, max_pages=max_pages)
     torch.cuda.synchronize()
     assert (c.sink_len, c.n_pages, c.res_len) == (bulk.sink_len, bulk.n_pages, bulk.res_len)
     assert torch.equal(c.k_pages[:, :, :c.n_pages], bulk.k_pages[:, :, :bulk.n_pages])

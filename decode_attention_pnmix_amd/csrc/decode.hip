@@ -6,11 +6,12 @@
 // group is unpacked on chip and consumed at once).  TriAxialKV fact sheet: flash-decoding
 // splits merged by online log-sum-exp.
 //
-// Work decomposition.  One wave (workgroup of 64) takes one (sequence, KV head, split).  A page
-// split walks a contiguous run of packed pages; one extra split per (sequence, KV head) takes the
-// fp16 sink and residual rows.  All n_g query heads of the GQA group are served from one read of
-// each page, so every packed byte crosses HBM once per step.  Partials (m, l, o) in log2 units go
-// to the workspace; a second kernel merges them.
+// Work decomposition.  One wave takes one (sequence, KV head, split); a workgroup holds one wave
+// or (for small batches) up to eight, whose partials it merges on chip.  A page split walks a
+// run of packed pages; the fp16 splits take 64-token chunks of the sink and residual rows.  All
+// n_g query heads of the GQA group are served from one read of each page, so every packed byte
+// crosses HBM once per step.  Partials (m, l, o) in log2 units go to the workspace; a second
+// kernel merges them.
 //
 // Page split, per page (keys quantized per channel, k = S_c q + Z_c; values per token and group,
 // v = S_tg q + Z_tg):
@@ -22,18 +23,18 @@
 //   the B operand are 16 keys, K is 64 channels.  The B operand is the packed code itself: the
 //   LSB plane byte of (channel, 8 tokens) and the upper-bit plane byte of (salient channel,
 //   4 tokens) are masked in place, one bit field per MFMA, so a tile holds the keys 8i + b of a
-//   page (i = 0..15) and a 16-byte load of either plane feeds eight tiles.  Integer accumulation
-//   is exact; the four digit partials of a key sit in one lane and are combined in fp32.
-// * p.V runs on the fp16 matrix cores (v_mfma_f32_16x16x32_f16).  Rows are (head, value group):
-//   w = p S_tg 2^k (2^k a per-page power of two that puts the page's largest w just under 2^15,
-//   far from the fp16 subnormal floor; the accumulator is rescaled with the softmax factor when
-//   k changes) is split into fp16 hi + lo (two MFMAs, about 22 bits, both halves rounded to
-//   nearest even), columns are 16 channels,
-//   K is 32 keys.  The 2-bit value codes enter as fp16 subnormals code * 2^-16 (the field moved
-//   to bits 8..9 of its half, a shift and an AND per two codes), scaled back by 2^16 at the end.
-//   Codes at the bottom of the subnormal range (code * 2^-24) are exact one product at a time
-//   but lose bits in the matrix core's 32-term sums (an absolute error near 2^-24 per
-//   instruction, measured); at 2^-16 the sums are as accurate as fp32 accumulation.
+//   page (i = 0..15) and a 16-byte load of either plane feeds eight tiles.  The upper-bit rows
+//   hold the LSB rows' digit words of the salient channels, written by the same per-page loop at
+//   each channel's salient rank.  Integer accumulation is exact; the four digit partials of a
+//   key sit in one lane and are combined in fp32.
+// * p.V runs on the int8 matrix cores too.  w = p S_tg per (head, key, value group) becomes
+//   fixed point below 2^23 with a per-head power-of-two scale set from that head's largest p on
+//   the page times the page's largest value scale (so the result does not depend on how pages
+//   are split); its three base-256 digits go to an LDS table whose rows are (head, digit), plus
+//   one row of ones per head whose product is the column sum of the codes (it restores the
+//   offset of the two lower digits, stored as u - 128).  The B operand is again the packed value
+//   byte masked in place: a byte holds channels j, j + d/4, j + d/2, j + 3d/4 of one token, so
+//   one 2-bit field of 16 consecutive bytes is 16 consecutive channels of one value group.
 // * The Z terms and the softmax bookkeeping run on the vector ALU in fp32.
 #include <algorithm>
 

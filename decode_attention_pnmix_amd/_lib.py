@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         "pnmix_quantize_v_page": (st, [cp, i32, P, P]),
         "pnmix_decode_attn": (st, [cp, i32, i32, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P,
                                    sz, P]),
+        "pnmix_decode_attn_paged": (st, [cp, i32, i32, P, P, P, P, P, ctypes.c_int64, P, P, P,
+                                         P, P, ctypes.c_float, P, P, sz, P]),
         "pnmix_append_kv": (st, [cp, i32, P, P, P, P, P, P, P, P]),
         "pnmix_commit_page": (st, [cp, i32, i32, P, P]),
     }
@@ -82,7 +84,7 @@ EXPORTED = ("pnmix_check_cfg", "pnmix_hi_pairs", "pnmix_mask_words", "pnmix_k_pa
             "pnmix_v_page_bytes", "pnmix_score_workspace_bytes", "pnmix_decode_splits",
             "pnmix_decode_workspace_bytes", "pnmix_last_error", "pnmix_score_prefill",
             "pnmix_quantize_k_page", "pnmix_quantize_v_page", "pnmix_decode_attn",
-            "pnmix_append_kv", "pnmix_commit_page")
+            "pnmix_append_kv", "pnmix_commit_page", "pnmix_decode_attn_paged")
 
 
 def _check(status: int):
@@ -228,6 +230,38 @@ def pnmix_decode_attn(cfg, q, k_sink, v_sink, k_pages, v_pages, k_res, v_res, le
                                    _ptr(v_res), _ptr(lens), _ptr(mask), float(sm_scale),
                                    _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)))
+    return out
+
+
+def pnmix_decode_attn_paged(cfg, q, k_sink, v_sink, k_pool, v_pool, block_table, k_res, v_res,
+                            lens, mask, sm_scale: float, out: torch.Tensor | None = None,
+                            ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """pnmix_decode_attn over pages held in pools through a block table: k_pool
+    [n_blocks][H_kv][k page bytes] u8, v_pool [n_blocks][H_kv][v page bytes] u8, block_table
+    [B][max_blocks] int32 (page p of sequence b is block block_table[b][p])."""
+    B = q.shape[0]
+    max_blocks = block_table.shape[1]
+    n_blocks = k_pool.shape[0]
+    _expect(q, (B, cfg.H_q, cfg.d), _F16, "q")
+    _expect(k_sink, (B, cfg.H_kv, cfg.N_s, cfg.d), _F16, "k_sink")
+    _expect(v_sink, (B, cfg.H_kv, cfg.N_s, cfg.d), _F16, "v_sink")
+    _expect(k_pool, (n_blocks, cfg.H_kv, pnmix_k_page_bytes(cfg)), _U8, "k_pool")
+    _expect(v_pool, (n_blocks, cfg.H_kv, pnmix_v_page_bytes(cfg)), _U8, "v_pool")
+    _expect(block_table, (B, max_blocks), _U32, "block_table")
+    _expect(k_res, (B, cfg.H_kv, cfg.N, cfg.d), _F16, "k_res")
+    _expect(v_res, (B, cfg.H_kv, cfg.N, cfg.d), _F16, "v_res")
+    _expect(lens, (B, 4), _U32, "lens")
+    _expect(mask, (B, cfg.H_kv, pnmix_mask_words(cfg)), _U32, "mask")
+    if out is None:
+        out = torch.empty(B, cfg.H_q, cfg.d, dtype=torch.float32, device=q.device)
+    need = pnmix_decode_workspace_bytes(cfg, B, max_blocks)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().pnmix_decode_attn_paged(ctypes.byref(cfg), B, max_blocks, _ptr(q), _ptr(k_sink),
+                                         _ptr(v_sink), _ptr(k_pool), _ptr(v_pool), n_blocks,
+                                         _ptr(block_table), _ptr(k_res), _ptr(v_res), _ptr(lens),
+                                         _ptr(mask), float(sm_scale), _ptr(out), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)))
     return out
 
 

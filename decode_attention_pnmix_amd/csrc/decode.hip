@@ -59,8 +59,10 @@ struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* k_sink;
   const uint16_t* v_sink;
-  const uint8_t* k_pages;
-  const uint8_t* v_pages;
+  const uint8_t* k_pages;  // [B][H_kv][max_pages][kpb], or with a block table the pool
+  const uint8_t* v_pages;  // [n_blocks][H_kv][kpb] (likewise vpb)
+  const int32_t* table;    // NULL (contiguous pages) or the block table [B][max_pages]
+  int64_t n_blocks;        // blocks in the pools (block table only)
   const uint16_t* k_res;
   const uint16_t* v_res;
   const pnmix_seq_len* lens;
@@ -563,7 +565,7 @@ __device__ __forceinline__ int salient_rank2(uint32_t w0, uint32_t w1, int c, in
   return r < 2 * n_hi ? r : -1;
 }
 
-template <int D, int NT, int KG, int KH>
+template <int D, int NT, int KG, int KH, bool PG>
 __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t bh,
                            const PartOut& po) {
   using S_ = Shape<D, KH>;
@@ -618,8 +620,26 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // a branch would make the compiler wait, on the path that issued it, for everything in flight
   // wherever an older load's data is used after the branch rejoins.
   const rsrc_t nul = buf_rsrc(a.k_pages, 0);
-  auto load_k = [&](int pgk, rsrc_t krs) {
-    const uint32_t so = (uint32_t)(pgk * a.kpb);
+  // Page pg of this (sequence, KV head): contiguous pages share one resource at offset pg * bytes;
+  // with a block table the page is block table[b][pg] of the pool (its own resource, offset 0;
+  // the block index is clamped to the pool, so no entry can address outside it).
+  auto page_rsrc = [&](const uint8_t* pool, int64_t bytes, rsrc_t whole, int pg, bool valid,
+                       uint32_t& so) -> rsrc_t {
+    so = 0u;
+    if (!valid) return nul;
+    if constexpr (PG) {
+      const int64_t blk = min(max((int64_t)kconst(a.table + (int64_t)b * a.max_pages + pg)[0],
+                                  (int64_t)0), a.n_blocks - 1);
+      return buf_rsrc(pool + (blk * a.H_kv + h) * bytes, bytes);
+    } else {
+      so = (uint32_t)(pg * bytes);
+      return whole;
+    }
+  };
+  auto load_k = [&](int pgk, bool valid) {
+    uint32_t so;
+    const rsrc_t krs_p = page_rsrc(a.k_pages, a.kpb, krs, pgk, valid, so);
+    const rsrc_t krs = krs_p;
 #pragma unroll
     for (int ks = 0; ks < KL; ++ks) {
       const int c0 = 64 * ks + 16 * qb;
@@ -643,8 +663,10 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   const uint32_t vS = kN * D / 4 + 2 * 8 * oct;  // S [NGV][N] fp16 after the codes, then Z
   v4u sS[4], zZ[4];
   v4u cv[NMB][2];
-  auto load_v = [&](int pgv, rsrc_t vrs) {
-    const uint32_t vso = (uint32_t)(pgv * a.vpb);
+  auto load_v = [&](int pgv, bool valid) {
+    uint32_t vso;
+    const rsrc_t vrs_p = page_rsrc(a.v_pages, a.vpb, vrs, pgv, valid, vso);
+    const rsrc_t vrs = vrs_p;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // groups past NGV repeat the last one: the page maximum is unchanged and the per-group
@@ -662,8 +684,8 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // Pages of this split: split, split + page_splits, ...  (a split past the last page drops
   // the loads of its first one)
   const int step = a.page_splits, p0 = split;
-  load_k(p0, krs);
-  if constexpr (!kLate) load_v(p0, vrs);
+  load_k(p0, true);
+  if constexpr (!kLate) load_v(p0, true);
 
   const auto mrow = kconst(a.mask + bh * a.words);
   const uint32_t mw0 = mrow[0], mw1 = a.words > 1 ? mrow[1] : 0u;
@@ -866,9 +888,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     // ---- the key side of this page is consumed: fetch the next page's (with several head
     // tiles: fetch the value side now and the next keys after p.V, to keep fewer registers live)
     if constexpr (kLate) {
-      load_v(pg, vrs);
+      load_v(pg, true);
     } else {
-      load_k(more ? pg + step : 0, more ? krs : nul);
+      load_k(pg + step, more);
     }
 
     // ---- p.V fixed point, per head: x = rne(p S 2^sh) with 2^sh above the head's largest
@@ -986,9 +1008,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       }
     }
     if constexpr (kLate) {
-      load_k(more ? pg + step : 0, more ? krs : nul);
+      load_k(pg + step, more);
     } else {
-      load_v(more ? pg + step : 0, more ? vrs : nul);
+      load_v(pg + step, more);
     }
     wave_sync();  // T, W and Sl are rewritten by the next page (and by the partial)
   }
@@ -1102,7 +1124,7 @@ struct KernelWaves {
 // Two waves per SIMD (at most 256 registers) where the compiler fits them without spills:
 // one head tile with at most two key groups, or two head tiles with one key group (and one
 // upper-bit K-step at d = 128).
-template <int D, int NT, int KG, int KH>
+template <int D, int NT, int KG, int KH, bool PG>
 __global__ void __launch_bounds__((64 * KernelWaves<D, NT, KG, KH>::max_nw))
 __attribute__((amdgpu_waves_per_eu((KernelWaves<D, NT, KG, KH>::two ? 2 : 1))))
 decode_kernel(DecodeArgs a) {
@@ -1117,7 +1139,7 @@ decode_kernel(DecodeArgs a) {
   lds_f32* const st = (lds_f32*)(wl);
   const PartOut po{a.part_o + pbase * D, a.part_ml + pbase * 2, st, st + ng * D, nw > 1};
   if (split < a.page_splits) {
-    page_split<D, NT, KG, KH>(a, wl, split, bh, po);
+    page_split<D, NT, KG, KH, PG>(a, wl, split, bh, po);
   } else if (split < a.page_splits + a.n16) {
     const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
     const int sink_len = min(max(kconst(&a.lens[b].sink_len)[0], 0), a.N_s);
@@ -1246,10 +1268,10 @@ struct MaxWaves {
 };
 
 // dynamic LDS above 64 KiB has to be allowed per kernel
-template <int D, int NT, int KG, int KH>
+template <int D, int NT, int KG, int KH, bool PG>
 static hipError_t allow_lds(size_t bytes) {
   if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, NT, KG, KH>),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, NT, KG, KH, PG>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
@@ -1261,8 +1283,8 @@ struct BlocksPerCu {
   template <int D, int NT, int KG, int KH>
   int run() const {
     int n = 0;
-    if (allow_lds<D, NT, KG, KH>(lds) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, NT, KG, KH>, threads,
+    if (allow_lds<D, NT, KG, KH, false>(lds) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, NT, KG, KH, false>, threads,
                                                      lds) != hipSuccess ||
         n <= 0) {
       (void)hipGetLastError();
@@ -1328,13 +1350,19 @@ struct Launch {
   const pnmix_cfg& c;
   const DecodeArgs& a;
   hipStream_t stream;
+  template <int D, int NT, int KG, int KH, bool PG>
+  hipError_t split_kernel() const {
+    const hipError_t la = allow_lds<D, NT, KG, KH, PG>(p.lds_bytes);
+    if (la != hipSuccess) return la;
+    hipLaunchKernelGGL((decode_kernel<D, NT, KG, KH, PG>), dim3(p.splits, B * c.H_kv),
+                       dim3(64 * p.nw), p.lds_bytes, stream, a);
+    return hipGetLastError();
+  }
   template <int D, int NT, int KG, int KH>
   hipError_t run() const {
-    const hipError_t la = allow_lds<D, NT, KG, KH>(p.lds_bytes);
-    if (la != hipSuccess) return la;
-    hipLaunchKernelGGL((decode_kernel<D, NT, KG, KH>), dim3(p.splits, B * c.H_kv),
-                       dim3(64 * p.nw), p.lds_bytes, stream, a);
-    const hipError_t e = hipGetLastError();
+    // pages through a block table, or contiguous per (sequence, KV head)
+    const hipError_t e = a.table ? split_kernel<D, NT, KG, KH, true>()
+                                 : split_kernel<D, NT, KG, KH, false>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(B * c.H_q), dim3(256), 0, stream, a);
     return hipGetLastError();
@@ -1345,7 +1373,8 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
                          const uint16_t* k_sink, const uint16_t* v_sink, const uint8_t* k_pages,
                          const uint8_t* v_pages, const uint16_t* k_res, const uint16_t* v_res,
                          const pnmix_seq_len* lens, const uint32_t* mask, float sm_scale,
-                         float* out, void* ws, hipStream_t stream) {
+                         float* out, void* ws, hipStream_t stream, const int32_t* block_table,
+                         int64_t n_blocks) {
   const DecodePlan p = decode_plan(c, B, max_pages);
   const int ng = c.H_q / c.H_kv;
   const size_t per = (size_t)B * c.H_kv * p.splits * ng;
@@ -1355,6 +1384,8 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
   a.v_sink = v_sink;
   a.k_pages = k_pages;
   a.v_pages = v_pages;
+  a.table = block_table;
+  a.n_blocks = n_blocks;
   a.k_res = k_res;
   a.v_res = v_res;
   a.lens = lens;

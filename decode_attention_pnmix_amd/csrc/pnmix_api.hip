@@ -173,6 +173,41 @@ pnmix_status pnmix_decode_attn(const pnmix_cfg* c, int32_t B, int32_t max_pages,
                     "pnmix_decode_attn");
 }
 
+pnmix_status pnmix_decode_attn_paged(const pnmix_cfg* c, int32_t B, int32_t max_blocks,
+                                     const uint16_t* q, const uint16_t* k_sink,
+                                     const uint16_t* v_sink, const uint8_t* k_pool,
+                                     const uint8_t* v_pool, int64_t n_blocks,
+                                     const int32_t* block_table, const uint16_t* k_res,
+                                     const uint16_t* v_res, const pnmix_seq_len* lens,
+                                     const uint32_t* mask, float sm_scale, float* out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (B <= 0 || max_blocks < 0)
+    return fail(PNMIX_E_INVALID, "B = %d must be positive, max_blocks = %d >= 0", B, max_blocks);
+  if ((long long)B * c->H_kv > 65535) return fail(PNMIX_E_UNSUPPORTED, "B * H_kv > 65535");
+  if (!q || !k_res || !v_res || !lens || !mask || !out || !ws)
+    return fail(PNMIX_E_INVALID, "q, k_res, v_res, lens, mask, out and ws must be non-NULL");
+  if (c->N_s > 0 && (!k_sink || !v_sink))
+    return fail(PNMIX_E_INVALID, "k_sink and v_sink must be non-NULL when N_s > 0");
+  if (max_blocks > 0 && (!k_pool || !v_pool || !block_table || n_blocks <= 0))
+    return fail(PNMIX_E_INVALID,
+                "k_pool, v_pool and block_table must be non-NULL and n_blocks > 0 when "
+                "max_blocks > 0");
+  if (!std::isfinite(sm_scale)) return fail(PNMIX_E_INVALID, "sm_scale is not finite");
+  const pnmix::DecodePlan plan = pnmix::decode_plan(*c, B, max_blocks);
+  if (plan.lds_wave > 65536)
+    return fail(PNMIX_E_UNSUPPORTED, "n_g = %d with G = %d needs %zu bytes of LDS (> 64 KiB)",
+                c->H_q / c->H_kv, c->G, plan.lds_wave);
+  if (ws_bytes < plan.ws_bytes)
+    return fail(PNMIX_E_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, plan.ws_bytes);
+  return hip_status(pnmix::launch_decode(*c, B, max_blocks, q, k_sink, v_sink, k_pool, v_pool,
+                                         k_res, v_res, lens, mask, sm_scale, out, ws,
+                                         (hipStream_t)stream, max_blocks > 0 ? block_table : nullptr,
+                                         n_blocks),
+                    "pnmix_decode_attn_paged");
+}
+
 pnmix_status pnmix_append_kv(const pnmix_cfg* c, int32_t B, const uint16_t* k_new,
                              const uint16_t* v_new, uint16_t* k_sink, uint16_t* v_sink,
                              uint16_t* k_res, uint16_t* v_res, pnmix_seq_len* lens,

@@ -172,6 +172,29 @@ pnmix_status pnmix_decode_attn(const pnmix_cfg* cfg, int32_t B, int32_t max_page
                                const pnmix_seq_len* lens, const uint32_t* mask, float sm_scale,
                                float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Decode attention over pages held in a shared pool through a block table ([BLOG] "How it
+ * composes with paging, GQA and offload": a page of the quantized cache is a fixed-size block
+ * carrying its own scales, so quantized pages slot into paged attention's block pool).  Same
+ * operation, arithmetic and results as pnmix_decode_attn above, bit for bit: only the address
+ * of page p of sequence b changes.
+ *   k_pool   [n_blocks][H_kv][pnmix_k_page_bytes] u8: block i holds one page of every KV head
+ *   v_pool   [n_blocks][H_kv][pnmix_v_page_bytes] u8
+ *   block_table [B][max_blocks] int32: page p of sequence b is block block_table[b][p]; only
+ *            the first lens[b].n_pages entries of a row are read (and the first entry of rows
+ *            whose split plan starts a page there), each clamped to [0, n_blocks)
+ *   the other arguments as in pnmix_decode_attn, with max_blocks in place of max_pages; the
+ *   workspace is pnmix_decode_workspace_bytes(cfg, B, max_blocks) bytes.
+ * Pages are written into pool blocks with pnmix_quantize_k_page / pnmix_quantize_v_page (each
+ * job names its destination). */
+pnmix_status pnmix_decode_attn_paged(const pnmix_cfg* cfg, int32_t B, int32_t max_blocks,
+                                     const uint16_t* q, const uint16_t* k_sink,
+                                     const uint16_t* v_sink, const uint8_t* k_pool,
+                                     const uint8_t* v_pool, int64_t n_blocks,
+                                     const int32_t* block_table, const uint16_t* k_res,
+                                     const uint16_t* v_res, const pnmix_seq_len* lens,
+                                     const uint32_t* mask, float sm_scale, float* out, void* ws,
+                                     size_t ws_bytes, void* stream);
+
 /* ---- online cache placement ([PNMIX] sec. 2: new keys and values enter the FP16 residual
  * buffer of N tokens, which is quantized and appended to the cache when full; sec. 5: the
  * first N_s tokens are FP16 sinks) ------------------------------------------------------- */

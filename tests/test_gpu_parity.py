@@ -442,3 +442,49 @@ def test_decode_instantiations(case):
         err = np.abs(out_h[b] - ref).max()
         say(f"   b={b} max|err|={err:.3e}")
         assert err <= ATOL, (name, b, err)
+
+
+# ------------------------------------------------------------------------- paged page pools
+
+PAGED_CASES = [
+    # id, workload, B, T, spare table columns, ragged page counts
+    ("qwen3-8b-B1", "qwen3-8b-1L-32k", 1, 32 + 20 * 128 + 77, 0, False),
+    ("qwen3-32b-B3", "qwen3-32b-64L-b32-32k", 3, 32 + 5 * 128 + 9, 3, True),
+    ("qwen3-8b-B8", "qwen3-8b-36L-b32-8k", 8, 32 + 6 * 128 + 128, 2, True),
+    ("llama-B40", "llama3.1-8b-32L-b110-8k", 40, 32 + 4 * 128 + 1, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[c[0] for c in PAGED_CASES])
+def test_paged_decode_equals_contiguous(case):
+    """The same pages scattered over a shuffled block pool and read through a block table give
+    the same outputs, bit for bit, as the contiguous page arrays (same kernels, same split
+    plan).  Pool blocks no table entry names hold random bytes; table entries past a sequence's
+    page count hold junk (negative or past the pool), which is never used."""
+    name, wname, B, T, spare, ragged = case
+    w = synth.WORKLOADS[wname]
+    lc, _ = cfgs(w)
+    qp, k, v, qd = layer_inputs(w, 4, B, T)
+    n_pages = (T - w.N_s) // w.N
+    c = fill_cache_bulk(w, lc, qp, k, v, T, max_pages=n_pages + spare)
+    if ragged:  # fewer pages for some sequences (their residual rows stay)
+        for b in range(0, B, 2):
+            c.lens[b, 1] = (b // 2) % (n_pages + 1)
+    out_c = c.attend(qd)
+    H, mp = w.H_kv, c.max_pages
+    n_blocks = B * mp + 7
+    gen = torch.Generator().manual_seed(11)
+    perm = torch.randperm(n_blocks, generator=gen)[:B * mp].reshape(B, mp)
+    kpb, vpb = P.pnmix_k_page_bytes(lc), P.pnmix_v_page_bytes(lc)
+    k_pool = torch.randint(0, 256, (n_blocks, H, kpb), dtype=torch.uint8, generator=gen).cuda()
+    v_pool = torch.randint(0, 256, (n_blocks, H, vpb), dtype=torch.uint8, generator=gen).cuda()
+    idx = perm[:, :n_pages].reshape(-1).cuda()
+    k_pool[idx] = c.k_pages[:, :, :n_pages].transpose(1, 2).reshape(-1, H, kpb)
+    v_pool[idx] = c.v_pages[:, :, :n_pages].transpose(1, 2).reshape(-1, H, vpb)
+    table = perm.to(torch.int32).clone()
+    table[:, n_pages:] = torch.where(torch.arange(spare) % 2 == 0, -5, n_blocks + 100)
+    out_p = P.pnmix_decode_attn_paged(lc, qd, c.k_sink, c.v_sink, k_pool, v_pool, table.cuda(),
+                                      c.k_res, c.v_res, c.lens, c.mask, c.sm_scale)
+    torch.cuda.synchronize()
+    say(f"[paged] {name} B={B} pages={n_pages} table={mp} blocks={n_blocks}")
+    assert torch.equal(out_p, out_c)

@@ -577,7 +577,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   constexpr int NMB = (D / 4) / MW;        // value-byte column blocks
   // value loads after q.K and key prefetch after p.V, only where prefetching both sides a page
   // ahead would spill (the 8-head tiles with one or two key groups fit it in registers)
-  constexpr bool kLate = NT >= 4 || (NT == 2 && KG >= 4);
+  constexpr bool kLate = NT >= 2;
 
   const int lane = threadIdx.x & 63;
   const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
@@ -623,22 +623,28 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // Page pg of this (sequence, KV head): contiguous pages share one resource at offset pg * bytes;
   // with a block table the page is block table[b][pg] of the pool (its own resource, offset 0;
   // the block index is clamped to the pool, so no entry can address outside it).
-  auto page_rsrc = [&](const uint8_t* pool, int64_t bytes, rsrc_t whole, int pg, bool valid,
-                       uint32_t& so) -> rsrc_t {
+  // The block of page pg (table entries are read once per page, ahead of both of its loads).
+  auto page_blk = [&](int pg) -> int64_t {
+    if constexpr (PG)
+      return min(max((int64_t)kconst(a.table + (int64_t)b * a.max_pages + pg)[0], (int64_t)0),
+                 a.n_blocks - 1);
+    else
+      return 0;
+  };
+  auto page_rsrc = [&](const uint8_t* pool, int64_t bytes, rsrc_t whole, int pg, int64_t blk,
+                       bool valid, uint32_t& so) -> rsrc_t {
     so = 0u;
     if (!valid) return nul;
     if constexpr (PG) {
-      const int64_t blk = min(max((int64_t)kconst(a.table + (int64_t)b * a.max_pages + pg)[0],
-                                  (int64_t)0), a.n_blocks - 1);
       return buf_rsrc(pool + (blk * a.H_kv + h) * bytes, bytes);
     } else {
       so = (uint32_t)(pg * bytes);
       return whole;
     }
   };
-  auto load_k = [&](int pgk, bool valid) {
+  auto load_k = [&](int pgk, int64_t blk, bool valid) {
     uint32_t so;
-    const rsrc_t krs_p = page_rsrc(a.k_pages, a.kpb, krs, pgk, valid, so);
+    const rsrc_t krs_p = page_rsrc(a.k_pages, a.kpb, krs, pgk, blk, valid, so);
     const rsrc_t krs = krs_p;
 #pragma unroll
     for (int ks = 0; ks < KL; ++ks) {
@@ -663,9 +669,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   const uint32_t vS = kN * D / 4 + 2 * 8 * oct;  // S [NGV][N] fp16 after the codes, then Z
   v4u sS[4], zZ[4];
   v4u cv[NMB][2];
-  auto load_v = [&](int pgv, bool valid) {
+  auto load_v = [&](int pgv, int64_t blk, bool valid) {
     uint32_t vso;
-    const rsrc_t vrs_p = page_rsrc(a.v_pages, a.vpb, vrs, pgv, valid, vso);
+    const rsrc_t vrs_p = page_rsrc(a.v_pages, a.vpb, vrs, pgv, blk, valid, vso);
     const rsrc_t vrs = vrs_p;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -684,8 +690,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // Pages of this split: split, split + page_splits, ...  (a split past the last page drops
   // the loads of its first one)
   const int step = a.page_splits, p0 = split;
-  load_k(p0, true);
-  if constexpr (!kLate) load_v(p0, true);
+  int64_t blk_cur = page_blk(p0);  // p0 < page_splits <= max_pages: inside the table row
+  load_k(p0, blk_cur, true);
+  if constexpr (!kLate) load_v(p0, blk_cur, true);
 
   const auto mrow = kconst(a.mask + bh * a.words);
   const uint32_t mw0 = mrow[0], mw1 = a.words > 1 ? mrow[1] : 0u;
@@ -694,18 +701,18 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // o = 0.  (No early exit: a branch that stores its partial early would force waits for all
   // loads in flight at the point where it rejoins.)
 
-  // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NT][NGV][16][kWS] bytes;
+  // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NGV][16][kWS] bytes (one head tile at a time);
   // bias [KG][NH] f32; head maxima [NH] f32; scaled queries [NH][D] f32.
   uint8_t* T = lds;
   uint8_t* W = lds + a.lds_T;
-  float* biasl = reinterpret_cast<float*>(W + NT * NGV * 16 * kWS);
+  float* biasl = reinterpret_cast<float*>(W + NGV * 16 * kWS);
   float* qm = biasl + 4 * NH;
   float* qs = qm + NH;
 
   // ---- once per split: clear the digit table, salient ranks, scaled queries
   for (int i = lane * 16; i < a.lds_T; i += 64 * 16) *reinterpret_cast<v4u*>(T + i) = v4u{0, 0, 0, 0};
   // p.V digit rows (head, 3) are all ones: their sums are the column sums of the value codes
-  for (int i = lane; i < NT * NGV * 4 * (kN / 16); i += 64) {
+  for (int i = lane; i < NGV * 4 * (kN / 16); i += 64) {
     const int r = i / (kN / 16), c16 = i % (kN / 16);
     *reinterpret_cast<v4u*>(W + (4 * r + 3) * kWS + 16 * c16) =
         v4u{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
@@ -769,6 +776,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 
   for (int pg = p0; pg < n_pages; pg += step) {
     const bool more = pg + step < n_pages;
+    const int64_t blk_next = page_blk(more ? pg + step : pg);
 
     // ---- key scales: page maximum -> per-head fixed-point exponent
     uint32_t smax = 0u;
@@ -888,9 +896,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     // ---- the key side of this page is consumed: fetch the next page's (with several head
     // tiles: fetch the value side now and the next keys after p.V, to keep fewer registers live)
     if constexpr (kLate) {
-      load_v(pg, true);
+      load_v(pg, blk_cur, true);
     } else {
-      load_k(pg + step, more);
+      load_k(pg + step, blk_next, more);
     }
 
     // ---- p.V fixed point, per head: x = rne(p S 2^sh) with 2^sh above the head's largest
@@ -903,10 +911,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       for (int e = 0; e < 4; ++e) svm2 = pk_max_u16(svm2, sS[g][e]);  // S >= 0: bit order
     const float svmax = wave_max_nonneg(fmaxf(f16lo(svm2), f16hi(svm2)));
 
-    // ---- online softmax per head, value-offset term on the vector ALU, digits of w to LDS
-    bool rescale = false;
-    float alpha[NT];
-    int sh[NT];
+    // ---- per head tile: online softmax, value-offset term on the vector ALU, digits of w to
+    // LDS, then p.V.  The tiles take turns on one digit table W, which keeps a wave's LDS slice
+    // small enough for two waves per SIMD with two head tiles.
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       float pm = lg[t][0];
@@ -914,16 +921,16 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       for (int bb = 1; bb < 8; ++bb) pm = fmaxf(pm, lg[t][bb]);
       pm = row_max16(pm);
       const float mn = fmaxf(m_run[t], pm);
-      alpha[t] = __builtin_amdgcn_exp2f(m_run[t] - mn);
-      rescale |= (alpha[t] != 1.0f);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[t] - mn);
       m_run[t] = mn;
+      int sh;
       {
         const float top = __builtin_amdgcn_exp2f(pm - mn) * svmax;  // >= every w of this head
         int e = 0;
         if (top > 0.0f) e = (int)((__builtin_bit_cast(uint32_t, top) >> 23) & 0xFF) - 127;
-        sh[t] = min(max(22 - e, -126), 126);
+        sh = min(max(22 - e, -126), 126);
       }
-      const float sv2 = pow2i(sh[t]);
+      const float sv2 = pow2i(sh);
       float p[8], pw[8], ps = 0.0f;
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
@@ -931,12 +938,12 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         ps += p[bb];
         pw[bb] = p[bb] * sv2;
       }
-      l_run[t] = l_run[t] * alpha[t] + ps;
+      l_run[t] = l_run[t] * alpha + ps;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         if (g >= NGV) break;
         const v4u zz = zZ[g], ss = sS[g];
-        float zs = zacc[t][g] * alpha[t];
+        float zs = zacc[t][g] * alpha;
         uint32_t x[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -951,67 +958,64 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         transpose3(x, d0);
         transpose3(x + 4, d1);
         // digit rows 0, 1 as int8 u - 128 (the ones row 3 restores the offset); row 2 as is
-        uint8_t* row = W + ((t * NGV + g) * 16 + 4 * qb) * kWS + 8 * oct;
+        uint8_t* row = W + (g * 16 + 4 * qb) * kWS + 8 * oct;
         *reinterpret_cast<uint2*>(row) = make_uint2(d0[0] ^ 0x80808080u, d1[0] ^ 0x80808080u);
         *reinterpret_cast<uint2*>(row + kWS) = make_uint2(d0[1] ^ 0x80808080u, d1[1] ^ 0x80808080u);
         *reinterpret_cast<uint2*>(row + 2 * kWS) = make_uint2(d0[2], d1[2]);
       }
-    }
-    if (__any(rescale)) {
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int v = 0; v < NTV; ++v) acc[t][v] *= alpha[t];
-    }
-    wave_sync();  // the w digits are in LDS
-
-    // ---- p.V: tile v = 16 channels of one value group; rows (head, digit), K = 64 keys
-#pragma unroll
-    for (int v = 0; v < NTV; ++v) {
-      // MW = 16: tile (block mb, field u) = channels 16 mb + u d/4 + n;
-      // MW = 8:  tile tb = fields 2tb (n < 8) and 2tb + 1 (n >= 8) = channels 16 tb + n
-      const int mb = MW == 16 ? v % NMB : 0;
-      const int fu = MW == 16 ? v / NMB : v;
-      const int cbase = MW == 16 ? 16 * mb + fu * (D / 4) : 16 * v;
-      const int g = cbase / a.g_V;
-      v4i Bv[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const v4u w = cv[mb][ks];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t f;
-          if (MW == 16) {
-            f = fu == 0 ? (w[e] & 0x03030303u)
-              : fu == 1 ? (w[e] & 0x0C0C0C0Cu)
-              : fu == 2 ? (w[e] & 0x30303030u)
-                        : ((w[e] >> 2) & 0x30303030u);
-          } else {
-            const uint32_t ws = w[e] >> vsh;
-            f = fu == 0 ? (ws & 0x03030303u) : (ws & 0x30303030u);
-          }
-          Bv[ks][e] = (int)f;
-        }
+        for (int v = 0; v < NTV; ++v) acc[t][v] *= alpha;
       }
-      // field weight of the masked bytes: code * {1, 4, 16, 16}[u] (MW 16), {1, 16}[tb] (MW 8)
-      const float fw = MW == 16 ? (fu == 0 ? 1.0f : fu == 1 ? 0.25f : 0.0625f)
-                                : (fu == 0 ? 1.0f : 0.0625f);
+      wave_sync();  // the w digits of this tile are in LDS
+
+      // ---- p.V: tile v = 16 channels of one value group; rows (head, digit), K = 64 keys
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint8_t* wrow = W + ((t * NGV + g) * 16 + (lane & 15)) * kWS + 16 * qb;
+      for (int v = 0; v < NTV; ++v) {
+        // MW = 16: tile (block mb, field u) = channels 16 mb + u d/4 + n;
+        // MW = 8:  tile tb = fields 2tb (n < 8) and 2tb + 1 (n >= 8) = channels 16 tb + n
+        const int mb = MW == 16 ? v % NMB : 0;
+        const int fu = MW == 16 ? v / NMB : v;
+        const int cbase = MW == 16 ? 16 * mb + fu * (D / 4) : 16 * v;
+        const int g = cbase / a.g_V;
+        v4i Bv[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const v4u w = cv[mb][ks];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t f;
+            if (MW == 16) {
+              f = fu == 0 ? (w[e] & 0x03030303u)
+                : fu == 1 ? (w[e] & 0x0C0C0C0Cu)
+                : fu == 2 ? (w[e] & 0x30303030u)
+                          : ((w[e] >> 2) & 0x30303030u);
+            } else {
+              const uint32_t ws = w[e] >> vsh;
+              f = fu == 0 ? (ws & 0x03030303u) : (ws & 0x30303030u);
+            }
+            Bv[ks][e] = (int)f;
+          }
+        }
+        // field weight of the masked bytes: code * {1, 4, 16, 16}[u] (MW 16), {1, 16}[tb] (MW 8)
+        const float fw = MW == 16 ? (fu == 0 ? 1.0f : fu == 1 ? 0.25f : 0.0625f)
+                                  : (fu == 0 ? 1.0f : 0.0625f);
+        const uint8_t* wrow = W + (g * 16 + (lane & 15)) * kWS + 16 * qb;
         const v4i A0 = *reinterpret_cast<const v4i*>(wrow);
         const v4i A1 = *reinterpret_cast<const v4i*>(wrow + 64);
         v4i c = v4i{0, 0, 0, 0};
         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, Bv[0], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, Bv[1], c, 0, 0, 0);
-        acc[t][v] = __builtin_fmaf(combine_pv(c), pow2i(-sh[t]) * fw, acc[t][v]);
+        acc[t][v] = __builtin_fmaf(combine_pv(c), pow2i(-sh) * fw, acc[t][v]);
       }
+      if (t + 1 < NT) wave_sync();  // the next tile rewrites W
     }
     if constexpr (kLate) {
-      load_k(pg + step, more);
+      load_k(pg + step, blk_next, more);
     } else {
-      load_v(pg + step, more);
+      load_v(pg + step, blk_next, more);
     }
+    blk_cur = blk_next;
     wave_sync();  // T, W and Sl are rewritten by the next page (and by the partial)
   }
 
@@ -1193,7 +1197,7 @@ static size_t lds_T_bytes(const pnmix_cfg& c) {
 
 static size_t lds_bytes(const pnmix_cfg& c) {
   const int NT = n_tiles(c);
-  const size_t W = (size_t)NT * (c.d / c.g_V) * 16 * kWS;
+  const size_t W = (size_t)(c.d / c.g_V) * 16 * kWS;  // one table, shared by the head tiles
   return lds_T_bytes(c) + W + 4 * 4 * NT * 4 + 4 * NT * 4 + (size_t)4 * NT * c.d * 4;
 }
 

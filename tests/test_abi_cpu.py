@@ -120,6 +120,26 @@ def test_validation_before_launch():
                                  FAKE, FAKE, dws, None) == L.PNMIX_E_UNSUPPORTED
 
 
+def test_paged_validation_before_launch():
+    lib = P.lib()
+    c = _cfg()
+    dws = P.pnmix_decode_workspace_bytes(c, 4, 10)
+
+    def call(max_blocks=10, n_blocks=40, table=FAKE, k_pool=FAKE, ws_bytes=dws, cfg=c, B=4):
+        return lib.pnmix_decode_attn_paged(ctypes.byref(cfg), B, max_blocks, FAKE, FAKE, FAKE,
+                                           k_pool, FAKE, n_blocks, table, FAKE, FAKE, FAKE, FAKE,
+                                           ctypes.c_float(0.088), FAKE, FAKE, ws_bytes, None)
+
+    assert call(table=None) == L.PNMIX_E_INVALID
+    assert call(k_pool=None) == L.PNMIX_E_INVALID
+    assert call(n_blocks=0) == L.PNMIX_E_INVALID
+    assert call(max_blocks=-1) == L.PNMIX_E_INVALID
+    assert call(B=0) == L.PNMIX_E_INVALID
+    assert call(ws_bytes=dws - 1) == L.PNMIX_E_WORKSPACE
+    assert call(cfg=_cfg(b_V=3)) == L.PNMIX_E_UNSUPPORTED
+    assert P.pnmix_last_error()
+
+
 def test_no_device_is_an_error_not_a_fallback():
     import torch
     if torch.cuda.is_available():

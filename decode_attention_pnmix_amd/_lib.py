@@ -210,12 +210,12 @@ def pnmix_decode_attn(cfg, q, k_sink, v_sink, k_pages, v_pages, k_res, v_res, le
     mask [B][H_kv][words] -> out [B][H_q][d] f32.  ws, when given, is a device byte buffer of
     at least pnmix_decode_workspace_bytes(...) bytes that holds the split-K partials."""
     B = q.shape[0]
-    max_pages = k_pages.shape[2]
+    max_pages = k_pages.shape[1]
     _expect(q, (B, cfg.H_q, cfg.d), _F16, "q")
     _expect(k_sink, (B, cfg.H_kv, cfg.N_s, cfg.d), _F16, "k_sink")
     _expect(v_sink, (B, cfg.H_kv, cfg.N_s, cfg.d), _F16, "v_sink")
-    _expect(k_pages, (B, cfg.H_kv, max_pages, pnmix_k_page_bytes(cfg)), _U8, "k_pages")
-    _expect(v_pages, (B, cfg.H_kv, max_pages, pnmix_v_page_bytes(cfg)), _U8, "v_pages")
+    _expect(k_pages, (B, max_pages, cfg.H_kv, pnmix_k_page_bytes(cfg)), _U8, "k_pages")
+    _expect(v_pages, (B, max_pages, cfg.H_kv, pnmix_v_page_bytes(cfg)), _U8, "v_pages")
     _expect(k_res, (B, cfg.H_kv, cfg.N, cfg.d), _F16, "k_res")
     _expect(v_res, (B, cfg.H_kv, cfg.N, cfg.d), _F16, "v_res")
     _expect(lens, (B, 4), _U32, "lens")

@@ -29,9 +29,10 @@ class PNMixLayerCache:
         f16 = torch.float16
         self.k_sink = torch.zeros(B, H, cfg.N_s, d, dtype=f16, device=device)
         self.v_sink = torch.zeros_like(self.k_sink)
-        self.k_pages = torch.zeros(B, H, max_pages, L.pnmix_k_page_bytes(cfg), dtype=torch.uint8,
+        # pages [B][max_pages][H_kv][bytes]: page p of every KV head side by side
+        self.k_pages = torch.zeros(B, max_pages, H, L.pnmix_k_page_bytes(cfg), dtype=torch.uint8,
                                    device=device)
-        self.v_pages = torch.zeros(B, H, max_pages, L.pnmix_v_page_bytes(cfg), dtype=torch.uint8,
+        self.v_pages = torch.zeros(B, max_pages, H, L.pnmix_v_page_bytes(cfg), dtype=torch.uint8,
                                    device=device)
         self.k_res = torch.zeros(B, H, cfg.N, d, dtype=f16, device=device)
         self.v_res = torch.zeros_like(self.k_res)
@@ -64,7 +65,7 @@ class PNMixLayerCache:
             for h in range(H):
                 for i in range(n):
                     srcs.append(base + (((b * H + h) * T) + first_token + i * cfg.N) * d * es)
-                    slot = (b * H + h) * self.max_pages + page_slot + i
+                    slot = (b * self.max_pages + page_slot + i) * H + h
                     kd.append(self.k_pages.data_ptr() + slot * kpb)
                     vd.append(self.v_pages.data_ptr() + slot * vpb)
                     rows.append(b * H + h)

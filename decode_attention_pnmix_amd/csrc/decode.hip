@@ -59,7 +59,7 @@ struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* k_sink;
   const uint16_t* v_sink;
-  const uint8_t* k_pages;  // [B][H_kv][max_pages][kpb], or with a block table the pool
+  const uint8_t* k_pages;  // [B][max_pages][H_kv][kpb], or with a block table the pool
   const uint8_t* v_pages;  // [n_blocks][H_kv][kpb] (likewise vpb)
   const int32_t* table;    // NULL (contiguous pages) or the block table [B][max_pages]
   int64_t n_blocks;        // blocks in the pools (block table only)
@@ -597,7 +597,6 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   const int oct = lane & 15;  // octet of the q.K B operand (keys 8 oct + b)
   const int qb = lane >> 4;   // K block (16 channels / 8 keys) of this lane
   const int kg_lane = (8 * oct) / G;  // key group of this lane's keys
-  const int64_t page_base = bh * a.max_pages;
   const int sOff = kN * D / 8 + kN * n_sal / 4;      // K page: S after lo and hi planes
   const int zOff = sOff + 2 * KG * D;
   // p.V: this lane's value-byte column within a tile block, and (for 8-column tiles) the
@@ -613,16 +612,21 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // 4 fp16 of S and Z per key group for this lane's channels 4 j .. 4 j + 3, j = lane % JL
   // (the same channels for every prep unit of the lane: 64 is a multiple of JL)
   uint2 sv[KG], zv[KG];
-  const rsrc_t krs = buf_rsrc(a.k_pages + page_base * a.kpb, (int64_t)a.max_pages * a.kpb);
-  const rsrc_t vrs = buf_rsrc(a.v_pages + page_base * a.vpb, (int64_t)a.max_pages * a.vpb);
+  // Contiguous pages [B][max_pages][H_kv][bytes] (the block pool's layout, block b * max_pages
+  // + p): page pg of this head lies pg * H_kv * bytes past this head's first page
+  const int64_t page_row = ((int64_t)b * a.max_pages * a.H_kv + h);
+  const int64_t span = ((int64_t)(a.max_pages - 1) * a.H_kv + 1);
+  const rsrc_t krs = buf_rsrc(a.k_pages + page_row * a.kpb, a.max_pages > 0 ? span * a.kpb : 0);
+  const rsrc_t vrs = buf_rsrc(a.v_pages + page_row * a.vpb, a.max_pages > 0 ? span * a.vpb : 0);
   // The next page's loads are issued whether or not there is a next page, through a resource
   // of zero bytes when there is none (every lane reads zero, nothing is fetched): a load under
   // a branch would make the compiler wait, on the path that issued it, for everything in flight
   // wherever an older load's data is used after the branch rejoins.
   const rsrc_t nul = buf_rsrc(a.k_pages, 0);
-  // Page pg of this (sequence, KV head): contiguous pages share one resource at offset pg * bytes;
-  // with a block table the page is block table[b][pg] of the pool (its own resource, offset 0;
-  // the block index is clamped to the pool, so no entry can address outside it).
+  // Page pg of this (sequence, KV head): contiguous pages share one resource at offset
+  // pg * H_kv * bytes; with a block table the page is block table[b][pg] of the pool (its own
+  // resource, offset 0; the block index is clamped to the pool, so no entry can address
+  // outside it).
   // The block of page pg (table entries are read once per page, ahead of both of its loads).
   auto page_blk = [&](int pg) -> int64_t {
     if constexpr (PG)
@@ -638,7 +642,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     if constexpr (PG) {
       return buf_rsrc(pool + (blk * a.H_kv + h) * bytes, bytes);
     } else {
-      so = (uint32_t)(pg * bytes);
+      so = (uint32_t)((int64_t)pg * a.H_kv * bytes);
       return whole;
     }
   };

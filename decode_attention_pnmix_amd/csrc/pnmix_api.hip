@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "kernels.h"
@@ -159,6 +160,10 @@ pnmix_status pnmix_decode_attn(const pnmix_cfg* c, int32_t B, int32_t max_pages,
     return fail(PNMIX_E_INVALID, "k_sink and v_sink must be non-NULL when N_s > 0");
   if (max_pages > 0 && (!k_pages || !v_pages))
     return fail(PNMIX_E_INVALID, "k_pages and v_pages must be non-NULL when max_pages > 0");
+  if ((long long)max_pages * c->H_kv *
+          (long long)std::max(pnmix_k_page_bytes(c), pnmix_v_page_bytes(c)) > 0xFFFFFFFFLL)
+    return fail(PNMIX_E_UNSUPPORTED,
+                "max_pages * H_kv * page bytes exceeds 4 GiB (use pnmix_decode_attn_paged)");
   if (!std::isfinite(sm_scale)) return fail(PNMIX_E_INVALID, "sm_scale is not finite");
   const pnmix::DecodePlan plan = pnmix::decode_plan(*c, B, max_pages);
   if (plan.lds_wave > 65536)

@@ -275,8 +275,8 @@ def test_decode_ragged_lengths_and_edges():
     v_sink = torch.zeros_like(k_sink)
     k_res = torch.zeros(B, 2, 128, 64, dtype=torch.float16, device="cuda")
     v_res = torch.zeros_like(k_res)
-    k_pages = torch.zeros(B, 2, max_pages, kpb, dtype=torch.uint8, device="cuda")
-    v_pages = torch.zeros(B, 2, max_pages, vpb, dtype=torch.uint8, device="cuda")
+    k_pages = torch.zeros(B, max_pages, 2, kpb, dtype=torch.uint8, device="cuda")
+    v_pages = torch.zeros(B, max_pages, 2, vpb, dtype=torch.uint8, device="cuda")
     lens = torch.zeros(B, 4, dtype=torch.int32)
     srcs, kd, vd, rows, vsrcs = [], [], [], [], []
     for b, (s, npg, r) in enumerate(lens_list):
@@ -288,8 +288,8 @@ def test_decode_ragged_lengths_and_edges():
                 off = ((b * 2 + h) * Tmax + 32 + p * 128) * 64 * 2
                 srcs.append(k.data_ptr() + off)
                 vsrcs.append(v.data_ptr() + off)
-                kd.append(k_pages.data_ptr() + ((b * 2 + h) * max_pages + p) * kpb)
-                vd.append(v_pages.data_ptr() + ((b * 2 + h) * max_pages + p) * vpb)
+                kd.append(k_pages.data_ptr() + ((b * max_pages + p) * 2 + h) * kpb)
+                vd.append(v_pages.data_ptr() + ((b * max_pages + p) * 2 + h) * vpb)
                 rows.append(b * 2 + h)
         a = 32 + npg * 128
         k_res[b, :, :r] = k[b, :, a:a + r]
@@ -392,8 +392,8 @@ def test_online_fill_equals_bulk_fill(name):
     bulk = fill_cache_bulk(w, lc, qp, k, v, T, max_pages=max_pages)
     torch.cuda.synchronize()
     assert (c.sink_len, c.n_pages, c.res_len) == (bulk.sink_len, bulk.n_pages, bulk.res_len)
-    assert torch.equal(c.k_pages[:, :, :c.n_pages], bulk.k_pages[:, :, :bulk.n_pages])
-    assert torch.equal(c.v_pages[:, :, :c.n_pages], bulk.v_pages[:, :, :bulk.n_pages])
+    assert torch.equal(c.k_pages[:, :c.n_pages], bulk.k_pages[:, :bulk.n_pages])
+    assert torch.equal(c.v_pages[:, :c.n_pages], bulk.v_pages[:, :bulk.n_pages])
     assert torch.equal(c.k_sink, bulk.k_sink)
     assert torch.equal(c.k_res[:, :, :c.res_len], bulk.k_res[:, :, :bulk.res_len])
 
@@ -479,8 +479,8 @@ def test_paged_decode_equals_contiguous(case):
     k_pool = torch.randint(0, 256, (n_blocks, H, kpb), dtype=torch.uint8, generator=gen).cuda()
     v_pool = torch.randint(0, 256, (n_blocks, H, vpb), dtype=torch.uint8, generator=gen).cuda()
     idx = perm[:, :n_pages].reshape(-1).cuda()
-    k_pool[idx] = c.k_pages[:, :, :n_pages].transpose(1, 2).reshape(-1, H, kpb)
-    v_pool[idx] = c.v_pages[:, :, :n_pages].transpose(1, 2).reshape(-1, H, vpb)
+    k_pool[idx] = c.k_pages[:, :n_pages].reshape(-1, H, kpb)
+    v_pool[idx] = c.v_pages[:, :n_pages].reshape(-1, H, vpb)
     table = perm.to(torch.int32).clone()
     table[:, n_pages:] = torch.where(torch.arange(spare) % 2 == 0, -5, n_blocks + 100)
     out_p = P.pnmix_decode_attn_paged(lc, qd, c.k_sink, c.v_sink, k_pool, v_pool, table.cuda(),

@@ -488,3 +488,59 @@ def test_paged_decode_equals_contiguous(case):
     torch.cuda.synchronize()
     say(f"[paged] {name} B={B} pages={n_pages} table={mp} blocks={n_blocks}")
     assert torch.equal(out_p, out_c)
+
+
+def test_decode_without_pages_both_entry_points():
+    """max_pages = 0 (sinks and residual rows only): both decode entry points, against the
+    oracle, with ragged sink and residual counts."""
+    w = synth.Workload("nopages", 1, 1, 8, 2, 64, 1, 1e4, 64, 1024, 0.5, 64, g_V=16)
+    lc, oc = cfgs(w)
+    lens_list = [(0, 0, 0), (7, 0, 0), (32, 0, 0), (32, 0, 1), (32, 0, 128), (32, 0, 65)]
+    B = len(lens_list)
+    say(f"[decode-nopages] B={B}")
+    qp, k, v, qd = layer_inputs(w, 2, B, 32 + 128, 64)
+    _, mask = P.pnmix_score_prefill(lc, qp, k[:, :, :64].contiguous())
+    k_sink = torch.zeros(B, 2, 32, 64, dtype=torch.float16, device="cuda")
+    v_sink = torch.zeros_like(k_sink)
+    k_res = torch.zeros(B, 2, 128, 64, dtype=torch.float16, device="cuda")
+    v_res = torch.zeros_like(k_res)
+    lens = torch.zeros(B, 4, dtype=torch.int32)
+    for b, (s_, _, r) in enumerate(lens_list):
+        lens[b, :3] = torch.tensor([s_, 0, r])
+        k_sink[b, :, :s_] = k[b, :, :s_]
+        v_sink[b, :, :s_] = v[b, :, :s_]
+        k_res[b, :, :r] = k[b, :, 32:32 + r]
+        v_res[b, :, :r] = v[b, :, 32:32 + r]
+    lens = lens.cuda()
+    kp0 = torch.zeros(B, 0, 2, P.pnmix_k_page_bytes(lc), dtype=torch.uint8, device="cuda")
+    vp0 = torch.zeros(B, 0, 2, P.pnmix_v_page_bytes(lc), dtype=torch.uint8, device="cuda")
+    out_c = P.pnmix_decode_attn(lc, qd, k_sink, v_sink, kp0, vp0, k_res, v_res, lens, mask,
+                                sm_scale(64))
+    kpool = torch.zeros(1, 2, P.pnmix_k_page_bytes(lc), dtype=torch.uint8, device="cuda")
+    vpool = torch.zeros(1, 2, P.pnmix_v_page_bytes(lc), dtype=torch.uint8, device="cuda")
+    table = torch.zeros(B, 0, dtype=torch.int32, device="cuda")
+    out_p = P.pnmix_decode_attn_paged(lc, qd, k_sink, v_sink, kpool, vpool, table, k_res, v_res,
+                                      lens, mask, sm_scale(64))
+    torch.cuda.synchronize()
+    assert torch.equal(out_c, out_p)
+    out_h = out_c.cpu().numpy()
+    mask_h = mask.cpu().numpy().view(np.uint32)
+    kh, vh = u16(k), u16(v)
+    for b, (s_, _, r) in enumerate(lens_list):
+        if s_ + r == 0:
+            assert np.all(out_h[b] == 0)
+            continue
+        ks = np.zeros((2, 32, 64), np.uint16)
+        vs = np.zeros_like(ks)
+        ks[:, :s_] = kh[b, :, :s_]
+        vs[:, :s_] = vh[b, :, :s_]
+        kr = np.zeros((2, 128, 64), np.uint16)
+        vr = np.zeros_like(kr)
+        kr[:, :r] = kh[b, :, 32:32 + r]
+        vr[:, :r] = vh[b, :, 32:32 + r]
+        kp = np.zeros((2, 0, P.pnmix_k_page_bytes(lc)), np.uint8)
+        vp = np.zeros((2, 0, P.pnmix_v_page_bytes(lc)), np.uint8)
+        ref = oracle.decode_attn_f64(oc, u16(qd[b]), ks, vs, kp, vp, kr, vr, mask_h[b], s_, 0,
+                                     r, sm_scale(64))
+        err = np.abs(out_h[b] - ref).max()
+        assert err <= ATOL, (lens_list[b], err)

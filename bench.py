@@ -285,11 +285,9 @@ def main():
     def run_step(i, lens_log=None):
         for layer, c in enumerate(caches):
             qst, kst, vst = inputs[layer]
-            c.append(kst[i], vst[i])
+            c.step(qst[i], kst[i], vst[i], outs[layer])  # append + attend, then flush if full
             if lens_log is not None and layer == 0:
                 lens_log.append((c.sink_len, c.n_pages, c.res_len))
-            c.attend(qst[i], outs[layer])
-            c.flush()
 
     for i in range(W):
         run_step(i)
@@ -298,6 +296,8 @@ def main():
     # ---- capture the K timed steps once, then replay them from the same starting state
     saved_lens = [c.lens.clone() for c in caches]
     saved_host = [(c.sink_len, c.n_pages, c.res_len) for c in caches]
+    # a step reads one lengths buffer and writes the other; the graph's first step reads these
+    saved_bufs = [(c.lens, c._lens_next) for c in caches]
     lens_log = []
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -305,7 +305,8 @@ def main():
             run_step(i, lens_log)
 
     def restore():
-        for c, sl, sh in zip(caches, saved_lens, saved_host):
+        for c, sl, sh, bufs in zip(caches, saved_lens, saved_host, saved_bufs):
+            c.lens, c._lens_next = bufs
             c.lens.copy_(sl)
             c.sink_len, c.n_pages, c.res_len = sh
         torch.cuda.synchronize()

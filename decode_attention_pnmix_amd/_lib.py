@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                    sz, P]),
         "pnmix_decode_attn_paged": (st, [cp, i32, i32, P, P, P, P, P, ctypes.c_int64, P, P, P,
                                          P, P, ctypes.c_float, P, P, sz, P]),
+        "pnmix_append_decode_attn": (st, [cp, i32, i32] + [P] * 12 + [ctypes.c_float, P, P, sz,
+                                                                     P]),
         "pnmix_append_kv": (st, [cp, i32, P, P, P, P, P, P, P, P]),
         "pnmix_commit_page": (st, [cp, i32, i32, P, P]),
     }
@@ -84,7 +86,8 @@ EXPORTED = ("pnmix_check_cfg", "pnmix_hi_pairs", "pnmix_mask_words", "pnmix_k_pa
             "pnmix_v_page_bytes", "pnmix_score_workspace_bytes", "pnmix_decode_splits",
             "pnmix_decode_workspace_bytes", "pnmix_last_error", "pnmix_score_prefill",
             "pnmix_quantize_k_page", "pnmix_quantize_v_page", "pnmix_decode_attn",
-            "pnmix_append_kv", "pnmix_commit_page", "pnmix_decode_attn_paged")
+            "pnmix_append_kv", "pnmix_commit_page", "pnmix_decode_attn_paged",
+            "pnmix_append_decode_attn")
 
 
 def _check(status: int):
@@ -230,6 +233,40 @@ def pnmix_decode_attn(cfg, q, k_sink, v_sink, k_pages, v_pages, k_res, v_res, le
                                    _ptr(v_res), _ptr(lens), _ptr(mask), float(sm_scale),
                                    _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)))
+    return out
+
+
+def pnmix_append_decode_attn(cfg, q, k_new, v_new, k_sink, v_sink, k_pages, v_pages, k_res,
+                             v_res, lens, lens_out, mask, sm_scale: float,
+                             out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                             stream=None) -> torch.Tensor:
+    """pnmix_append_kv then pnmix_decode_attn in one call: k_new, v_new [B][H_kv][d] fp16 enter
+    the sinks or residual rows, lens [B][4] (before) is read, lens_out [B][4] (after) written."""
+    B = q.shape[0]
+    max_pages = k_pages.shape[1]
+    _expect(q, (B, cfg.H_q, cfg.d), _F16, "q")
+    _expect(k_new, (B, cfg.H_kv, cfg.d), _F16, "k_new")
+    _expect(v_new, (B, cfg.H_kv, cfg.d), _F16, "v_new")
+    _expect(k_sink, (B, cfg.H_kv, cfg.N_s, cfg.d), _F16, "k_sink")
+    _expect(v_sink, (B, cfg.H_kv, cfg.N_s, cfg.d), _F16, "v_sink")
+    _expect(k_pages, (B, max_pages, cfg.H_kv, pnmix_k_page_bytes(cfg)), _U8, "k_pages")
+    _expect(v_pages, (B, max_pages, cfg.H_kv, pnmix_v_page_bytes(cfg)), _U8, "v_pages")
+    _expect(k_res, (B, cfg.H_kv, cfg.N, cfg.d), _F16, "k_res")
+    _expect(v_res, (B, cfg.H_kv, cfg.N, cfg.d), _F16, "v_res")
+    _expect(lens, (B, 4), _U32, "lens")
+    _expect(lens_out, (B, 4), _U32, "lens_out")
+    _expect(mask, (B, cfg.H_kv, pnmix_mask_words(cfg)), _U32, "mask")
+    if out is None:
+        out = torch.empty(B, cfg.H_q, cfg.d, dtype=torch.float32, device=q.device)
+    need = pnmix_decode_workspace_bytes(cfg, B, max_pages)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().pnmix_append_decode_attn(ctypes.byref(cfg), B, max_pages, _ptr(q), _ptr(k_new),
+                                          _ptr(v_new), _ptr(k_sink), _ptr(v_sink), _ptr(k_pages),
+                                          _ptr(v_pages), _ptr(k_res), _ptr(v_res), _ptr(lens),
+                                          _ptr(lens_out), _ptr(mask), float(sm_scale), _ptr(out),
+                                          _ptr(ws), ws.numel() * ws.element_size(),
+                                          _stream(stream)))
     return out
 
 

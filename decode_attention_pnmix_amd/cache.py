@@ -40,6 +40,7 @@ class PNMixLayerCache:
         self.sigma = None
         self.sink_len = self.n_pages = self.res_len = 0
         self.lens = torch.zeros(B, 4, dtype=torch.int32, device=device)
+        self._lens_next = torch.zeros_like(self.lens)  # lengths written by a fused step
         self.sm_scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
         self.ws = torch.empty(max(L.pnmix_decode_workspace_bytes(cfg, B, max_pages), 256),
                               dtype=torch.uint8, device=device)
@@ -182,8 +183,19 @@ class PNMixLayerCache:
         return True
 
     def step(self, q, k_new, v_new, out=None):
-        """One decode step: append, attend, then quantize if the residual buffer is full."""
-        self.append(k_new, v_new)
-        o = self.attend(q, out)
+        """One decode step: append and attend in one call (pnmix_append_decode_attn, the same
+        outputs as append then attend), then quantize if the residual buffer is full."""
+        cfg = self.cfg
+        if self.res_len >= cfg.N:
+            raise RuntimeError("residual buffer full: flush() after attending")
+        o = L.pnmix_append_decode_attn(cfg, q, k_new, v_new, self.k_sink, self.v_sink,
+                                       self.k_pages, self.v_pages, self.k_res, self.v_res,
+                                       self.lens, self._lens_next, self.mask, self.sm_scale,
+                                       out=out, ws=self.ws)
+        self.lens, self._lens_next = self._lens_next, self.lens
+        if self.sink_len < cfg.N_s and self.n_pages == 0 and self.res_len == 0:
+            self.sink_len += 1
+        else:
+            self.res_len += 1
         self.flush()
         return o

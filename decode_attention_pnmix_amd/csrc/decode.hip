@@ -67,6 +67,13 @@ struct DecodeArgs {
   const uint16_t* v_res;
   const pnmix_seq_len* lens;
   const uint32_t* mask;
+  // Append fused into the call (NULL k_new: none): the new key and value rows [B][H_kv][d] take
+  // part in the attention straight from k_new / v_new, and the merge kernel then writes them
+  // into the sink or residual rows (k_sink ... v_res are the caller's writable buffers) and
+  // the advanced lengths into lens_out (never the lens array every wave reads).
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  pnmix_seq_len* lens_out;
   float* part_o;   // [B*H_kv][splits][n_g][d]
   float* part_ml;  // [B*H_kv][splits][n_g][2]
   float* out;      // [B][H_q][d]
@@ -401,10 +408,29 @@ __device__ void write_empty_partial(const DecodeArgs& a, const PartOut& po) {
 //   [channel][token] rows;
 // * every softmax quantity of head n lives in the lanes of column n: the maximum is taken over
 //   the lane's 8 tokens, then over the four lane groups.
+// Where a fused append puts sequence b's new row, from its lengths before the call (the rule
+// of the append entry point): sink row sink_len while the sinks are filling and the sequence
+// has neither pages nor residual rows (kind 0), else residual row res_len if that is below N
+// (kind 1), else nowhere (kind 2).
+__device__ __forceinline__ void append_slot(const pnmix_seq_len& L, int N_s, int& kind, int& row) {
+  if (L.sink_len < N_s && L.n_pages == 0 && L.res_len == 0) {
+    kind = 0;
+    row = max(L.sink_len, 0);
+  } else if (L.res_len >= 0 && L.res_len < kN) {
+    kind = 1;
+    row = L.res_len;
+  } else {
+    kind = 2;
+    row = 0;
+  }
+}
+
+// t_new >= 0: fp16 row t_new (sinks first, then residual rows) is the fused append's new row,
+// read from k_new / v_new instead of the cache.
 template <int D>
 __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, const PartOut& po,
                             int sink_len, int res_len, int chunk, int n_chunk_splits,
-                            uint8_t* lds) {
+                            uint8_t* lds, int t_new) {
   constexpr int KS = D / 32;         // 32-channel K-steps of S^T
   constexpr int CT = D / 16;         // 16-channel tiles of O^T
   constexpr int VS = 36;             // V^T row stride in halves: 32 tokens + 4 (bank spread)
@@ -426,8 +452,16 @@ __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, const
   const uint16_t* v_s = a.v_sink + bh * a.N_s * D;
   const uint16_t* k_r = a.k_res + bh * kN * D - (int64_t)sink_len * D;  // row t >= sink_len
   const uint16_t* v_r = a.v_res + bh * kN * D - (int64_t)sink_len * D;
-  auto krow = [&](int t) { t = min(t, T16 - 1); return (t < sink_len ? k_s : k_r) + (int64_t)t * D; };
-  auto vrow = [&](int t) { t = min(t, T16 - 1); return (t < sink_len ? v_s : v_r) + (int64_t)t * D; };
+  const uint16_t* k_n = t_new >= 0 ? a.k_new + bh * D : k_s;
+  const uint16_t* v_n = t_new >= 0 ? a.v_new + bh * D : v_s;
+  auto krow = [&](int t) {
+    t = min(t, T16 - 1);
+    return t == t_new ? k_n : (t < sink_len ? k_s : k_r) + (int64_t)t * D;
+  };
+  auto vrow = [&](int t) {
+    t = min(t, T16 - 1);
+    return t == t_new ? v_n : (t < sink_len ? v_s : v_r) + (int64_t)t * D;
+  };
   float m = -INFINITY, l = 0.0f;  // l: this lane's tokens only, summed over lane groups at the end
   v4f acc[CT];
 #pragma unroll
@@ -1113,6 +1147,30 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
     const float inv = acc.l > 0.0f ? 1.0f / acc.l : 0.0f;
     *reinterpret_cast<v4f*>(a.out + (int64_t)bhq * D + 4 * tid) = acc.o * inv;
   }
+  // Fused append: every split of this call has read the cache and the lengths, so the new rows
+  // go in now, one (sequence, KV head) per block of its first query head, and the advanced
+  // lengths into lens_out.
+  if (a.k_new && hh == 0) {
+    const pnmix_seq_len L = a.lens[b];
+    int kind, row;
+    append_slot(L, a.N_s, kind, row);
+    if (kind != 2 && tid < 2 * (D / 8)) {
+      const bool isv = tid >= D / 8;
+      const int c8 = isv ? tid - D / 8 : tid;
+      const int cap = kind == 0 ? a.N_s : kN;
+      uint16_t* dst = const_cast<uint16_t*>(kind == 0 ? (isv ? a.v_sink : a.k_sink)
+                                                      : (isv ? a.v_res : a.k_res));
+      const uint16_t* src = (isv ? a.v_new : a.k_new) + bh * D + 8 * c8;
+      *reinterpret_cast<v4u*>(dst + (bh * cap + row) * D + 8 * c8) =
+          *reinterpret_cast<const v4u*>(src);
+    }
+    if (h == 0 && tid == 0) {
+      pnmix_seq_len Lo = L;
+      if (kind == 0) Lo.sink_len = row + 1;
+      if (kind == 1) Lo.res_len = row + 1;
+      a.lens_out[b] = Lo;
+    }
+  }
 }
 
 // Waves per workgroup the split kernel is compiled for: eight for the instantiations that run
@@ -1150,9 +1208,21 @@ decode_kernel(DecodeArgs a) {
     page_split<D, NT, KG, KH, PG>(a, wl, split, bh, po);
   } else if (split < a.page_splits + a.n16) {
     const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
-    const int sink_len = min(max(kconst(&a.lens[b].sink_len)[0], 0), a.N_s);
-    const int res_len = min(max(kconst(&a.lens[b].res_len)[0], 0), kN);
-    fp16_region<D>(a, b, h, bh, po, sink_len, res_len, split - a.page_splits, a.n16, wl);
+    pnmix_seq_len L;
+    L.sink_len = kconst(&a.lens[b].sink_len)[0];
+    L.n_pages = kconst(&a.lens[b].n_pages)[0];
+    L.res_len = kconst(&a.lens[b].res_len)[0];
+    int t_new = -1;
+    if (a.k_new) {  // the fused append's row joins the fp16 rows
+      int kind, row;
+      append_slot(L, a.N_s, kind, row);
+      if (kind == 0) L.sink_len = row + 1;
+      if (kind == 1) L.res_len = row + 1;
+      if (kind != 2) t_new = kind == 0 ? row : min(max(L.sink_len, 0), a.N_s) + row;
+    }
+    const int sink_len = min(max(L.sink_len, 0), a.N_s);
+    const int res_len = min(max(L.res_len, 0), kN);
+    fp16_region<D>(a, b, h, bh, po, sink_len, res_len, split - a.page_splits, a.n16, wl, t_new);
   } else {
     write_empty_partial<D>(a, po);
   }
@@ -1382,7 +1452,8 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
                          const uint8_t* v_pages, const uint16_t* k_res, const uint16_t* v_res,
                          const pnmix_seq_len* lens, const uint32_t* mask, float sm_scale,
                          float* out, void* ws, hipStream_t stream, const int32_t* block_table,
-                         int64_t n_blocks) {
+                         int64_t n_blocks, const uint16_t* k_new, const uint16_t* v_new,
+                         pnmix_seq_len* lens_out) {
   const DecodePlan p = decode_plan(c, B, max_pages);
   const int ng = c.H_q / c.H_kv;
   const size_t per = (size_t)B * c.H_kv * p.splits * ng;
@@ -1394,6 +1465,9 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
   a.v_pages = v_pages;
   a.table = block_table;
   a.n_blocks = n_blocks;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.lens_out = lens_out;
   a.k_res = k_res;
   a.v_res = v_res;
   a.lens = lens;

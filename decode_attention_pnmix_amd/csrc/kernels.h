@@ -34,7 +34,9 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
                          const uint8_t* v_pages, const uint16_t* k_res, const uint16_t* v_res,
                          const pnmix_seq_len* lens, const uint32_t* mask, float sm_scale,
                          float* out, void* ws, hipStream_t stream,
-                         const int32_t* block_table = nullptr, int64_t n_blocks = 0);
+                         const int32_t* block_table = nullptr, int64_t n_blocks = 0,
+                         const uint16_t* k_new = nullptr, const uint16_t* v_new = nullptr,
+                         pnmix_seq_len* lens_out = nullptr);
 
 hipError_t launch_append_kv(const pnmix_cfg& c, int B, const uint16_t* k_new,
                             const uint16_t* v_new, uint16_t* k_sink, uint16_t* v_sink,

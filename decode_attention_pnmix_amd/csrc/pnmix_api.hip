@@ -143,12 +143,14 @@ pnmix_status pnmix_quantize_v_page(const pnmix_cfg* c, int32_t n_pages, const pn
                     "pnmix_quantize_v_page");
 }
 
-pnmix_status pnmix_decode_attn(const pnmix_cfg* c, int32_t B, int32_t max_pages,
-                               const uint16_t* q, const uint16_t* k_sink, const uint16_t* v_sink,
-                               const uint8_t* k_pages, const uint8_t* v_pages,
-                               const uint16_t* k_res, const uint16_t* v_res,
-                               const pnmix_seq_len* lens, const uint32_t* mask, float sm_scale,
-                               float* out, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks shared by the contiguous decode entry points (before any HIP call).
+static pnmix_status check_decode(const pnmix_cfg* c, int32_t B, int32_t max_pages,
+                                 const uint16_t* q, const uint16_t* k_sink,
+                                 const uint16_t* v_sink, const uint8_t* k_pages,
+                                 const uint8_t* v_pages, const uint16_t* k_res,
+                                 const uint16_t* v_res, const pnmix_seq_len* lens,
+                                 const uint32_t* mask, float sm_scale, float* out, void* ws,
+                                 size_t ws_bytes) {
   pnmix_status s = check(c);
   if (s != PNMIX_OK) return s;
   if (B <= 0 || max_pages < 0)
@@ -169,13 +171,48 @@ pnmix_status pnmix_decode_attn(const pnmix_cfg* c, int32_t B, int32_t max_pages,
   if (plan.lds_wave > 65536)
     return fail(PNMIX_E_UNSUPPORTED, "n_g = %d with G = %d needs %zu bytes of LDS (> 64 KiB)",
                 c->H_q / c->H_kv, c->G, plan.lds_wave);
-  const size_t need = plan.ws_bytes;
-  if (ws_bytes < need)
-    return fail(PNMIX_E_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
+  if (ws_bytes < plan.ws_bytes)
+    return fail(PNMIX_E_WORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, plan.ws_bytes);
+  return PNMIX_OK;
+}
+
+pnmix_status pnmix_decode_attn(const pnmix_cfg* c, int32_t B, int32_t max_pages,
+                               const uint16_t* q, const uint16_t* k_sink, const uint16_t* v_sink,
+                               const uint8_t* k_pages, const uint8_t* v_pages,
+                               const uint16_t* k_res, const uint16_t* v_res,
+                               const pnmix_seq_len* lens, const uint32_t* mask, float sm_scale,
+                               float* out, void* ws, size_t ws_bytes, void* stream) {
+  const pnmix_status s = check_decode(c, B, max_pages, q, k_sink, v_sink, k_pages, v_pages,
+                                      k_res, v_res, lens, mask, sm_scale, out, ws, ws_bytes);
+  if (s != PNMIX_OK) return s;
   return hip_status(pnmix::launch_decode(*c, B, max_pages, q, k_sink, v_sink, k_pages, v_pages,
                                          k_res, v_res, lens, mask, sm_scale, out, ws,
                                          (hipStream_t)stream),
                     "pnmix_decode_attn");
+}
+
+pnmix_status pnmix_append_decode_attn(const pnmix_cfg* c, int32_t B, int32_t max_pages,
+                                      const uint16_t* q, const uint16_t* k_new,
+                                      const uint16_t* v_new, uint16_t* k_sink, uint16_t* v_sink,
+                                      const uint8_t* k_pages, const uint8_t* v_pages,
+                                      uint16_t* k_res, uint16_t* v_res,
+                                      const pnmix_seq_len* lens, pnmix_seq_len* lens_out,
+                                      const uint32_t* mask, float sm_scale, float* out, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  const pnmix_status s = check_decode(c, B, max_pages, q, k_sink, v_sink, k_pages, v_pages,
+                                      k_res, v_res, lens, mask, sm_scale, out, ws, ws_bytes);
+  if (s != PNMIX_OK) return s;
+  if (!k_new || !v_new || !lens_out)
+    return fail(PNMIX_E_INVALID, "k_new, v_new and lens_out must be non-NULL");
+  const char* lo = reinterpret_cast<const char*>(lens_out);
+  const char* li = reinterpret_cast<const char*>(lens);
+  const size_t lb = (size_t)B * sizeof(pnmix_seq_len);
+  if (lo < li + lb && li < lo + lb)
+    return fail(PNMIX_E_INVALID, "lens_out must not overlap lens");
+  return hip_status(pnmix::launch_decode(*c, B, max_pages, q, k_sink, v_sink, k_pages, v_pages,
+                                         k_res, v_res, lens, mask, sm_scale, out, ws,
+                                         (hipStream_t)stream, nullptr, 0, k_new, v_new, lens_out),
+                    "pnmix_append_decode_attn");
 }
 
 pnmix_status pnmix_decode_attn_paged(const pnmix_cfg* c, int32_t B, int32_t max_blocks,

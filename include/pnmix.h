@@ -175,6 +175,27 @@ pnmix_status pnmix_decode_attn(const pnmix_cfg* cfg, int32_t B, int32_t max_page
                                const pnmix_seq_len* lens, const uint32_t* mask, float sm_scale,
                                float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* One decode step in one call: pnmix_append_kv then pnmix_decode_attn ([PNMIX] sec. 2: the
+ * new key and value enter the FP16 residual buffer, or the sinks while those fill, and the step
+ * attends over the cache that includes them), with the same outputs bit for bit and one launch
+ * fewer.  The new rows join the attention straight from k_new / v_new; once every split has
+ * read the cache they are written into k_sink / v_sink or k_res / v_res at the row
+ * pnmix_append_kv would use, and the lengths after the append go to lens_out.
+ *   k_new, v_new [B][H_kv][d] fp16
+ *   lens       [B] lengths before the step (read only)
+ *   lens_out   [B] lengths after the step (written); must not overlap lens
+ *   the other arguments as in pnmix_decode_attn (k_sink ... v_res are written).
+ * A sequence whose residual buffer already holds N rows takes no new row (lens_out = lens for
+ * it), as with pnmix_append_kv. */
+pnmix_status pnmix_append_decode_attn(const pnmix_cfg* cfg, int32_t B, int32_t max_pages,
+                                      const uint16_t* q, const uint16_t* k_new,
+                                      const uint16_t* v_new, uint16_t* k_sink, uint16_t* v_sink,
+                                      const uint8_t* k_pages, const uint8_t* v_pages,
+                                      uint16_t* k_res, uint16_t* v_res,
+                                      const pnmix_seq_len* lens, pnmix_seq_len* lens_out,
+                                      const uint32_t* mask, float sm_scale, float* out, void* ws,
+                                      size_t ws_bytes, void* stream);
+
 /* Decode attention over pages held in a shared pool through a block table ([BLOG] "How it
  * composes with paging, GQA and offload": a page of the quantized cache is a fixed-size block
  * carrying its own scales, so quantized pages slot into paged attention's block pool).  Same

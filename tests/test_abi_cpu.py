@@ -146,6 +146,23 @@ def test_paged_validation_before_launch():
     assert P.pnmix_last_error()
 
 
+def test_fused_step_validation_before_launch():
+    lib = P.lib()
+    c = _cfg()
+    dws = P.pnmix_decode_workspace_bytes(c, 4, 10)
+
+    def call(k_new=FAKE, lens=FAKE, lens_out=ctypes.c_void_p(0x20000)):
+        return lib.pnmix_append_decode_attn(ctypes.byref(c), 4, 10, FAKE, k_new, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, FAKE, lens, lens_out, FAKE,
+                                            ctypes.c_float(0.088), FAKE, FAKE, dws, None)
+
+    assert call(k_new=None) == L.PNMIX_E_INVALID
+    assert call(lens_out=None) == L.PNMIX_E_INVALID
+    assert call(lens_out=FAKE) == L.PNMIX_E_INVALID  # lens_out is lens
+    assert call(lens_out=ctypes.c_void_p(0x10000 + 16)) == L.PNMIX_E_INVALID  # overlapping
+    assert "overlap" in P.pnmix_last_error()
+
+
 def test_no_device_is_an_error_not_a_fallback():
     import torch
     if torch.cuda.is_available():

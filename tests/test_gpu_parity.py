@@ -544,3 +544,53 @@ def test_decode_without_pages_both_entry_points():
                                      r, sm_scale(64))
         err = np.abs(out_h[b] - ref).max()
         assert err <= ATOL, (lens_list[b], err)
+
+
+def test_fused_step_equals_append_then_attend():
+    """pnmix_append_decode_attn (the cache's step) against pnmix_append_kv + pnmix_decode_attn,
+    bit for bit, from a 5-token prompt: sinks filling, residual rows, a page flush; then a
+    sequence whose residual buffer is full takes no new row."""
+    w = synth.Workload("fused", 1, 2, 8, 2, 64, 1, 1e4, 5, 5 + 200, 0.5, 64, g_V=16)
+    lc, _ = cfgs(w)
+    T = w.T
+    max_pages = (T - w.N_s) // w.N + 1
+    qp, k, v, _ = layer_inputs(w, 1, w.B, T)
+    sq = synth.pair_scales(w.H_q, w.d // 2, w.sigma_ln, "cuda", w.name, 1, "q")
+    c1 = P.PNMixLayerCache(lc, w.B, max_pages)
+    c2 = P.PNMixLayerCache(lc, w.B, max_pages)
+    for c in (c1, c2):
+        c.prefill(qp, k[:, :, :w.P].contiguous(), v[:, :, :w.P].contiguous())
+    say(f"[fused] B={w.B} P={w.P} T={T}")
+    for t in range(w.P, T):
+        qt = synth.rope_tokens(sq, w.B, torch.tensor([t], device="cuda"), w.d, w.pairing,
+                               w.rope_base, "cuda", w.name, 1, "qstep", t)[:, :, 0].contiguous()
+        kt, vt = k[:, :, t].contiguous(), v[:, :, t].contiguous()
+        o1 = c1.step(qt, kt, vt)
+        c2.append(kt, vt)
+        o2 = c2.attend(qt)
+        c2.flush()
+        assert torch.equal(o1, o2), t
+    torch.cuda.synchronize()
+    assert (c1.sink_len, c1.n_pages, c1.res_len) == (c2.sink_len, c2.n_pages, c2.res_len)
+    assert c1.n_pages == 1 and c1.sink_len == w.N_s
+    for name in ("lens", "k_sink", "v_sink", "k_res", "v_res", "k_pages", "v_pages"):
+        assert torch.equal(getattr(c1, name), getattr(c2, name)), name
+    # residual buffer full for sequence 1: no row is placed and its lengths stay
+    lens_full = c2.lens.clone()
+    lens_full[1, 2] = w.N
+    k_res0, lens_out = c2.k_res.clone(), torch.full_like(lens_full, -7)
+    kt, vt = k[:, :, 3].contiguous(), v[:, :, 3].contiguous()
+    qt = synth.rope_tokens(sq, w.B, torch.tensor([T], device="cuda"), w.d, w.pairing,
+                           w.rope_base, "cuda", w.name, 1, "qstep", T)[:, :, 0].contiguous()
+    ref = P.pnmix_decode_attn(lc, qt, c2.k_sink, c2.v_sink, c2.k_pages, c2.v_pages, c2.k_res,
+                              c2.v_res, lens_full, c2.mask, c2.sm_scale)
+    torch.cuda.synchronize()
+    out = P.pnmix_append_decode_attn(lc, qt, kt, vt, c2.k_sink, c2.v_sink, c2.k_pages,
+                                     c2.v_pages, c2.k_res, c2.v_res, lens_full, lens_out,
+                                     c2.mask, c2.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out[1], ref[1])
+    assert torch.equal(lens_out[1], lens_full[1])
+    assert torch.equal(c2.k_res[1], k_res0[1])
+    r0 = int(lens_full[0, 2])
+    assert int(lens_out[0, 2]) == r0 + 1 and torch.equal(c2.k_res[0, :, r0], kt[0])

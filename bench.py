@@ -233,7 +233,7 @@ def main():
                                      args.lens), indent=1))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence and KV head with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)

@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   PNMIX_OK = 0,
   PNMIX_E_INVALID = 1,     /* null pointer, bad size, inconsistent configuration */
-  PNMIX_E_UNSUPPORTED = 2, /* valid PN-Mix setting this build does not implement */
+  PNMIX_E_UNSUPPORTED = 2, /* valid PN-Mix setting this library does not implement */
   PNMIX_E_WORKSPACE = 3,   /* workspace smaller than the *_workspace_bytes query */
   PNMIX_E_HIP = 4          /* HIP runtime or launch error (including: no device) */
 } pnmix_status;

@@ -1086,8 +1086,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 
 // Second launch: one workgroup of 256 per (sequence, query head).  out = sum_s 2^(m_s - m) o_s /
 // sum_s 2^(m_s - m) l_s with m = max_s m_s (log2 units).  Thread (split lane sl, channel quad cq)
-// loads (m, l, o) of its splits sl, sl + SL, ... in one round (up to kMergeChunk at a time) and
-// folds them in ascending order with the online rule (m, l, o) <- (m', l 2^(m - m') +
+// loads (m, l, o) of its splits sl, sl + SL, ... CH at a time (CH = the number of splits a lane
+// has, rounded up to a power of two, at most kMergeChunk: a lane issues no loads for splits
+// that do not exist beyond that rounding) and folds them in ascending order with the online rule (m, l, o) <- (m', l 2^(m - m') +
 // l_s 2^(m_s - m'), same for o), m' = max(m, m_s); the SL lane results are folded the same way,
 // in ascending sl, through LDS.  A sequence with no tokens (every m_s = -inf) gets out = 0.
 constexpr int kMergeChunk = 8;
@@ -1104,7 +1105,7 @@ struct MergeAcc {
     m = mn;
   }
 };
-template <int D>
+template <int D, int CH>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   constexpr int Q = D / 4, SL = 256 / Q;
   __shared__ v4f red_o[256];
@@ -1121,18 +1122,18 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   const rsrc_t mlr = buf_rsrc(a.part_ml + bh * S * ng * 2, (int64_t)S * ng * 2 * 4);
   const rsrc_t por = buf_rsrc(a.part_o + bh * S * ng * D, (int64_t)S * ng * D * 4);
   MergeAcc acc{-INFINITY, 0.0f, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
-  for (int s0 = sl; s0 < S; s0 += kMergeChunk * SL) {
-    v4u ob[kMergeChunk];
-    uint32_t mb[kMergeChunk], lb[kMergeChunk];
+  for (int s0 = sl; s0 < S; s0 += CH * SL) {
+    v4u ob[CH];
+    uint32_t mb[CH], lb[CH];
 #pragma unroll
-    for (int j = 0; j < kMergeChunk; ++j) {
+    for (int j = 0; j < CH; ++j) {
       const int r = (s0 + j * SL) * ng + hh;
       ob[j] = bload16(por, (uint32_t)(4 * (r * D + 4 * cq)), 0u);
       mb[j] = __builtin_amdgcn_raw_buffer_load_b32(mlr, (uint32_t)(8 * r), 0u, 0);
       lb[j] = __builtin_amdgcn_raw_buffer_load_b32(mlr, (uint32_t)(8 * r + 4), 0u, 0);
     }
 #pragma unroll
-    for (int j = 0; j < kMergeChunk; ++j)
+    for (int j = 0; j < CH; ++j)
       if (s0 + j * SL < S)
         acc.fold(__builtin_bit_cast(float, mb[j]), __builtin_bit_cast(float, lb[j]),
                  __builtin_bit_cast(v4f, ob[j]));
@@ -1442,7 +1443,17 @@ struct Launch {
     const hipError_t e = a.table ? split_kernel<D, NT, KG, KH, true>()
                                  : split_kernel<D, NT, KG, KH, false>();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(B * c.H_q), dim3(256), 0, stream, a);
+    // loads per lane and round: the lane's split count rounded up to a power of two (<= 8)
+    const int per_lane = (a.splits + (256 / (D / 4)) - 1) / (256 / (D / 4));
+    if (per_lane <= 1)
+      hipLaunchKernelGGL((decode_merge_kernel<D, 1>), dim3(B * c.H_q), dim3(256), 0, stream, a);
+    else if (per_lane <= 2)
+      hipLaunchKernelGGL((decode_merge_kernel<D, 2>), dim3(B * c.H_q), dim3(256), 0, stream, a);
+    else if (per_lane <= 4)
+      hipLaunchKernelGGL((decode_merge_kernel<D, 4>), dim3(B * c.H_q), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<D, kMergeChunk>), dim3(B * c.H_q), dim3(256), 0,
+                         stream, a);
     return hipGetLastError();
   }
 };

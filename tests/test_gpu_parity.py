@@ -594,3 +594,22 @@ def test_fused_step_equals_append_then_attend():
     assert torch.equal(c2.k_res[1], k_res0[1])
     r0 = int(lens_full[0, 2])
     assert int(lens_out[0, 2]) == r0 + 1 and torch.equal(c2.k_res[0, :, r0], kt[0])
+
+
+def test_decode_many_splits():
+    """One long sequence of a 2-KV-head model (640 pages at d = 128): more than 64 partials per
+    (sequence, KV head), so each merge lane folds its splits in several rounds of eight loads."""
+    T = 32 + 640 * 128 + 17
+    w = synth.Workload("many-splits", 1, 1, 8, 2, 128, 1, 1e6, 141, T, 0.5, 128)
+    lc, oc = cfgs(w)
+    n_splits = P.pnmix_decode_splits(lc, 1, (T - w.N_s) // w.N)
+    say(f"[decode-many-splits] T={T} splits={n_splits}")
+    assert n_splits > 64
+    qp, k, v, qd = layer_inputs(w, 9, 1, T)
+    cache = fill_cache_bulk(w, lc, qp, k, v, T)
+    out = cache.attend(qd)
+    torch.cuda.synchronize()
+    ref = oracle_decode(w, oc, u16(qp[0]), u16(k[0]), u16(v[0]), u16(qd[0]), T, sm_scale(w.d))
+    err = np.abs(out[0].cpu().numpy() - ref).max()
+    say(f"   max|err|={err:.3e}")
+    assert err <= ATOL

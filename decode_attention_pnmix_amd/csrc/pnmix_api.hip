@@ -163,9 +163,9 @@ static pnmix_status check_decode(const pnmix_cfg* c, int32_t B, int32_t max_page
   if (max_pages > 0 && (!k_pages || !v_pages))
     return fail(PNMIX_E_INVALID, "k_pages and v_pages must be non-NULL when max_pages > 0");
   if ((long long)max_pages * c->H_kv *
-          (long long)std::max(pnmix_k_page_bytes(c), pnmix_v_page_bytes(c)) > 0xFFFFFFFFLL)
+          (long long)std::max(pnmix_k_page_bytes(c), pnmix_v_page_bytes(c)) > 0x7FFFFFFFLL)
     return fail(PNMIX_E_UNSUPPORTED,
-                "max_pages * H_kv * page bytes exceeds 4 GiB (use pnmix_decode_attn_paged)");
+                "max_pages * H_kv * page bytes exceeds 2 GiB (use pnmix_decode_attn_paged)");
   if (!std::isfinite(sm_scale)) return fail(PNMIX_E_INVALID, "sm_scale is not finite");
   const pnmix::DecodePlan plan = pnmix::decode_plan(*c, B, max_pages);
   if (plan.lds_wave > 65536)

@@ -159,7 +159,8 @@ pnmix_status pnmix_quantize_v_page(const pnmix_cfg* cfg, int32_t n_pages,
  *   k_pages [B][max_pages][H_kv][pnmix_k_page_bytes], v_pages [...][pnmix_v_page_bytes]:
  *           page p of every KV head of sequence b side by side (the pool layout of
  *           pnmix_decode_attn_paged below with block b * max_pages + p);
- *           max_pages * H_kv * page bytes must stay within 4 GiB (else PNMIX_E_UNSUPPORTED)
+ *           max_pages * H_kv * page bytes must stay below 2 GiB (one buffer resource spans a
+ *           sequence's pages; else PNMIX_E_UNSUPPORTED)
  *   k_res, v_res     [B][H_kv][N][d] fp16
  *   lens    [B] pnmix_seq_len; mask [B][H_kv][mask_words] (the rows the pages were packed with)
  *   out     [B][H_q][d] fp32: softmax(q k^T * sm_scale) v over sinks, pages (k = S q + Z with the

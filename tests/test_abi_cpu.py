@@ -118,12 +118,12 @@ def test_validation_before_launch():
                                  None) == L.PNMIX_E_INVALID
     assert lib.pnmix_decode_attn(ctypes.byref(_cfg(b_V=3)), 4, 10, *args, ctypes.c_float(0.1),
                                  FAKE, FAKE, dws, None) == L.PNMIX_E_UNSUPPORTED
-    # one sequence's contiguous pages must span at most 4 GiB (32-bit buffer offsets)
-    big = 2**32 // (8 * P.pnmix_v_page_bytes(c)) + 1
+    # one sequence's contiguous pages must span less than 2 GiB (one buffer resource)
+    big = 2**31 // (8 * P.pnmix_v_page_bytes(c)) + 1
     assert lib.pnmix_decode_attn(ctypes.byref(c), 1, big, *args, ctypes.c_float(0.088), FAKE,
                                  FAKE, P.pnmix_decode_workspace_bytes(c, 1, big),
                                  None) == L.PNMIX_E_UNSUPPORTED
-    assert "4 GiB" in P.pnmix_last_error()
+    assert "2 GiB" in P.pnmix_last_error()
 
 
 def test_paged_validation_before_launch():

@@ -49,7 +49,6 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kN = 128;  // page and residual length
-constexpr int kMaxSplits = 256;  // split-K partitions per (sequence, KV head): one merge thread each
 constexpr int kMergeSplits = 136;  // the planner's cap: beyond it the merge costs more than it saves
 constexpr int kWS = kN + 16;     // row stride of the p.V digit table (rows on distinct banks)
 constexpr float kLog2e = 1.4426950408889634f;

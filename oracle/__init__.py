@@ -238,6 +238,8 @@ def unpack_k_page(cfg: Cfg, page: np.ndarray, mask_row: np.ndarray):
 
 
 def unpack_v_page(cfg: Cfg, page: np.ndarray):
+    """codes [N][d], S and Z [N][d/g_V] of a quantized value page (b_V < 16)."""
+    assert cfg.b_V != 16, "a b_V = 16 page holds fp16 values, not codes"
     page = np.ascontiguousarray(page, dtype=np.uint8)
     codes = np.empty((cfg.N, cfg.d), np.uint8)
     S = np.empty((cfg.N, cfg.d // cfg.g_V), np.uint16)

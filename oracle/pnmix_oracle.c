@@ -85,8 +85,9 @@ int orc_check_cfg(const orc_cfg* c) {
   if (c->n_hi_pairs < 0 || c->n_hi_pairs > c->d / 2) return 1;
   if (c->N <= 0 || c->N % 16) return 1;
   if (c->G <= 0 || c->N % c->G || c->G % 8) return 1;
-  if (c->b_H != 3 || c->b_L != 1) return 1;
-  if (c->b_V != 2 || c->g_V <= 0 || c->d % c->g_V || c->g_V % 4) return 1;
+  if (c->b_L < 1 || c->b_L > 4 || c->b_H < c->b_L || c->b_H > 4) return 1;
+  if (c->b_V != 1 && c->b_V != 2 && c->b_V != 4 && c->b_V != 16) return 1;
+  if (c->g_V <= 0 || c->d % c->g_V || c->g_V % 4) return 1;
   if (c->N_s < 0) return 1;
   return 0;
 }
@@ -120,15 +121,19 @@ static int channel_salient(const orc_cfg* c, const uint32_t* mask_row, int32_t c
   return mask_bit(mask_row, pair);
 }
 
-/* K page: lo plane [N/8][d] + hi plane [N/4][n_sal] + S [N/G][d] + Z [N/G][d] (fp16) */
+/* K page: lo plane [N/8][b_L][d] + hi plane [N/8][b_H - b_L][n_sal] + S [N/G][d] + Z [N/G][d]
+ * (fp16).  With (b_H, b_L) = (3, 1) this is the LSB plane [N/8][d] and the upper-2-bit plane
+ * [N/4][n_sal] of the kernel-implementation appendix. */
 int64_t orc_k_page_bytes(const orc_cfg* c) {
   int64_t n_sal = 2 * (int64_t)c->n_hi_pairs;
-  return (int64_t)c->N * c->d / 8 + (int64_t)c->N * n_sal / 4 +
+  return (int64_t)c->N * c->d * c->b_L / 8 + (int64_t)c->N * n_sal * (c->b_H - c->b_L) / 8 +
          2 * 2 * (int64_t)(c->N / c->G) * c->d;
 }
 
-/* V page: codes [d/4][N] + S [d/g_V][N] + Z [d/g_V][N] (fp16) */
+/* V page: codes [d b_V / 8][N] + S [d/g_V][N] + Z [d/g_V][N] (fp16); with b_V = 16 (values
+ * kept in full precision) the page is the fp16 rows [N][d] themselves. */
 int64_t orc_v_page_bytes(const orc_cfg* c) {
+  if (c->b_V == 16) return 2 * (int64_t)c->N * c->d;
   return (int64_t)c->N * c->d * c->b_V / 8 + 2 * 2 * (int64_t)c->N * (c->d / c->g_V);
 }
 
@@ -284,28 +289,59 @@ static void put_f16(uint8_t* p, uint16_t v) {
 
 static uint16_t get_f16(const uint8_t* p) { return (uint16_t)(p[0] | ((uint16_t)p[1] << 8)); }
 
+/* Token bit plane of width w bits ([PNMIX] kernel-implementation appendix: the LSB of a key
+ * channel is packed 8 consecutive tokens per byte, its upper 2 bits 4 consecutive tokens per
+ * byte).  Generalised to any width w: the w-bit fields of 8 consecutive tokens 8j..8j+7 of one
+ * column form an 8w-bit little-endian stream (token 8j+k at bits wk..wk+w-1), stored as w bytes
+ * [j][0..w-1] of that column; plane bytes are arranged [N/8][w][ncols].  For w = 1 this is the
+ * LSB byte of 8 tokens, for w = 2 two bytes of 4 tokens each. */
+static void plane_put(uint8_t* plane, int32_t ncols, int32_t w, int32_t col, int32_t t,
+                      uint32_t field) {
+  int32_t j = t / 8, k = t % 8;
+  for (int32_t bit = 0; bit < w; ++bit) {
+    int32_t pos = w * k + bit; /* position in the 8w-bit stream */
+    if ((field >> bit) & 1u)
+      plane[((int64_t)j * w + pos / 8) * ncols + col] |= (uint8_t)(1u << (pos % 8));
+  }
+}
+
+static uint32_t plane_get(const uint8_t* plane, int32_t ncols, int32_t w, int32_t col,
+                          int32_t t) {
+  int32_t j = t / 8, k = t % 8;
+  uint32_t field = 0;
+  for (int32_t bit = 0; bit < w; ++bit) {
+    int32_t pos = w * k + bit;
+    field |= (uint32_t)((plane[((int64_t)j * w + pos / 8) * ncols + col] >> (pos % 8)) & 1u)
+             << bit;
+  }
+  return field;
+}
+
 /* K page ([PNMIX] kernel-implementation appendix; [REPRO] H3/L1 packing; [SUMMARY]):
  * keys are quantized per channel over token groups of G; channels of salient pairs use
- * b_H = 3 bits, the rest b_L = 1 bit with Eq. 7.  The least significant bit of every
- * channel goes to the lo plane, 8 consecutive tokens of one channel per byte:
- *     lo[j][c] bit k = q(8j + k, c) & 1                       ([N/8][d] bytes)
- * the upper two bits of salient channels go to the hi plane, 4 consecutive tokens of one
- * channel per byte, salient channels in ascending channel order (rank r):
- *     hi[j][r] bits 2k..2k+1 = q(4j + k, sal(r)) >> 1          ([N/4][n_sal] bytes)
- * then S[g][c] and Z[g][c] as little-endian fp16 ([N/G][d] each). */
+ * b_H bits, the rest b_L bits (Eq. 7 for any 1-bit group).  The low b_L bits of every
+ * channel's code go to the lo plane (width b_L, all d channels); the upper b_H - b_L bits of
+ * the salient channels go to the hi plane (width b_H - b_L, n_sal columns, salient channels in
+ * ascending channel order = rank r):
+ *     lo [N/8][b_L][d]            field of (t, c) = q(t, c) & (2^b_L - 1)
+ *     hi [N/8][b_H - b_L][n_sal]  field of (t, r) = q(t, sal(r)) >> b_L
+ * then S[g][c] and Z[g][c] as little-endian fp16 ([N/G][d] each).  With (b_H, b_L) = (3, 1):
+ * lo byte [j][c] bit k = q(8j + k, c) & 1 and hi byte [j][r] bits 2k..2k+1 = q(4j + k, sal(r))
+ * >> 1, the appendix's two planes. */
 int orc_quantize_k_page(const orc_cfg* c, const uint16_t* src, int64_t src_row_stride,
                         const uint32_t* mask_row, uint8_t* dst) {
   if (orc_check_cfg(c) || !src || !mask_row || !dst) return 1;
   const int32_t N = c->N, d = c->d, G = c->G, ngr = N / G;
   const int32_t n_sal = 2 * c->n_hi_pairs;
+  const int32_t wL = c->b_L, wH = c->b_H - c->b_L;
   int32_t cnt = 0;
   for (int32_t ch = 0; ch < d; ++ch) cnt += channel_salient(c, mask_row, ch);
   if (cnt != n_sal) return 1; /* mask popcount must equal n_hi_pairs */
   uint8_t* codes = (uint8_t*)malloc((size_t)N * d);
   if (!codes) return 1;
   uint8_t* lo = dst;
-  uint8_t* hi = dst + (int64_t)N * d / 8;
-  uint8_t* Sp = hi + (int64_t)N * n_sal / 4;
+  uint8_t* hi = dst + (int64_t)N * d * wL / 8;
+  uint8_t* Sp = hi + (int64_t)N * n_sal * wH / 8;
   uint8_t* Zp = Sp + 2 * (int64_t)ngr * d;
   for (int32_t g = 0; g < ngr; ++g) {
     for (int32_t ch = 0; ch < d; ++ch) {
@@ -316,50 +352,59 @@ int orc_quantize_k_page(const orc_cfg* c, const uint16_t* src, int64_t src_row_s
       put_f16(Zp + 2 * ((int64_t)g * d + ch), m.Z);
     }
   }
-  memset(lo, 0, (size_t)N * d / 8);
-  memset(hi, 0, (size_t)N * n_sal / 4);
+  memset(lo, 0, (size_t)N * d * wL / 8);
+  memset(hi, 0, (size_t)N * n_sal * wH / 8);
   for (int32_t t = 0; t < N; ++t)
     for (int32_t ch = 0; ch < d; ++ch)
-      lo[(t / 8) * d + ch] |= (uint8_t)((codes[t * d + ch] & 1u) << (t % 8));
-  int32_t r = 0;
-  for (int32_t ch = 0; ch < d; ++ch) {
-    if (!channel_salient(c, mask_row, ch)) continue;
-    for (int32_t t = 0; t < N; ++t)
-      hi[(t / 4) * n_sal + r] |= (uint8_t)(((codes[t * d + ch] >> 1) & 3u) << (2 * (t % 4)));
-    r++;
+      plane_put(lo, d, wL, ch, t, codes[t * d + ch] & ((1u << wL) - 1u));
+  if (wH > 0) {
+    int32_t r = 0;
+    for (int32_t ch = 0; ch < d; ++ch) {
+      if (!channel_salient(c, mask_row, ch)) continue;
+      for (int32_t t = 0; t < N; ++t) plane_put(hi, n_sal, wH, r, t, (uint32_t)codes[t * d + ch] >> wL);
+      r++;
+    }
   }
   free(codes);
   return 0;
 }
 
 /* V page ([PNMIX] sec. 2 and kernel-implementation appendix; [SUMMARY]): values are
- * quantized per token over channel groups of g_V at b_V = 2 bits (Eq. 2, constant rule);
- * 4 channels of one token share a byte.  This library's byte holds the channels a quarter
- * of the head apart: byte [j][t] (j < d/4, bytes arranged [d/4][N]) carries channel
- * j + u d/4 of token t in bits 2u..2u+1.  Then S[g][t], Z[g][t] as little-endian fp16
- * ([d/g_V][N] each, group-major). */
+ * quantized per token over channel groups of g_V at b_V bits (Eq. 2, Eq. 7 for b_V = 1, the
+ * constant rule).  Consecutive channels of one token share a byte, as the appendix packs
+ * 4 consecutive channel values of a token into one byte at b_V = 2: byte [m][t] holds the
+ * channels e m .. e m + e - 1 of token t, e = 8 / b_V, channel e m + u in bits
+ * b_V u .. b_V u + b_V - 1.  Bytes are arranged [d b_V / 8][N] (the N tokens of one byte
+ * column contiguous), then S[g][t], Z[g][t] as little-endian fp16 ([d/g_V][N] each,
+ * group-major).  With b_V = 16 the values stay fp16 and the page is the rows [N][d]. */
 int orc_quantize_v_page(const orc_cfg* c, const uint16_t* src, int64_t src_row_stride,
                         uint8_t* dst) {
   if (orc_check_cfg(c) || !src || !dst) return 1;
-  const int32_t N = c->N, d = c->d, ng = d / c->g_V;
+  const int32_t N = c->N, d = c->d, ng = d / c->g_V, bV = c->b_V;
+  if (bV == 16) {
+    for (int32_t t = 0; t < N; ++t)
+      for (int32_t ch = 0; ch < d; ++ch)
+        put_f16(dst + 2 * ((int64_t)t * d + ch), src[(int64_t)t * src_row_stride + ch]);
+    return 0;
+  }
+  const int32_t e = 8 / bV; /* channels per byte */
   uint8_t* codes = (uint8_t*)malloc((size_t)N * d);
   if (!codes) return 1;
   uint8_t* cb = dst;
-  uint8_t* Sp = dst + (int64_t)N * d / 4;
+  uint8_t* Sp = dst + (int64_t)N * d * bV / 8;
   uint8_t* Zp = Sp + 2 * (int64_t)N * ng;
   for (int32_t t = 0; t < N; ++t) {
     for (int32_t g = 0; g < ng; ++g) {
       group_meta m = quantize_group(src + (int64_t)t * src_row_stride + g * c->g_V, 1, c->g_V,
-                                    c->b_V, codes + (int64_t)t * d + g * c->g_V, 1);
+                                    bV, codes + (int64_t)t * d + g * c->g_V, 1);
       put_f16(Sp + 2 * ((int64_t)g * N + t), m.S);
       put_f16(Zp + 2 * ((int64_t)g * N + t), m.Z);
     }
   }
-  memset(cb, 0, (size_t)N * d / 4);
+  memset(cb, 0, (size_t)N * d * bV / 8);
   for (int32_t t = 0; t < N; ++t)
     for (int32_t ch = 0; ch < d; ++ch)
-      cb[(int64_t)(ch % (d / 4)) * N + t] |=
-          (uint8_t)((codes[t * d + ch] & 3u) << (2 * (ch / (d / 4))));
+      cb[(int64_t)(ch / e) * N + t] |= (uint8_t)(codes[t * d + ch] << (bV * (ch % e)));
   free(codes);
   return 0;
 }
@@ -373,21 +418,22 @@ int orc_unpack_k_page(const orc_cfg* c, const uint8_t* page, const uint32_t* mas
   if (orc_check_cfg(c) || !page || !mask_row) return 1;
   const int32_t N = c->N, d = c->d, ngr = N / c->G;
   const int32_t n_sal = 2 * c->n_hi_pairs;
+  const int32_t wL = c->b_L, wH = c->b_H - c->b_L;
   const uint8_t* lo = page;
-  const uint8_t* hi = page + (int64_t)N * d / 8;
-  const uint8_t* Sp = hi + (int64_t)N * n_sal / 4;
+  const uint8_t* hi = page + (int64_t)N * d * wL / 8;
+  const uint8_t* Sp = hi + (int64_t)N * n_sal * wH / 8;
   const uint8_t* Zp = Sp + 2 * (int64_t)ngr * d;
   if (codes) {
     for (int32_t t = 0; t < N; ++t)
-      for (int32_t ch = 0; ch < d; ++ch)
-        codes[t * d + ch] = (uint8_t)((lo[(t / 8) * d + ch] >> (t % 8)) & 1u);
-    int32_t r = 0;
-    for (int32_t ch = 0; ch < d; ++ch) {
-      if (!channel_salient(c, mask_row, ch)) continue;
-      for (int32_t t = 0; t < N; ++t)
-        codes[t * d + ch] |=
-            (uint8_t)(((hi[(t / 4) * n_sal + r] >> (2 * (t % 4))) & 3u) << 1);
-      r++;
+      for (int32_t ch = 0; ch < d; ++ch) codes[t * d + ch] = (uint8_t)plane_get(lo, d, wL, ch, t);
+    if (wH > 0) {
+      int32_t r = 0;
+      for (int32_t ch = 0; ch < d; ++ch) {
+        if (!channel_salient(c, mask_row, ch)) continue;
+        for (int32_t t = 0; t < N; ++t)
+          codes[t * d + ch] |= (uint8_t)(plane_get(hi, n_sal, wH, r, t) << wL);
+        r++;
+      }
     }
   }
   for (int32_t i = 0; i < ngr * d; ++i) {
@@ -397,18 +443,19 @@ int orc_unpack_k_page(const orc_cfg* c, const uint8_t* page, const uint32_t* mas
   return 0;
 }
 
+/* b_V < 16 only (a b_V = 16 page holds no codes) */
 int orc_unpack_v_page(const orc_cfg* c, const uint8_t* page, uint8_t* codes, uint16_t* S,
                       uint16_t* Z) {
-  if (orc_check_cfg(c) || !page) return 1;
-  const int32_t N = c->N, d = c->d, ng = d / c->g_V;
+  if (orc_check_cfg(c) || !page || c->b_V == 16) return 1;
+  const int32_t N = c->N, d = c->d, ng = d / c->g_V, bV = c->b_V, e = 8 / bV;
   const uint8_t* cb = page;
-  const uint8_t* Sp = page + (int64_t)N * d / 4;
+  const uint8_t* Sp = page + (int64_t)N * d * bV / 8;
   const uint8_t* Zp = Sp + 2 * (int64_t)N * ng;
   if (codes)
     for (int32_t t = 0; t < N; ++t)
       for (int32_t ch = 0; ch < d; ++ch)
         codes[t * d + ch] =
-            (uint8_t)((cb[(int64_t)(ch % (d / 4)) * N + t] >> (2 * (ch / (d / 4)))) & 3u);
+            (uint8_t)((cb[(int64_t)(ch / e) * N + t] >> (bV * (ch % e))) & ((1u << bV) - 1u));
   /* S, Z are returned per token, [N][d/g_V], from the group-major storage */
   for (int32_t t = 0; t < N; ++t)
     for (int32_t g = 0; g < ng; ++g) {
@@ -421,6 +468,7 @@ int orc_unpack_v_page(const orc_cfg* c, const uint8_t* page, uint8_t* codes, uin
 /* reconstruction x = s q + z of Eq. 2 with the stored fp16 metadata, in float64 */
 int orc_dequant_k_page(const orc_cfg* c, const uint8_t* page, const uint32_t* mask_row,
                        double* out) {
+  if (orc_check_cfg(c) || !page || !mask_row || !out) return 1;
   const int32_t N = c->N, d = c->d, G = c->G, ngr = N / G;
   uint8_t* codes = (uint8_t*)malloc((size_t)N * d);
   uint16_t* S = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)ngr * d);
@@ -440,7 +488,12 @@ int orc_dequant_k_page(const orc_cfg* c, const uint8_t* page, const uint32_t* ma
 }
 
 int orc_dequant_v_page(const orc_cfg* c, const uint8_t* page, double* out) {
+  if (orc_check_cfg(c) || !page || !out) return 1;
   const int32_t N = c->N, d = c->d, ng = d / c->g_V;
+  if (c->b_V == 16) {
+    for (int64_t i = 0; i < (int64_t)N * d; ++i) out[i] = (double)orc_h2f(get_f16(page + 2 * i));
+    return 0;
+  }
   uint8_t* codes = (uint8_t*)malloc((size_t)N * d);
   uint16_t* S = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)N * ng);
   uint16_t* Z = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)N * ng);

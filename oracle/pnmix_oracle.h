@@ -26,10 +26,15 @@
  *     ascending token order inside a chunk, chunk sums added in ascending chunk order,
  *     mean = sum / (float)P; sigma = ((sum over the group's query heads, ascending) /
  *     (float)n_g) * key_mean; top-n_hi pairs by sigma, ties to the lower pair index.
- *   - quantization: exact min and max (canonicalised: -0 -> +0); s = (mx - mn) / L;
+ *   - quantization: exact min and max (canonicalised: -0 -> +0); L = 2^b - 1 with b = b_H
+ *     for channels of masked pairs, b_L for the others, b_V for values; s = (mx - mn) / L;
  *     inv = 1 / s (one IEEE reciprocal per group); q = clamp(rne((x - mn) * inv), 0, L);
  *     L = 1 groups store Eq. 7 metadata h((mx - mn) * 0.5f), h((3 mn + mx) * 0.25f);
  *     other groups store h(s), h(mn); constant groups store (+0, h(mn)) and codes 0.
+ *   - packing: key codes split into a low plane (b_L bits of every channel) and a high plane
+ *     (the b_H - b_L upper bits of the salient channels), each packing 8 consecutive tokens of
+ *     a channel into as many bytes as the plane is wide; value codes packed 8 / b_V
+ *     consecutive channels of one token per byte.
  *   - decode: float64 softmax attention over the dequantized cache (k = S * q + Z with the
  *     stored fp16 S and Z), token order sinks, pages, residual.
  *
@@ -47,8 +52,8 @@ extern "C" {
 typedef struct {
   int32_t H_q, H_kv, d, pairing; /* pairing 0: (2i, 2i+1); 1: (i, i + d/2) */
   int32_t n_hi_pairs;            /* floor(r * d / 2) pairs kept at b_H bits */
-  int32_t G, b_H, b_L;           /* key token group, (3, 1) */
-  int32_t b_V, g_V;              /* value bits (2) and channel group */
+  int32_t G, b_H, b_L;           /* key token group; 1 <= b_L <= b_H <= 4 */
+  int32_t b_V, g_V;              /* value bits (1, 2, 4, or 16 = fp16 kept) and channel group */
   int32_t N_s, N;                /* sink count and page / residual length */
 } orc_cfg;
 
@@ -84,13 +89,14 @@ int orc_quantize_v_page(const orc_cfg* c, const uint16_t* src, int64_t src_row_s
                         uint8_t* dst);
 
 /* unpack a page: codes [N][d] (one code per byte), S and Z fp16 bits.
- * K: S, Z [N/G][d].  V: S, Z [N][d/g_V]. */
+ * K: S, Z [N/G][d].  V: S, Z [N][d/g_V] (b_V < 16 only). */
 int orc_unpack_k_page(const orc_cfg* c, const uint8_t* page, const uint32_t* mask_row,
                       uint8_t* codes, uint16_t* S, uint16_t* Z);
 int orc_unpack_v_page(const orc_cfg* c, const uint8_t* page, uint8_t* codes, uint16_t* S,
                       uint16_t* Z);
 
-/* dequantize a page to float64 [N][d]: x = S * q + Z with the stored fp16 S, Z */
+/* dequantize a page to float64 [N][d]: x = S * q + Z with the stored fp16 S, Z (a b_V = 16
+ * value page: the fp16 values) */
 int orc_dequant_k_page(const orc_cfg* c, const uint8_t* page, const uint32_t* mask_row,
                        double* out);
 int orc_dequant_v_page(const orc_cfg* c, const uint8_t* page, double* out);

@@ -62,6 +62,59 @@ def test_golden_v_page(orc):
                                                 Z.reshape(-1).view(np.uint8)]))
 
 
+@pytest.mark.parametrize("name", ["k_h4_l2", "k_h4_l3"])
+def test_golden_k_page_general_widths(orc, name):
+    kv = json.load(open(GOLDEN))["general_widths"][name]
+    cfg = orc.Cfg(**kv["cfg"])
+    src = np.zeros((cfg.N, cfg.d), np.float16)
+    for ch, vals in kv["values"].items():
+        src[:, int(ch)] = vals
+    mask = np.array(kv["mask_row"], np.uint32)
+    page = orc.quantize_k_page(cfg, src.view(np.uint16), mask)
+    want = np.concatenate([_hexbytes(kv["lo_hex"]), _hexbytes(kv["hi_hex"]),
+                           _hexf16(kv["S_f16_hex"]).view(np.uint8),
+                           _hexf16(kv["Z_f16_hex"]).view(np.uint8)])
+    assert page.size == orc.k_page_bytes(cfg) == want.size
+    assert np.array_equal(page, want)
+    codes, _, _ = orc.unpack_k_page(cfg, page, mask)
+    assert np.array_equal(codes[:, 0], np.arange(16))  # channel 0 holds t, s = 1, z = 0
+
+
+def _token_rows(spec, N):
+    even, odd = (json.loads(spec[k]) for k in ("even", "odd"))
+    return np.array([even if t % 2 == 0 else odd for t in range(N)], np.float16)
+
+
+@pytest.mark.parametrize("name", ["v_b4", "v_b1"])
+def test_golden_v_page_general_widths(orc, name):
+    vv = json.load(open(GOLDEN))["general_widths"][name]
+    cfg = orc.Cfg(**vv["cfg"])
+    src = _token_rows(vv["token_values"], cfg.N)
+    page = orc.quantize_v_page(cfg, src.view(np.uint16))
+    ng = cfg.d // cfg.g_V
+    S = np.zeros((ng, cfg.N), np.uint16)
+    Z = np.zeros((ng, cfg.N), np.uint16)
+    for t in range(cfg.N):
+        par = "even" if t % 2 == 0 else "odd"
+        S[:, t] = _hexf16([vv["S_f16_hex_per_token"][par]])
+        Z[:, t] = _hexf16([vv["Z_f16_hex_per_token"][par]])
+    want = np.concatenate([_hexbytes(vv["codes_hex"]), S.reshape(-1).view(np.uint8),
+                           Z.reshape(-1).view(np.uint8)])
+    assert page.size == orc.v_page_bytes(cfg) == want.size
+    assert np.array_equal(page, want)
+
+
+def test_v_page_b16_keeps_fp16_rows(orc):
+    """b_V = 16 (the value cache the bit-width sweep keeps in full precision): the page is the
+    token rows themselves and dequantizes to them exactly."""
+    cfg = orc.Cfg(H_q=1, H_kv=1, d=32, pairing=0, n_hi_pairs=8, b_V=16)
+    x = torch.randn(128, 32, generator=torch.Generator().manual_seed(2)).to(torch.float16).numpy()
+    page = orc.quantize_v_page(cfg, x.view(np.uint16))
+    assert page.size == 128 * 32 * 2 == orc.v_page_bytes(cfg)
+    assert np.array_equal(page.view(np.uint16).reshape(128, 32), x.view(np.uint16))
+    assert np.array_equal(orc.dequant_v_page(cfg, page), x.astype(np.float64))
+
+
 def _page(cfg, seed, sigma_ln=1.0, const_channels=(), signed_zero=False):
     sc = synth.pair_scales(1, cfg.d // 2, sigma_ln, "cpu", "oracle-quant", seed)
     x = synth.rope_tokens(sc, 1, torch.arange(cfg.N) + 1000, cfg.d, cfg.pairing, 1e4, "cpu",
@@ -94,17 +147,23 @@ def _salient(cfg, orc, mask):
     return s
 
 
-@pytest.mark.parametrize("pairing,G,r", [(0, 128, 0.5), (1, 128, 0.5), (1, 64, 0.4),
-                                          (1, 32, 0.25), (0, 128, 1.0), (1, 64, 0.0)])
-def test_k_page_levels(orc, pairing, G, r):
+@pytest.mark.parametrize("pairing,G,r,bH,bL", [
+    (0, 128, 0.5, 3, 1), (1, 128, 0.5, 3, 1), (1, 64, 0.4, 3, 1), (1, 32, 0.25, 3, 1),
+    (0, 128, 1.0, 3, 1), (1, 64, 0.0, 3, 1),
+    # the bit-width sweep: b_H, b_L in {4, 3, 2, 1}, b_H >= b_L
+    (1, 128, 0.3, 4, 2), (0, 64, 0.6, 4, 1), (1, 128, 0.5, 2, 1), (1, 64, 0.2, 4, 3),
+    (0, 128, 0.5, 2, 2), (1, 128, 0.7, 4, 4), (1, 64, 0.5, 1, 1), (0, 32, 0.9, 3, 2)])
+def test_k_page_levels(orc, pairing, G, r, bH, bL):
     d = 128
-    cfg = orc.Cfg(H_q=1, H_kv=1, d=d, pairing=pairing, n_hi_pairs=orc.hi_pairs(r, d), G=G)
+    cfg = orc.Cfg(H_q=1, H_kv=1, d=d, pairing=pairing, n_hi_pairs=orc.hi_pairs(r, d), G=G,
+                  b_H=bH, b_L=bL)
     rng = np.random.default_rng(int(r * 100) + G)
     pairs = sorted(rng.choice(d // 2, cfg.n_hi_pairs, replace=False).tolist())
     mask = _mask_for(cfg, pairs)
     x = _page(cfg, seed=G + pairing, const_channels=(5, 77), signed_zero=True)
     page = orc.quantize_k_page(cfg, x.view(np.uint16), mask)
-    assert page.size == cfg.N * d // 8 + cfg.N * cfg.n_sal // 4 + 4 * (cfg.N // G) * d
+    assert page.size == (cfg.N * d * bL // 8 + cfg.N * cfg.n_sal * (bH - bL) // 8 +
+                         4 * (cfg.N // G) * d)
     codes, S, Z = orc.unpack_k_page(cfg, page, mask)
     sal = _salient(cfg, orc, mask)
     assert sal.sum() == cfg.n_sal
@@ -124,7 +183,7 @@ def test_k_page_levels(orc, pairing, G, r):
                 assert S[g, c] == 0 and np.all(q == 0)
                 assert Zg == mn and np.all(Sg * q + Zg == v)
                 continue
-            L = 7 if sal[c] else 1
+            L = 2 ** (bH if sal[c] else bL) - 1
             assert q.max() <= L
             levels = mn + np.arange(L + 1) * (mx - mn) / L
             # Eq. 2: the code is the nearest of the 2^b levels (fp64 reference levels); a
@@ -204,15 +263,16 @@ def test_k_rejects_wrong_popcount(orc):
         orc.quantize_k_page(cfg, x, np.array([0b111], np.uint32))
 
 
-@pytest.mark.parametrize("g_V", [32, 16])
-def test_v_page_levels(orc, g_V):
+@pytest.mark.parametrize("g_V,bV", [(32, 2), (16, 2), (32, 4), (16, 4), (64, 1), (128, 1)])
+def test_v_page_levels(orc, g_V, bV):
     d = 128
-    cfg = orc.Cfg(H_q=1, H_kv=1, d=d, pairing=1, n_hi_pairs=32, g_V=g_V)
-    g = torch.Generator().manual_seed(5)
+    cfg = orc.Cfg(H_q=1, H_kv=1, d=d, pairing=1, n_hi_pairs=32, g_V=g_V, b_V=bV)
+    L = 2 ** bV - 1
+    g = torch.Generator().manual_seed(5 + bV)
     x = torch.randn(128, d, generator=g).to(torch.float16).numpy()
     x[3, :g_V] = 1.5  # a constant group
     page = orc.quantize_v_page(cfg, x.view(np.uint16))
-    assert page.size == 128 * d // 4 + 4 * 128 * (d // g_V)
+    assert page.size == 128 * d * bV // 8 + 4 * 128 * (d // g_V)
     codes, S, Z = orc.unpack_v_page(cfg, page)
     xf = x.astype(np.float64)
     for t in range(128):
@@ -225,15 +285,20 @@ def test_v_page_levels(orc, g_V):
             if mn == mx:
                 assert S[t, gi] == 0 and np.all(q == 0) and Zg == mn
                 continue
-            assert Zg == mn
-            levels = mn + np.arange(4) * (mx - mn) / 3
+            assert q.max() <= L
+            levels = mn + np.arange(L + 1) * (mx - mn) / L
             dist = np.abs(v[:, None] - levels[None, :])
             best = dist.argmin(axis=1)
             amb = np.abs(dist[np.arange(g_V), best] - dist[np.arange(g_V), q]) <= 4e-7 * (mx - mn)
             assert np.all((q == best) | amb)
-            s32 = (np.float32(mx) - np.float32(mn)) / np.float32(3)
-            assert Sg == float(np.float16(s32))
+            s32 = (np.float32(mx) - np.float32(mn)) / np.float32(L)
             assert np.all(np.abs(v - (float(s32) * q + mn)) <= float(s32) / 2 * (1 + 1e-6))
+            if L == 1:  # Eq. 7 metadata for a 1-bit value group
+                assert Sg == float(np.float16((mx - mn) / 2))
+                assert Zg == float(np.float16((3 * mn + mx) / 4))
+                assert np.all((q == 1) == (v > (mn + mx) / 2))
+            else:
+                assert Zg == mn and Sg == float(np.float16(s32))
 
 
 def test_page_sizes_and_printed_average_bits(orc):

@@ -144,7 +144,8 @@ def cpu_baseline(w, sample, seconds, threads):
     import numpy as np
     import oracle
     oracle.build(force=False)
-    oc = oracle.Cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_V=w.b_V, g_V=w.g_V,
+    oc = oracle.Cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_H=w.b_H, b_L=w.b_L,
+                    b_V=w.b_V, g_V=w.g_V,
                     N_s=w.N_s, N=w.N)
     sm = float(np.float32(1.0 / math.sqrt(w.d)))
     prepared = []
@@ -249,7 +250,8 @@ def main():
         sys.exit(1)
     dev = "cuda"
     w = synth.WORKLOADS[args.workload]
-    cfg = P.make_cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_V=w.b_V, g_V=w.g_V,
+    cfg = P.make_cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_H=w.b_H, b_L=w.b_L,
+                    b_V=w.b_V, g_V=w.g_V,
                      N_s=w.N_s, N=w.N)
     kpb, vpb = P.pnmix_k_page_bytes(cfg), P.pnmix_v_page_bytes(cfg)
     W, K = args.warmup, args.steps

@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
                                                                      P]),
         "pnmix_append_kv": (st, [cp, i32, P, P, P, P, P, P, P, P]),
         "pnmix_commit_page": (st, [cp, i32, i32, P, P]),
+        "pnmix_dequant_k_pages": (st, [cp, i32, P, P, P, P]),
+        "pnmix_dequant_v_pages": (st, [cp, i32, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -87,7 +89,7 @@ EXPORTED = ("pnmix_check_cfg", "pnmix_hi_pairs", "pnmix_mask_words", "pnmix_k_pa
             "pnmix_decode_workspace_bytes", "pnmix_last_error", "pnmix_score_prefill",
             "pnmix_quantize_k_page", "pnmix_quantize_v_page", "pnmix_decode_attn",
             "pnmix_append_kv", "pnmix_commit_page", "pnmix_decode_attn_paged",
-            "pnmix_append_decode_attn")
+            "pnmix_append_decode_attn", "pnmix_dequant_k_pages", "pnmix_dequant_v_pages")
 
 
 def _check(status: int):
@@ -208,7 +210,7 @@ def pnmix_quantize_v_page(cfg, jobs: torch.Tensor, stream=None) -> None:
 def pnmix_decode_attn(cfg, q, k_sink, v_sink, k_pages, v_pages, k_res, v_res, lens, mask,
                       sm_scale: float, out: torch.Tensor | None = None,
                       ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """q [B][H_q][d] fp16; sinks [B][H_kv][N_s][d]; pages [B][H_kv][max_pages][bytes] u8;
+    """q [B][H_q][d] fp16; sinks [B][H_kv][N_s][d]; pages [B][max_pages][H_kv][bytes] u8;
     residual [B][H_kv][N][d]; lens [B][4] int32 (sink_len, n_pages, res_len, 0);
     mask [B][H_kv][words] -> out [B][H_q][d] f32.  ws, when given, is a device byte buffer of
     at least pnmix_decode_workspace_bytes(...) bytes that holds the split-K partials."""
@@ -313,6 +315,34 @@ def pnmix_append_kv(cfg, k_new, v_new, k_sink, v_sink, k_res, v_res, lens, strea
     _check(lib().pnmix_append_kv(ctypes.byref(cfg), B, _ptr(k_new), _ptr(v_new), _ptr(k_sink),
                                  _ptr(v_sink), _ptr(k_res), _ptr(v_res), _ptr(lens),
                                  _stream(stream)))
+
+
+def pnmix_dequant_k_pages(cfg, pages: torch.Tensor, mask: torch.Tensor,
+                          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """pages [n][k page bytes] u8, mask [n][words] (the row each page was packed with) ->
+    out [n][N][d] f32, x = S code + Z (analysis; decode never forms it)."""
+    n = pages.shape[0]
+    _expect(pages, (n, pnmix_k_page_bytes(cfg)), _U8, "pages")
+    _expect(mask, (n, pnmix_mask_words(cfg)), _U32, "mask")
+    if out is None:
+        out = torch.empty(n, cfg.N, cfg.d, dtype=torch.float32, device=pages.device)
+    _expect(out, (n, cfg.N, cfg.d), (torch.float32,), "out")
+    _check(lib().pnmix_dequant_k_pages(ctypes.byref(cfg), n, _ptr(pages), _ptr(mask), _ptr(out),
+                                       _stream(stream)))
+    return out
+
+
+def pnmix_dequant_v_pages(cfg, pages: torch.Tensor, out: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """pages [n][v page bytes] u8 -> out [n][N][d] f32 (analysis)."""
+    n = pages.shape[0]
+    _expect(pages, (n, pnmix_v_page_bytes(cfg)), _U8, "pages")
+    if out is None:
+        out = torch.empty(n, cfg.N, cfg.d, dtype=torch.float32, device=pages.device)
+    _expect(out, (n, cfg.N, cfg.d), (torch.float32,), "out")
+    _check(lib().pnmix_dequant_v_pages(ctypes.byref(cfg), n, _ptr(pages), _ptr(out),
+                                       _stream(stream)))
+    return out
 
 
 def pnmix_commit_page(cfg, max_pages: int, lens, stream=None) -> None:

@@ -53,4 +53,17 @@ __device__ __forceinline__ int salient_rank(const uint32_t* row, int c, int d, i
   return r < 2 * n_hi ? r : -1;
 }
 
+// Field of token t in a key bit plane of width w ([N/8][w][ncols] bytes): the w-bit fields of
+// tokens 8j..8j+7 of one column form an 8w-bit little-endian stream, token 8j+k at bits
+// wk..wk+w-1, stored as the w bytes [j][0..w-1] of that column (w = 1: the LSB byte of 8
+// tokens; w = 2: two bytes of 4 tokens each, the PN-Mix kernel-implementation appendix).
+__device__ __forceinline__ uint32_t plane_field(const uint8_t* plane, int ncols, int w, int col,
+                                                int t) {
+  const int j = t >> 3, pos = w * (t & 7), i0 = pos >> 3;
+  const uint8_t* p = plane + (int64_t)(j * w + i0) * ncols + col;
+  uint32_t v = p[0];
+  if (i0 + 1 < w) v |= (uint32_t)p[ncols] << 8;
+  return (v >> (pos & 7)) & ((1u << w) - 1u);
+}
+
 }  // namespace pnmix

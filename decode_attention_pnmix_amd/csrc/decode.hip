@@ -28,17 +28,21 @@
 //   each channel's salient rank.  Integer accumulation is exact; the four digit partials of a
 //   key sit in one lane and are combined in fp32.
 // * p.V runs on the int8 matrix cores too.  w = p S_tg per (head, key, value group) becomes
-//   fixed point below 2^23 with a per-head power-of-two scale set from that head's largest p on
+//   fixed point below 2^22 with a per-head power-of-two scale set from that head's largest p on
 //   the page times the page's largest value scale (so the result does not depend on how pages
 //   are split); its three base-256 digits go to an LDS table whose rows are (head, digit), plus
 //   one row of ones per head whose product is the column sum of the codes (it restores the
 //   offset of the two lower digits, stored as u - 128).  The B operand is again the packed value
-//   byte masked in place: a byte holds channels j, j + d/4, j + d/2, j + 3d/4 of one token, so
-//   one 2-bit field of 16 consecutive bytes is 16 consecutive channels of one value group.
+//   byte masked in place.  A byte holds 4 consecutive channels of one token (byte column m =
+//   channels 4m..4m+3, the N tokens of a column contiguous), so a tile takes 8 byte columns
+//   (32 channels, inside one value group of g_V >= 32) and two of their four 2-bit fields:
+//   column n < 8 reads byte column n with field f, column n >= 8 byte column n - 8 with field
+//   f + 2.  The 16 bytes a lane loads for its column serve two tiles (f = 0 and f = 1).
 // * The Z terms and the softmax bookkeeping run on the vector ALU in fp32.
 #include <algorithm>
 
 #include "common.h"
+#include "decode_args.h"
 #include "kernels.h"
 
 namespace pnmix {
@@ -48,44 +52,11 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kN = 128;  // page and residual length
 constexpr int kMergeSplits = 136;  // the planner's cap: beyond it the merge costs more than it saves
 constexpr int kWS = kN + 16;     // row stride of the p.V digit table (rows on distinct banks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTwo23 = 8388608.0f;  // y + 2^23 rounds y in [0, 2^23) to an integer (RNE)
 
-struct DecodeArgs {
-  const uint16_t* q;
-  const uint16_t* k_sink;
-  const uint16_t* v_sink;
-  const uint8_t* k_pages;  // [B][max_pages][H_kv][kpb], or with a block table the pool
-  const uint8_t* v_pages;  // [n_blocks][H_kv][kpb] (likewise vpb)
-  const int32_t* table;    // NULL (contiguous pages) or the block table [B][max_pages]
-  int64_t n_blocks;        // blocks in the pools (block table only)
-  const uint16_t* k_res;
-  const uint16_t* v_res;
-  const pnmix_seq_len* lens;
-  const uint32_t* mask;
-  // Append fused into the call (NULL k_new: none): the new key and value rows [B][H_kv][d] take
-  // part in the attention straight from k_new / v_new, and the merge kernel then writes them
-  // into the sink or residual rows (k_sink ... v_res are the caller's writable buffers) and
-  // the advanced lengths into lens_out (never the lens array every wave reads).
-  const uint16_t* k_new;
-  const uint16_t* v_new;
-  pnmix_seq_len* lens_out;
-  float* part_o;   // [B*H_kv][splits][n_g][d]
-  float* part_ml;  // [B*H_kv][splits][n_g][2]
-  float* out;      // [B][H_q][d]
-  float qscale;    // sm_scale * log2(e)
-  int H_q, H_kv, n_g, pairing, n_hi, n_sal, G, KG, g_V, NGV, N_s, max_pages, words;
-  int64_t kpb, vpb;
-  int splits;      // partials per (sequence, KV head): workgroups of the split kernel
-  int page_splits; // page splits per (sequence, KV head), then n16 fp16-row splits
-  int n16;
-  int nw;          // waves per workgroup, one split each
-  int lds_T;       // bytes of the q.K digit table (KG * NT * 16 rows * TL)
-  int lds_wave;    // LDS bytes of one wave's slice
-};
 
 template <int D, int KH>
 struct Shape {
@@ -94,7 +65,6 @@ struct Shape {
   // bytes per (head, digit) row of the q.K digit table: 64 per K-step, plus 16 so that the
   // 16 rows of an A-operand read start on 16 different 4-bank groups
   static constexpr int TL = 64 * (KL + KHM) + 16;
-  static constexpr int NM0 = (D + 63) / 64;  // 16-quad column halves of the p.V product
   static constexpr int JL = D / 4;           // 4-channel units per head
 };
 
@@ -407,23 +377,6 @@ __device__ void write_empty_partial(const DecodeArgs& a, const PartOut& po) {
 //   [channel][token] rows;
 // * every softmax quantity of head n lives in the lanes of column n: the maximum is taken over
 //   the lane's 8 tokens, then over the four lane groups.
-// Where a fused append puts sequence b's new row, from its lengths before the call (the rule
-// of the append entry point): sink row sink_len while the sinks are filling and the sequence
-// has neither pages nor residual rows (kind 0), else residual row res_len if that is below N
-// (kind 1), else nowhere (kind 2).
-__device__ __forceinline__ void append_slot(const pnmix_seq_len& L, int N_s, int& kind, int& row) {
-  if (L.sink_len < N_s && L.n_pages == 0 && L.res_len == 0) {
-    kind = 0;
-    row = max(L.sink_len, 0);
-  } else if (L.res_len >= 0 && L.res_len < kN) {
-    kind = 1;
-    row = L.res_len;
-  } else {
-    kind = 2;
-    row = 0;
-  }
-}
-
 // t_new >= 0: fp16 row t_new (sinks first, then residual rows) is the fused append's new row,
 // read from k_new / v_new instead of the cache.
 template <int D>
@@ -606,8 +559,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   constexpr int NH = 4 * NT;
   constexpr int UK = (NT * D + 63) / 64;   // LSB prep units per lane
   constexpr int NTV = D / 16;              // p.V column tiles of 16 channels
-  constexpr int MW = D / 4 >= 16 ? 16 : 8; // value-byte columns per tile
-  constexpr int NMB = (D / 4) / MW;        // value-byte column blocks
+  constexpr int NBLK = D / 32;             // blocks of 8 value-byte columns (32 channels)
   // value loads after q.K and key prefetch after p.V, only where prefetching both sides a page
   // ahead would spill (the 8-head tiles with one or two key groups fit it in registers)
   constexpr bool kLate = NT >= 2;
@@ -632,10 +584,13 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   const int kg_lane = (8 * oct) / G;  // key group of this lane's keys
   const int sOff = kN * D / 8 + kN * n_sal / 4;      // K page: S after lo and hi planes
   const int zOff = sOff + 2 * KG * D;
-  // p.V: this lane's value-byte column within a tile block, and (for 8-column tiles) the
-  // shift that brings its field pair to bits 0-1 / 4-5
-  const int vcol = lane & (MW - 1);
-  const int vsh = MW == 16 ? 0 : 2 * ((lane & 15) >> 3);
+  // p.V: this lane's value-byte column within a block of 8, and its B-operand mask: field 0
+  // (column n < 8) or field 2 (n >= 8) of every byte in place, for the tiles of field pair
+  // (0, 2); the tiles of pair (1, 3) mask the bytes shifted right by 2 the same way.  Field 2
+  // in place weighs 16 (codes 0..48: no int8 sign bit), so the lane's weight is 1 or 1/16.
+  const int vcol = lane & 7;
+  const uint32_t vmask = (lane & 8) ? 0x30303030u : 0x03030303u;
+  const float vfw = (lane & 8) ? 0.0625f : 1.0f;
 
   // Key side of one page in registers: this lane's packed codes (LSB rows and upper-bit rows
   // 2 oct, 2 oct + 1) and the scales of its prep units.  The next page's are loaded into them as
@@ -705,7 +660,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // code bytes of its p.V tile columns per K-step.
   const uint32_t vS = kN * D / 4 + 2 * 8 * oct;  // S [NGV][N] fp16 after the codes, then Z
   v4u sS[4], zZ[4];
-  v4u cv[NMB][2];
+  v4u cv[NBLK][2];
   auto load_v = [&](int pgv, int64_t blk, bool valid) {
     uint32_t vso;
     const rsrc_t vrs_p = page_rsrc(a.v_pages, a.vpb, vrs, pgv, blk, valid, vso);
@@ -719,10 +674,10 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       zZ[g] = bload16(vrs, vS + 2 * (NGV + gc) * kN, vso);
     }
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int bk = 0; bk < NBLK; ++bk)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        cv[mb][ks] = bload16(vrs, (mb * MW + vcol) * kN + 64 * ks + 16 * qb, vso);
+        cv[bk][ks] = bload16(vrs, (8 * bk + vcol) * kN + 64 * ks + 16 * qb, vso);
   };
   // Pages of this split: split, split + page_splits, ...  (a split past the last page drops
   // the loads of its first one)
@@ -939,8 +894,10 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     }
 
     // ---- p.V fixed point, per head: x = rne(p S 2^sh) with 2^sh above the head's largest
-    // p on this page times the page's largest value scale, so 0 <= x < 2^23 (23 bits relative
-    // to the page's own largest term, whatever the running maximum of earlier pages)
+    // p on this page times the page's largest value scale, so 0 <= x <= 2^22 (22 bits relative
+    // to the page's own largest term, whatever the running maximum of earlier pages).  The
+    // bound has a bit of headroom: top is a rounded product and x rounds once more, so x can
+    // reach 2^22 itself, and byte 2 of x then stays below 128 (never the int8 sign bit).
     uint32_t svm2 = 0u;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -965,7 +922,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         const float top = __builtin_amdgcn_exp2f(pm - mn) * svmax;  // >= every w of this head
         int e = 0;
         if (top > 0.0f) e = (int)((__builtin_bit_cast(uint32_t, top) >> 23) & 0xFF) - 127;
-        sh = min(max(22 - e, -126), 126);
+        sh = min(max(21 - e, -126), 126);
       }
       const float sv2 = pow2i(sh);
       float p[8], pw[8], ps = 0.0f;
@@ -986,7 +943,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         for (int e = 0; e < 4; ++e) {
           zs = fma_mix_lo(p[2 * e], zz[e], zs);
           zs = fma_mix_hi(p[2 * e + 1], zz[e], zs);
-          // 2^23 + x in the float's bits: x in bytes 0..2 (byte 2 < 128)
+          // 2^23 + x in the float's bits: x in bytes 0..2 (byte 2 <= 64)
           x[2 * e] = __builtin_bit_cast(uint32_t, fma_mix_lo(pw[2 * e], ss[e], kTwo23));
           x[2 * e + 1] = __builtin_bit_cast(uint32_t, fma_mix_hi(pw[2 * e + 1], ss[e], kTwo23));
         }
@@ -1006,37 +963,21 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       }
       wave_sync();  // the w digits of this tile are in LDS
 
-      // ---- p.V: tile v = 16 channels of one value group; rows (head, digit), K = 64 keys
+      // ---- p.V: tile v = (block bk = v / 2, field pair f = v % 2): column n is channel
+      // 4 (8 bk + n % 8) + f + 2 (n / 8), 32 channels of one value group; rows (head, digit),
+      // K = 64 keys
 #pragma unroll
       for (int v = 0; v < NTV; ++v) {
-        // MW = 16: tile (block mb, field u) = channels 16 mb + u d/4 + n;
-        // MW = 8:  tile tb = fields 2tb (n < 8) and 2tb + 1 (n >= 8) = channels 16 tb + n
-        const int mb = MW == 16 ? v % NMB : 0;
-        const int fu = MW == 16 ? v / NMB : v;
-        const int cbase = MW == 16 ? 16 * mb + fu * (D / 4) : 16 * v;
-        const int g = cbase / a.g_V;
+        const int bk = v / 2, f = v % 2;
+        const int g = (32 * bk) / a.g_V;
         v4i Bv[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const v4u w = cv[mb][ks];
+          const v4u w = cv[bk][ks];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            uint32_t f;
-            if (MW == 16) {
-              f = fu == 0 ? (w[e] & 0x03030303u)
-                : fu == 1 ? (w[e] & 0x0C0C0C0Cu)
-                : fu == 2 ? (w[e] & 0x30303030u)
-                          : ((w[e] >> 2) & 0x30303030u);
-            } else {
-              const uint32_t ws = w[e] >> vsh;
-              f = fu == 0 ? (ws & 0x03030303u) : (ws & 0x30303030u);
-            }
-            Bv[ks][e] = (int)f;
-          }
+          for (int e = 0; e < 4; ++e) Bv[ks][e] = (int)((f == 0 ? w[e] : (w[e] >> 2)) & vmask);
         }
-        // field weight of the masked bytes: code * {1, 4, 16, 16}[u] (MW 16), {1, 16}[tb] (MW 8)
-        const float fw = MW == 16 ? (fu == 0 ? 1.0f : fu == 1 ? 0.25f : 0.0625f)
-                                  : (fu == 0 ? 1.0f : 0.0625f);
+        const float fw = vfw;
         const uint8_t* wrow = W + (g * 16 + (lane & 15)) * kWS + 16 * qb;
         const v4i A0 = *reinterpret_cast<const v4i*>(wrow);
         const v4i A1 = *reinterpret_cast<const v4i*>(wrow + 64);
@@ -1067,9 +1008,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     if (hh < ng) {
 #pragma unroll
       for (int v = 0; v < NTV; ++v) {
-        const int mb = MW == 16 ? v % NMB : 0;
-        const int fu = MW == 16 ? v / NMB : v;
-        const int c = (MW == 16 ? 16 * mb + fu * (D / 4) : 16 * v) + (lane & 15);
+        const int c = 4 * (8 * (v / 2) + (lane & 7)) + (v % 2) + 2 * ((lane >> 3) & 1);
         const int gi = c / a.g_V;
         const float zsg = gi == 0 ? zs[0] : gi == 1 ? zs[1] : gi == 2 ? zs[2] : zs[3];
         po.o(hh * D + c, acc[t][v] + zsg);
@@ -1378,7 +1317,37 @@ struct BlocksPerCu {
 // fp16 splits is searched too.  Cost = rounds of resident workgroups x (pages per split + 1 for
 // the set-up), the fp16 splits' chunks counting half a page each; ties go to more page splits.
 // At most kMergeSplits partials per (sequence, KV head) (the merge reads every one).
+// The matrix-core split kernel serves (b_H, b_L, b_V) = (3, 1, 2) with value groups of at least
+// 32 channels (a p.V tile spans 32 channels of one group); every other setting takes the
+// generic kernel of decode_generic.hip.
+bool decode_fast_path(const pnmix_cfg& c) {
+  return c.b_H == 3 && c.b_L == 1 && c.b_V == 2 && c.g_V >= 32;
+}
+
+// Generic kernel plan: one 256-thread workgroup per (sequence, KV head, split) walking chunks
+// of 128 tokens (sinks, pages, residual); enough splits for about eight workgroups per compute
+// unit, at most one per chunk and kMergeSplits in all.
+static DecodePlan generic_plan(const pnmix_cfg& c, int B, int max_pages) {
+  DecodePlan p;
+  const long long items = std::max<long long>((long long)B * c.H_kv, 1);
+  const long long want = (8LL * device_cus() + items - 1) / items;
+  const int chunks = max_pages + 2;
+  p.splits = (int)std::max<long long>(1, std::min<long long>(want, std::min(chunks, kMergeSplits)));
+  p.page_splits = p.splits;
+  p.n16 = 0;
+  p.nw = 1;
+  p.pages_per_split = (max_pages + p.splits - 1) / p.splits;
+  p.lds_wave = generic_lds_bytes(c);
+  p.lds_bytes = p.lds_wave;
+  const int ng = c.H_q / c.H_kv;
+  const size_t per = (size_t)items * p.splits * ng;
+  const size_t o_bytes = (per * c.d * sizeof(float) + 255) & ~(size_t)255;
+  p.ws_bytes = o_bytes + ((per * 2 * sizeof(float) + 255) & ~(size_t)255);
+  return p;
+}
+
 DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
+  if (!decode_fast_path(c)) return generic_plan(c, B, max_pages);
   DecodePlan p;
   const long long items = std::max<long long>((long long)B * c.H_kv, 1);
   p.lds_wave = lds_wave_bytes(c);
@@ -1439,23 +1408,26 @@ struct Launch {
   template <int D, int NT, int KG, int KH>
   hipError_t run() const {
     // pages through a block table, or contiguous per (sequence, KV head)
-    const hipError_t e = a.table ? split_kernel<D, NT, KG, KH, true>()
-                                 : split_kernel<D, NT, KG, KH, false>();
-    if (e != hipSuccess) return e;
-    // loads per lane and round: the lane's split count rounded up to a power of two (<= 8)
-    const int per_lane = (a.splits + (256 / (D / 4)) - 1) / (256 / (D / 4));
-    if (per_lane <= 1)
-      hipLaunchKernelGGL((decode_merge_kernel<D, 1>), dim3(B * c.H_q), dim3(256), 0, stream, a);
-    else if (per_lane <= 2)
-      hipLaunchKernelGGL((decode_merge_kernel<D, 2>), dim3(B * c.H_q), dim3(256), 0, stream, a);
-    else if (per_lane <= 4)
-      hipLaunchKernelGGL((decode_merge_kernel<D, 4>), dim3(B * c.H_q), dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_merge_kernel<D, kMergeChunk>), dim3(B * c.H_q), dim3(256), 0,
-                         stream, a);
-    return hipGetLastError();
+    return a.table ? split_kernel<D, NT, KG, KH, true>() : split_kernel<D, NT, KG, KH, false>();
   }
 };
+
+// Merge launch: one workgroup of 256 per (sequence, query head); loads per lane and round: the
+// lane's split count rounded up to a power of two (<= 8).
+template <int D>
+static hipError_t launch_merge(const DecodeArgs& a, int B, hipStream_t stream) {
+  const int per_lane = (a.splits + (256 / (D / 4)) - 1) / (256 / (D / 4));
+  const dim3 grid(B * a.H_q), block(256);
+  if (per_lane <= 1)
+    hipLaunchKernelGGL((decode_merge_kernel<D, 1>), grid, block, 0, stream, a);
+  else if (per_lane <= 2)
+    hipLaunchKernelGGL((decode_merge_kernel<D, 2>), grid, block, 0, stream, a);
+  else if (per_lane <= 4)
+    hipLaunchKernelGGL((decode_merge_kernel<D, 4>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<D, kMergeChunk>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_t* q,
                          const uint16_t* k_sink, const uint16_t* v_sink, const uint8_t* k_pages,
@@ -1498,6 +1470,9 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
   a.g_V = c.g_V;
   a.NGV = c.d / c.g_V;
   a.N_s = c.N_s;
+  a.b_H = c.b_H;
+  a.b_L = c.b_L;
+  a.b_V = c.b_V;
   a.max_pages = max_pages;
   a.words = (c.d / 2 + 31) / 32;
   a.kpb = (int64_t)pnmix_k_page_bytes(&c);
@@ -1506,9 +1481,16 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
   a.page_splits = p.page_splits;
   a.n16 = p.n16;
   a.nw = p.nw;
-  a.lds_T = (int)lds_T_bytes(c);
+  a.lds_T = decode_fast_path(c) ? (int)lds_T_bytes(c) : 0;
   a.lds_wave = (int)p.lds_wave;
-  return dispatch(c, Launch{p, B, c, a, stream});
+  const hipError_t e = decode_fast_path(c) ? dispatch(c, Launch{p, B, c, a, stream})
+                                           : launch_generic_split(a, c.d, B, p.lds_bytes, stream);
+  if (e != hipSuccess) return e;
+  switch (c.d) {
+    case 32: return launch_merge<32>(a, B, stream);
+    case 64: return launch_merge<64>(a, B, stream);
+    default: return launch_merge<128>(a, B, stream);
+  }
 }
 
 }  // namespace pnmix

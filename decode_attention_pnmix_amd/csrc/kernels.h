@@ -17,6 +17,10 @@ hipError_t launch_quantize_k(const pnmix_cfg& c, int n_pages, const pnmix_page* 
                              const uint32_t* mask, hipStream_t stream);
 hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* pages,
                              hipStream_t stream);
+hipError_t launch_dequant_k(const pnmix_cfg& c, int n_pages, const uint8_t* pages,
+                            const uint32_t* mask, float* out, hipStream_t stream);
+hipError_t launch_dequant_v(const pnmix_cfg& c, int n_pages, const uint8_t* pages, float* out,
+                            hipStream_t stream);
 
 struct DecodePlan {
   int splits;           // partials per (sequence, KV head): workgroups of the split kernel
@@ -28,6 +32,7 @@ struct DecodePlan {
   size_t lds_wave;      // LDS slice of one wave
   size_t lds_bytes;     // dynamic LDS of one workgroup
 };
+bool decode_fast_path(const pnmix_cfg& c);
 DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages);
 hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_t* q,
                          const uint16_t* k_sink, const uint16_t* v_sink, const uint8_t* k_pages,

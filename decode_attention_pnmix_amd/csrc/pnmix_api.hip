@@ -48,9 +48,12 @@ pnmix_status check(const pnmix_cfg* c) {
   if (c->G <= 0 || c->N % c->G) return fail(PNMIX_E_INVALID, "G = %d does not divide N", c->G);
   if (c->G != 32 && c->G != 64 && c->G != 128)
     return fail(PNMIX_E_UNSUPPORTED, "G = %d not in {32, 64, 128}", c->G);
-  if (c->b_H != 3 || c->b_L != 1)
-    return fail(PNMIX_E_UNSUPPORTED, "(b_H, b_L) = (%d, %d); only (3, 1)", c->b_H, c->b_L);
-  if (c->b_V != 2) return fail(PNMIX_E_UNSUPPORTED, "b_V = %d; only 2", c->b_V);
+  if (c->b_L < 1 || c->b_H < c->b_L || c->b_H > 8)
+    return fail(PNMIX_E_INVALID, "(b_H, b_L) = (%d, %d): need 1 <= b_L <= b_H", c->b_H, c->b_L);
+  if (c->b_H > 4)
+    return fail(PNMIX_E_UNSUPPORTED, "(b_H, b_L) = (%d, %d): bit widths above 4", c->b_H, c->b_L);
+  if (c->b_V != 1 && c->b_V != 2 && c->b_V != 4 && c->b_V != 16)
+    return fail(PNMIX_E_UNSUPPORTED, "b_V = %d not in {1, 2, 4, 16}", c->b_V);
   if (c->g_V <= 0 || c->d % c->g_V) return fail(PNMIX_E_INVALID, "g_V = %d does not divide d", c->g_V);
   if (c->g_V != 16 && c->g_V != 32 && c->g_V != 64 && c->g_V != 128)
     return fail(PNMIX_E_UNSUPPORTED, "g_V = %d not in {16, 32, 64, 128}", c->g_V);
@@ -78,13 +81,15 @@ int32_t pnmix_hi_pairs(double r, int32_t d) {
 size_t pnmix_mask_words(const pnmix_cfg* c) { return c ? (size_t)(c->d / 2 + 31) / 32 : 0; }
 
 size_t pnmix_k_page_bytes(const pnmix_cfg* c) {
-  if (!c || c->G <= 0) return 0;
-  return (size_t)c->N * c->d / 8 + (size_t)c->N * 2 * c->n_hi_pairs / 4 +
+  if (!c || c->G <= 0 || c->b_L < 0 || c->b_H < c->b_L) return 0;
+  return (size_t)c->N * c->d * c->b_L / 8 +
+         (size_t)c->N * 2 * c->n_hi_pairs * (c->b_H - c->b_L) / 8 +
          4 * (size_t)(c->N / c->G) * c->d;
 }
 
 size_t pnmix_v_page_bytes(const pnmix_cfg* c) {
-  if (!c || c->g_V <= 0) return 0;
+  if (!c || c->g_V <= 0 || c->b_V <= 0) return 0;
+  if (c->b_V == 16) return 2 * (size_t)c->N * c->d;
   return (size_t)c->N * c->d * c->b_V / 8 + 4 * (size_t)c->N * (c->d / c->g_V);
 }
 
@@ -111,8 +116,8 @@ pnmix_status pnmix_score_prefill(const pnmix_cfg* c, int32_t B, int32_t P, const
   pnmix_status s = check(c);
   if (s != PNMIX_OK) return s;
   if (B <= 0 || P <= 0) return fail(PNMIX_E_INVALID, "B = %d, P = %d must be positive", B, P);
-  if ((long long)B * (c->H_q + c->H_kv) > 65535)
-    return fail(PNMIX_E_UNSUPPORTED, "B * (H_q + H_kv) > 65535");
+  if ((long long)B * (c->H_q + c->H_kv) > 0x7FFFFFFFLL || (P + 63) / 64 > 65535)
+    return fail(PNMIX_E_UNSUPPORTED, "B * (H_q + H_kv) >= 2^31 or P > 65535 * 64");
   if (!q || !k || !mask || !ws) return fail(PNMIX_E_INVALID, "q, k, mask and ws must be non-NULL");
   if (ws_bytes < pnmix::score_workspace_bytes(*c, B, P))
     return fail(PNMIX_E_WORKSPACE, "score workspace %zu < %zu bytes", ws_bytes,
@@ -248,6 +253,28 @@ pnmix_status pnmix_decode_attn_paged(const pnmix_cfg* c, int32_t B, int32_t max_
                                          (hipStream_t)stream, max_blocks > 0 ? block_table : nullptr,
                                          n_blocks),
                     "pnmix_decode_attn_paged");
+}
+
+pnmix_status pnmix_dequant_k_pages(const pnmix_cfg* c, int32_t n_pages, const uint8_t* pages,
+                                   const uint32_t* mask, float* out, void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (n_pages < 0) return fail(PNMIX_E_INVALID, "n_pages = %d < 0", n_pages);
+  if (n_pages == 0) return ok();
+  if (!pages || !mask || !out) return fail(PNMIX_E_INVALID, "pages, mask and out must be non-NULL");
+  return hip_status(pnmix::launch_dequant_k(*c, n_pages, pages, mask, out, (hipStream_t)stream),
+                    "pnmix_dequant_k_pages");
+}
+
+pnmix_status pnmix_dequant_v_pages(const pnmix_cfg* c, int32_t n_pages, const uint8_t* pages,
+                                   float* out, void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (n_pages < 0) return fail(PNMIX_E_INVALID, "n_pages = %d < 0", n_pages);
+  if (n_pages == 0) return ok();
+  if (!pages || !out) return fail(PNMIX_E_INVALID, "pages and out must be non-NULL");
+  return hip_status(pnmix::launch_dequant_v(*c, n_pages, pages, out, (hipStream_t)stream),
+                    "pnmix_dequant_v_pages");
 }
 
 pnmix_status pnmix_append_kv(const pnmix_cfg* c, int32_t B, const uint16_t* k_new,

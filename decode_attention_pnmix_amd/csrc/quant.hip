@@ -6,8 +6,7 @@
 // Eq. 7 midpoint correction of 1-bit groups, zero scale plus the original offset for constant
 // groups, H3/L1 packing.  Kernel-implementation appendix of the paper: LSB plane of every key
 // channel at 8 tokens per byte, upper-2-bit plane of salient channels at 4 tokens per byte,
-// values at 4 channels per byte (here the channels j, j + d/4, j + d/2, j + 3d/4, so that one
-// 2-bit field of 16 consecutive bytes holds 16 consecutive channels of one value group).
+// values at 4 consecutive channels of one token per byte.
 //
 // One workgroup of 2d threads per page; thread (octet k, block b) holds tokens 8k..8k+7 x
 // channels 8b..8b+7 of the N x d fp16 page in registers, read with one 16-byte load per token
@@ -21,8 +20,9 @@
 //      clamping before rounding gives the same code as rounding first, and adding 2^23 to a
 //      value in [0, L] rounds it to the nearest even integer and leaves it in the low
 //      mantissa bits.  Key LSB bytes are packed in registers and stored as 8-byte runs; the
-//      upper-bit plane (by salient rank) and the value bytes (four fields from four threads)
-//      are gathered in LDS and copied out 16 bytes a lane.
+//      upper-bit plane (by salient rank) and the value bytes (formed in registers: a thread's 8
+//      channels are two whole bytes of each of its tokens) are gathered in LDS and copied out
+//      16 bytes a lane.
 // Every float step is the reference arithmetic, so codes and fp16 metadata are bit-identical.
 #include "common.h"
 #include "kernels.h"
@@ -253,15 +253,19 @@ __global__ void __launch_bounds__(2 * D) quantize_k_kernel(const pnmix_page* __r
     reinterpret_cast<uint4*>(hi)[i] = reinterpret_cast<const uint4*>(hi_s)[i];
 }
 
+// Byte [m][t] of a value page holds channels 4m..4m+3 of token t (channel 4m+u in bits
+// 2u..2u+1); the LDS copy of the code bytes keeps rows [m] of N bytes at a stride of kVRow
+// words, which spreads the rows of one store over the banks.
+constexpr int kVRow = kN / 4 + 2;
+
 template <int D>
 __global__ void __launch_bounds__(2 * D) quantize_v_kernel(const pnmix_page* __restrict__ jobs,
                                                           int g_V) {
   constexpr int NB = D / 8;
-  __shared__ __align__(16) uint32_t part[kN * NB];  // (min, max) fp16 per token, block
-  __shared__ __align__(16) float2 meta[kN * 4];     // (min, 1/s) per token, group (<= 4)
-  __shared__ __align__(16) uint32_t cw[kN * D / 16]; // the page's code bytes [d/4][N]
+  __shared__ __align__(16) uint32_t part[kN * NB];      // (min, max) fp16 per token, block
+  __shared__ __align__(16) float2 meta[kN * 4];         // (min, 1/s) per token, group (<= 4)
+  __shared__ __align__(16) uint32_t cw[(D / 4) * kVRow]; // the page's code bytes [d/4][N]
   const int tid = threadIdx.x, b = tid % NB, k = tid / NB;
-  reinterpret_cast<uint4*>(cw)[tid] = make_uint4(0u, 0u, 0u, 0u);
   const pnmix_page job = jobs[blockIdx.x];
   const int ng = D / g_V;
   uint8_t* codes = job.dst;
@@ -300,89 +304,284 @@ __global__ void __launch_bounds__(2 * D) quantize_v_kernel(const pnmix_page* __r
   }
   __syncthreads();
 
-  // C: codes of the thread's 8 channels x 8 tokens.  Byte [j][t] of the page holds channel
-  // j + u d/4 of token t in bits 2u..2u+1: the thread's channels share u and fill 8
-  // consecutive bytes j; the four fields of a byte come from four threads, OR-ed in LDS.
+  // C: codes of the thread's 8 tokens x 8 channels.  Channels 8b..8b+3 and 8b+4..8b+7 are
+  // byte columns 2b and 2b+1: each token's two bytes are formed here.  A code is the low byte
+  // of its float 2^23 + q, so (u0 + 4 u1 + 16 u2 + 64 u3) has the byte q0 | q1 << 2 | q2 << 4 |
+  // q3 << 6 in its low 8 bits (the exponent bits land above them).
   const int gi = b / bg;
-  const int u = (8 * b) / (D / 4), j0 = (8 * b) % (D / 4);
   float2 mt[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) mt[e] = meta[(8 * k + e) * 4 + gi];
-  if constexpr (D == 128) {
-    // The four threads of a byte column (same k, u = 0..3) are lanes 4 apart in one 16-lane row:
-    // two DPP rotations of the row OR their fields in registers, and lane u then writes the
-    // column bytes of i = 2u, 2u + 1 with plain LDS stores (no atomics).
-    uint2 mine[2];
+  uint32_t by[2][8];  // [column 2b + i][token e], byte in bits 0..7
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t cu[8];
+  for (int e = 0; e < 8; ++e) {
+    uint32_t cu[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        cu[e] = code_bits_h(word(x[e], i >> 1), (i & 1) != 0, -mt[e].x, mt[e].y, 3.0f);
-      }
-      uint32_t w0 = gather_b0(cu[0], cu[1], cu[2], cu[3]) << (2 * u);
-      uint32_t w1 = gather_b0(cu[4], cu[5], cu[6], cu[7]) << (2 * u);
-      w0 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w0, 0x124, 0xF, 0xF, true);  // row_ror:4
-      w1 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w1, 0x124, 0xF, 0xF, true);
-      w0 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w0, 0x128, 0xF, 0xF, true);  // row_ror:8
-      w1 |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w1, 0x128, 0xF, 0xF, true);
-      if ((i >> 1) == u) mine[i & 1] = make_uint2(w0, w1);
-    }
+    for (int i = 0; i < 8; ++i)
+      cu[i] = code_bits_h(word(x[e], i >> 1), (i & 1) != 0, -mt[e].x, mt[e].y, 3.0f);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      *reinterpret_cast<uint2*>(cw + ((j0 + 2 * u + h) * kN + 8 * k) / 4) = mine[h];
-  } else {
+      by[h][e] = cu[4 * h] + (cu[4 * h + 1] << 2) + (cu[4 * h + 2] << 4) + (cu[4 * h + 3] << 6);
+  }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t cu[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        cu[e] = code_bits_h(word(x[e], i >> 1), (i & 1) != 0, -mt[e].x, mt[e].y, 3.0f);
-      }
-      uint32_t* dst = cw + ((j0 + i) * kN + 8 * k) / 4;
-      atomicOr(dst, gather_b0(cu[0], cu[1], cu[2], cu[3]) << (2 * u));
-      atomicOr(dst + 1, gather_b0(cu[4], cu[5], cu[6], cu[7]) << (2 * u));
-    }
+  for (int h = 0; h < 2; ++h)
+    *reinterpret_cast<uint2*>(cw + (2 * b + h) * kVRow + 2 * k) =
+        make_uint2(gather_b0(by[h][0], by[h][1], by[h][2], by[h][3]),
+                   gather_b0(by[h][4], by[h][5], by[h][6], by[h][7]));
+  __syncthreads();
+  // 16-byte pieces of the code area, one per thread: row tid / 8, bytes 16 (tid % 8) ..
+  {
+    const uint32_t* src = cw + (tid / 8) * kVRow + 4 * (tid % 8);
+    const uint2 lo2 = *reinterpret_cast<const uint2*>(src);
+    const uint2 hi2 = *reinterpret_cast<const uint2*>(src + 2);
+    reinterpret_cast<uint4*>(codes)[tid] = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Every other bit width: (b_H, b_L) with 1 <= b_L <= b_H <= 4 and b_V in {1, 2, 4, 16} (the
+// bit-width sweep of the PN-Mix paper's Table 14 / Figure 3).  Same arithmetic per group and
+// element as above (exact min / max, group_meta, code_bits), so codes and metadata are again
+// bit-identical to the reference; the layout generalises the appendix's planes: the low b_L
+// bits of every key channel in a plane of width b_L, the upper b_H - b_L bits of the salient
+// channels in a plane of that width (plane_field in common.h describes a plane), and 8 / b_V
+// consecutive channels of one token per value byte.  One workgroup of 256 threads per page, the
+// page staged in LDS; these kernels favour plainness over speed.
+
+// page rows -> LDS [N][D] fp16
+template <int D>
+__device__ __forceinline__ void stage_page(uint16_t* xs, const uint16_t* src, int64_t stride) {
+  for (int i = threadIdx.x; i < kN * D / 2; i += blockDim.x) {
+    const int t = i / (D / 2), c2 = i % (D / 2);
+    const uint16_t* r = src + (int64_t)t * stride + 2 * c2;
+    reinterpret_cast<uint32_t*>(xs)[i] = (uint32_t)r[0] | ((uint32_t)r[1] << 16);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) quantize_k_generic_kernel(
+    const pnmix_page* __restrict__ jobs, const uint32_t* __restrict__ mask, int pairing, int n_hi,
+    int G, int words, int bH, int bL) {
+  __shared__ __align__(16) uint16_t xs[kN * D];
+  __shared__ __align__(16) uint8_t q[kN * D];
+  __shared__ float2 meta[(kN / 32) * D];
+  __shared__ int rank_s[D];
+  __shared__ int chan_s[D];
+  const int tid = threadIdx.x;
+  const pnmix_page job = jobs[blockIdx.x];
+  const int n_sal = 2 * n_hi, wH = bH - bL, KG = kN / G;
+  uint8_t* lo = job.dst;
+  uint8_t* hi = lo + kN * D * bL / 8;
+  uint16_t* S = reinterpret_cast<uint16_t*>(hi + kN * n_sal * wH / 8);
+  uint16_t* Z = S + KG * D;
+  stage_page<D>(xs, job.src, job.src_row_stride);
+  const uint32_t* mrow = mask + job.mask_row * words;
+  for (int c = tid; c < D; c += 256) {
+    const int r = salient_rank(mrow, c, D, pairing, n_hi);
+    rank_s[c] = r;
+    if (r >= 0) chan_s[r] = c;
   }
   __syncthreads();
-  reinterpret_cast<uint4*>(codes)[tid] = reinterpret_cast<const uint4*>(cw)[tid];
+  for (int it = tid; it < KG * D; it += 256) {
+    const int g = it / D, c = it % D;
+    float mn = h2f(xs[(g * G) * D + c]), mx = mn;
+    for (int t = g * G + 1; t < (g + 1) * G; ++t) {
+      const float v = h2f(xs[t * D + c]);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+    const int L = (1 << (rank_s[c] >= 0 ? bH : bL)) - 1;
+    uint16_t s, z;
+    meta[g * D + c] = group_meta(mn, mx, L, s, z);
+    S[g * D + c] = s;
+    Z[g * D + c] = z;
+  }
+  __syncthreads();
+  for (int i = tid; i < kN * D; i += 256) {
+    const int t = i / D, c = i % D;
+    const float2 m = meta[(t / G) * D + c];
+    const float L = (float)((1 << (rank_s[c] >= 0 ? bH : bL)) - 1);
+    q[i] = (uint8_t)(code_bits(h2f(xs[i]), m.x, m.y, L) & 0xFFu);
+  }
+  __syncthreads();
+  // low plane: unit (octet j, channel c) -> its b_L bytes
+  for (int i = tid; i < (kN / 8) * D; i += 256) {
+    const int j = i / D, c = i % D;
+    uint32_t s = 0;
+    for (int k = 0; k < 8; ++k) s |= ((uint32_t)q[(8 * j + k) * D + c] & ((1u << bL) - 1u)) << (bL * k);
+    for (int b = 0; b < bL; ++b) lo[(j * bL + b) * D + c] = (uint8_t)(s >> (8 * b));
+  }
+  // high plane: unit (octet j, salient rank r) -> its b_H - b_L bytes
+  if (wH > 0)
+    for (int i = tid; i < (kN / 8) * n_sal; i += 256) {
+      const int j = i / n_sal, r = i % n_sal, c = chan_s[r];
+      uint32_t s = 0;
+      for (int k = 0; k < 8; ++k) s |= ((uint32_t)q[(8 * j + k) * D + c] >> bL) << (wH * k);
+      for (int b = 0; b < wH; ++b) hi[(j * wH + b) * n_sal + r] = (uint8_t)(s >> (8 * b));
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) quantize_v_generic_kernel(const pnmix_page* __restrict__ jobs,
+                                                                 int g_V, int bV) {
+  __shared__ __align__(16) uint16_t xs[kN * D];
+  __shared__ float2 meta[kN * 4];
+  const int tid = threadIdx.x;
+  const pnmix_page job = jobs[blockIdx.x];
+  if (bV == 16) {  // values kept in fp16: the page is the rows [N][D]
+    uint16_t* dst = reinterpret_cast<uint16_t*>(job.dst);
+    for (int i = tid; i < kN * D; i += 256) dst[i] = job.src[(int64_t)(i / D) * job.src_row_stride + i % D];
+    return;
+  }
+  const int ng = D / g_V, e = 8 / bV;
+  uint8_t* codes = job.dst;
+  uint16_t* S = reinterpret_cast<uint16_t*>(codes + kN * D * bV / 8);  // [ng][N]
+  uint16_t* Z = S + kN * ng;
+  stage_page<D>(xs, job.src, job.src_row_stride);
+  __syncthreads();
+  const int L = (1 << bV) - 1;
+  for (int it = tid; it < kN * ng; it += 256) {
+    const int t = it % kN, gi = it / kN;
+    float mn = h2f(xs[t * D + gi * g_V]), mx = mn;
+    for (int c = gi * g_V + 1; c < (gi + 1) * g_V; ++c) {
+      const float v = h2f(xs[t * D + c]);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+    uint16_t s, z;
+    meta[t * 4 + gi] = group_meta(mn, mx, L, s, z);
+    S[gi * kN + t] = s;
+    Z[gi * kN + t] = z;
+  }
+  __syncthreads();
+  // byte [m][t]: channels e m .. e m + e - 1 of token t
+  for (int i = tid; i < (D / e) * kN; i += 256) {
+    const int m = i / kN, t = i % kN;
+    uint32_t byte = 0;
+    for (int u = 0; u < e; ++u) {
+      const int c = e * m + u;
+      const float2 mt = meta[t * 4 + c / g_V];
+      byte |= (code_bits(h2f(xs[t * D + c]), mt.x, mt.y, (float)L) & 0xFFu) << (bV * u);
+    }
+    codes[i] = (uint8_t)byte;
+  }
+}
+
+// Dequantized pages for analysis: x = S code + Z with the stored fp16 S and Z, one fma in fp32
+// (the exact product and sum, rounded once).  One workgroup per page, out [N][D] f32.
+template <int D>
+__global__ void __launch_bounds__(256) dequant_k_kernel(const uint8_t* __restrict__ pages,
+                                                        int64_t kpb, const uint32_t* __restrict__ mask,
+                                                        int words, int pairing, int n_hi, int G,
+                                                        int bH, int bL, float* __restrict__ out) {
+  const uint8_t* pg = pages + (int64_t)blockIdx.x * kpb;
+  const uint32_t* mrow = mask + (int64_t)blockIdx.x * words;
+  const int n_sal = 2 * n_hi, wH = bH - bL;
+  const uint8_t* hi = pg + kN * D * bL / 8;
+  const uint8_t* Sp = hi + kN * n_sal * wH / 8;
+  const uint8_t* Zp = Sp + 2 * (kN / G) * D;
+  float* o = out + (int64_t)blockIdx.x * kN * D;
+  for (int i = threadIdx.x; i < kN * D; i += 256) {
+    const int t = i / D, c = i % D, g = t / G;
+    uint32_t code = plane_field(pg, D, bL, c, t);
+    const int r = salient_rank(mrow, c, D, pairing, n_hi);
+    if (wH > 0 && r >= 0) code |= plane_field(hi, n_sal, wH, r, t) << bL;
+    const float s = h2f(reinterpret_cast<const uint16_t*>(Sp)[g * D + c]);
+    const float z = h2f(reinterpret_cast<const uint16_t*>(Zp)[g * D + c]);
+    o[i] = __builtin_fmaf(s, (float)code, z);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) dequant_v_kernel(const uint8_t* __restrict__ pages,
+                                                        int64_t vpb, int g_V, int bV,
+                                                        float* __restrict__ out) {
+  const uint8_t* pg = pages + (int64_t)blockIdx.x * vpb;
+  float* o = out + (int64_t)blockIdx.x * kN * D;
+  if (bV == 16) {
+    for (int i = threadIdx.x; i < kN * D; i += 256) o[i] = h2f(reinterpret_cast<const uint16_t*>(pg)[i]);
+    return;
+  }
+  const int e = 8 / bV, ng = D / g_V;
+  const uint16_t* Sp = reinterpret_cast<const uint16_t*>(pg + kN * D * bV / 8);
+  const uint16_t* Zp = Sp + ng * kN;
+  for (int i = threadIdx.x; i < kN * D; i += 256) {
+    const int t = i / D, c = i % D, g = c / g_V;
+    const uint32_t code = (pg[(c / e) * kN + t] >> (bV * (c % e))) & ((1u << bV) - 1u);
+    o[i] = __builtin_fmaf(h2f(Sp[g * kN + t]), (float)code, h2f(Zp[g * kN + t]));
+  }
 }
 
 hipError_t launch_quantize_k(const pnmix_cfg& c, int n_pages, const pnmix_page* pages,
                              const uint32_t* mask, hipStream_t stream) {
   if (n_pages == 0) return hipSuccess;
   const int words = (c.d / 2 + 31) / 32;
+  const bool fast = c.b_H == 3 && c.b_L == 1;
+#define PNMIX_QK(DD)                                                                             \
+  if (fast)                                                                                      \
+    hipLaunchKernelGGL(quantize_k_kernel<DD>, dim3(n_pages), dim3(2 * DD), 0, stream, pages, mask, \
+                       c.pairing, c.n_hi_pairs, c.G, words);                                     \
+  else                                                                                           \
+    hipLaunchKernelGGL(quantize_k_generic_kernel<DD>, dim3(n_pages), dim3(256), 0, stream, pages, \
+                       mask, c.pairing, c.n_hi_pairs, c.G, words, c.b_H, c.b_L);
   switch (c.d) {
-    case 32:
-      hipLaunchKernelGGL(quantize_k_kernel<32>, dim3(n_pages), dim3(64), 0, stream, pages, mask,
-                         c.pairing, c.n_hi_pairs, c.G, words);
-      break;
-    case 64:
-      hipLaunchKernelGGL(quantize_k_kernel<64>, dim3(n_pages), dim3(128), 0, stream, pages,
-                         mask, c.pairing, c.n_hi_pairs, c.G, words);
-      break;
-    default:
-      hipLaunchKernelGGL(quantize_k_kernel<128>, dim3(n_pages), dim3(256), 0, stream, pages,
-                         mask, c.pairing, c.n_hi_pairs, c.G, words);
-      break;
+    case 32: PNMIX_QK(32) break;
+    case 64: PNMIX_QK(64) break;
+    default: PNMIX_QK(128) break;
   }
+#undef PNMIX_QK
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* pages,
                              hipStream_t stream) {
   if (n_pages == 0) return hipSuccess;
+  const bool fast = c.b_V == 2;
+#define PNMIX_QV(DD)                                                                             \
+  if (fast)                                                                                      \
+    hipLaunchKernelGGL(quantize_v_kernel<DD>, dim3(n_pages), dim3(2 * DD), 0, stream, pages, c.g_V); \
+  else                                                                                           \
+    hipLaunchKernelGGL(quantize_v_generic_kernel<DD>, dim3(n_pages), dim3(256), 0, stream, pages, \
+                       c.g_V, c.b_V);
+  switch (c.d) {
+    case 32: PNMIX_QV(32) break;
+    case 64: PNMIX_QV(64) break;
+    default: PNMIX_QV(128) break;
+  }
+#undef PNMIX_QV
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_k(const pnmix_cfg& c, int n_pages, const uint8_t* pages,
+                            const uint32_t* mask, float* out, hipStream_t stream) {
+  if (n_pages == 0) return hipSuccess;
+  const int words = (c.d / 2 + 31) / 32;
+  const int64_t kpb = (int64_t)pnmix_k_page_bytes(&c);
+#define PNMIX_DK(DD)                                                                             \
+  hipLaunchKernelGGL(dequant_k_kernel<DD>, dim3(n_pages), dim3(256), 0, stream, pages, kpb, mask, \
+                     words, c.pairing, c.n_hi_pairs, c.G, c.b_H, c.b_L, out);
+  switch (c.d) {
+    case 32: PNMIX_DK(32) break;
+    case 64: PNMIX_DK(64) break;
+    default: PNMIX_DK(128) break;
+  }
+#undef PNMIX_DK
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_v(const pnmix_cfg& c, int n_pages, const uint8_t* pages, float* out,
+                            hipStream_t stream) {
+  if (n_pages == 0) return hipSuccess;
+  const int64_t vpb = (int64_t)pnmix_v_page_bytes(&c);
   switch (c.d) {
     case 32:
-      hipLaunchKernelGGL(quantize_v_kernel<32>, dim3(n_pages), dim3(64), 0, stream, pages, c.g_V);
+      hipLaunchKernelGGL(dequant_v_kernel<32>, dim3(n_pages), dim3(256), 0, stream, pages, vpb, c.g_V, c.b_V, out);
       break;
     case 64:
-      hipLaunchKernelGGL(quantize_v_kernel<64>, dim3(n_pages), dim3(128), 0, stream, pages,
-                         c.g_V);
+      hipLaunchKernelGGL(dequant_v_kernel<64>, dim3(n_pages), dim3(256), 0, stream, pages, vpb, c.g_V, c.b_V, out);
       break;
     default:
-      hipLaunchKernelGGL(quantize_v_kernel<128>, dim3(n_pages), dim3(256), 0, stream, pages,
-                         c.g_V);
+      hipLaunchKernelGGL(dequant_v_kernel<128>, dim3(n_pages), dim3(256), 0, stream, pages, vpb, c.g_V, c.b_V, out);
       break;
   }
   return hipGetLastError();

@@ -27,8 +27,8 @@ __global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __rest
                                                           int H_q, int H_kv, int d, int pairing,
                                                           int P, int n_chunks) {
   __shared__ __align__(16) uint16_t tile[kSub * 128];  // kSub token rows of up to 128 fp16
-  const int chunk = blockIdx.x;
-  const int seq_head = blockIdx.y;  // b * (H_q + H_kv) + head
+  const int seq_head = blockIdx.x;  // b * (H_q + H_kv) + head (grid x: no 65535 limit)
+  const int chunk = blockIdx.y;
   const int H = H_q + H_kv;
   const int b = seq_head / H;
   const int head = seq_head % H;
@@ -132,7 +132,7 @@ hipError_t launch_score(const pnmix_cfg& c, int B, int P, const uint16_t* q, con
                         float* sigma, uint32_t* mask, void* ws, hipStream_t stream) {
   const int n_chunks = (P + kChunk - 1) / kChunk;
   float* chunk_sums = static_cast<float*>(ws);
-  dim3 g1(n_chunks, B * (c.H_q + c.H_kv));
+  dim3 g1(B * (c.H_q + c.H_kv), n_chunks);
   hipLaunchKernelGGL(score_chunks_kernel, g1, dim3(64), 0, stream, q, k, chunk_sums, c.H_q,
                      c.H_kv, c.d, c.pairing, P, n_chunks);
   hipError_t e = hipGetLastError();

@@ -126,7 +126,8 @@ def main() -> None:
     kw = k[:, :, T - win:].contiguous()
     for r in sorted({0.0, w.r, 1.0}):
         n_hi = L.pnmix_hi_pairs(r, w.d)
-        cfg = L.make_cfg(w.H_q, w.H_kv, w.d, w.pairing, n_hi, G=w.G, b_V=w.b_V, g_V=w.g_V,
+        cfg = L.make_cfg(w.H_q, w.H_kv, w.d, w.pairing, n_hi, G=w.G, b_H=w.b_H, b_L=w.b_L, b_V=w.b_V,
+                         g_V=w.g_V,
                          N_s=w.N_s, N=w.N)
         line = {"workload": w.name, "B": B, "T": T, "P": w.P, "r": r, "n_hi_pairs": n_hi}
         line.update(decode_fidelity(cfg, qp, k, v, qd))

@@ -4,7 +4,9 @@
  * PN-Mix keeps the key cache of a RoPE decoder in mixed precision: RoPE channel pairs with a
  * large query-key pair-norm product get b_H = 3 bits, the rest b_L = 1 bit with a midpoint
  * correction, selected once at prefill; values are quantized per token at b_V = 2 bits; the
- * first N_s tokens (sinks) and an N-token residual buffer stay in fp16.  Sources:
+ * first N_s tokens (sinks) and an N-token residual buffer stay in fp16.  The other bit widths of
+ * the paper's sweep (Table 14 / Figure 3: b_H, b_L in {1..4}, b_V = 16 values kept in fp16, and
+ * b_V in {1, 4}) are supported too, through plainer kernels.  Sources:
  *   [PNMIX]   "PN-Mix: Pair-Norm Guided Mixed-Precision Key Cache Quantization for Efficient
  *             Long-Output LLM Inference" (arXiv 2610.19605), sec. 2 (Eq. 1 GQA attention,
  *             Eq. 2 asymmetric group quantization, online residual buffer), sec. 5 (method,
@@ -58,8 +60,10 @@ typedef enum {
 
 /* Problem statement of one attention layer ([PNMIX] sec. 2 and 5; [REPRO]).
  * Supported: H_q % H_kv == 0 with n_g = H_q / H_kv <= 16; d in {32, 64, 128};
- * 0 <= n_hi_pairs <= d/2; N == 128; G in {32, 64, 128}; (b_H, b_L) == (3, 1); b_V == 2;
- * g_V in {16, 32, 64, 128} dividing d with d / g_V <= 4 value groups per token; 0 <= N_s <= 128. */
+ * 0 <= n_hi_pairs <= d/2; N == 128; G in {32, 64, 128}; 1 <= b_L <= b_H <= 4;
+ * b_V in {1, 2, 4, 16}; g_V in {16, 32, 64, 128} dividing d with d / g_V <= 4 value groups per
+ * token; 0 <= N_s <= 128.  (b_H, b_L, b_V) = (3, 1, 2) with g_V >= 32 runs on the matrix-core
+ * decode kernel; every other setting decodes on the generic kernel (same results contract). */
 typedef struct {
   int32_t H_q, H_kv, d, pairing;
   int32_t n_hi_pairs; /* floor(r * d / 2): pnmix_hi_pairs(r, d) */
@@ -94,9 +98,10 @@ pnmix_status pnmix_check_cfg(const pnmix_cfg* cfg);
 int32_t pnmix_hi_pairs(double r, int32_t d);
 /* uint32 words per (sequence, KV head) of the pair mask: ceil((d/2) / 32); bit i = pair i. */
 size_t pnmix_mask_words(const pnmix_cfg* cfg);
-/* K page: N*d/8 (LSB plane) + N*2*n_hi_pairs/4 (upper-2-bit plane) + 4*(N/G)*d (fp16 S, Z). */
+/* K page: N*d*b_L/8 (low plane) + N*2*n_hi_pairs*(b_H-b_L)/8 (high plane) + 4*(N/G)*d (fp16
+ * S, Z); with (3, 1) the LSB plane N*d/8 and the upper-2-bit plane N*2*n_hi_pairs/4. */
 size_t pnmix_k_page_bytes(const pnmix_cfg* cfg);
-/* V page: N*d*b_V/8 (codes) + 4*N*(d/g_V) (fp16 S, Z). */
+/* V page: N*d*b_V/8 (codes) + 4*N*(d/g_V) (fp16 S, Z); b_V = 16: the fp16 rows, 2*N*d. */
 size_t pnmix_v_page_bytes(const pnmix_cfg* cfg);
 /* Device workspace of pnmix_score_prefill (bytes, 256-aligned size). */
 size_t pnmix_score_workspace_bytes(const pnmix_cfg* cfg, int32_t B, int32_t P);
@@ -127,26 +132,33 @@ pnmix_status pnmix_score_prefill(const pnmix_cfg* cfg, int32_t B, int32_t P, con
 /* Key page quantization and H3/L1 packing ([PNMIX] sec. 2 Eq. 2 and kernel-implementation
  * appendix; [REPRO] Eq. 7, constant groups, H3/L1 packing).
  *   pages [n_pages] DEVICE array of jobs; mask [rows][mask_words] (row = job.mask_row).
- * Per channel c and token group g of G tokens: exact min mn and max mx (-0 -> +0); L = 7 if
- * c belongs to a masked pair else 1; if mx == mn: codes 0, S = +0, Z = mn; else
- * s = (mx-mn)/L, q = clamp(rne((x-mn) * (1/s)), 0, L), stored S = h(s), Z = h(mn) for L = 7
- * and (Eq. 7) S = h((mx-mn)*0.5), Z = h((3*mn + mx)*0.25) for L = 1 (fp32, no contraction,
- * h = fp32->fp16 round-half-even).  Page layout (bytes, LSB-first bits):
+ * Per channel c and token group g of G tokens: exact min mn and max mx (-0 -> +0);
+ * L = 2^b_H - 1 if c belongs to a masked pair else 2^b_L - 1; if mx == mn: codes 0, S = +0,
+ * Z = mn; else s = (mx-mn)/L, q = clamp(rne((x-mn) * (1/s)), 0, L), stored S = h(s), Z = h(mn)
+ * for L > 1 and (Eq. 7) S = h((mx-mn)*0.5), Z = h((3*mn + mx)*0.25) for L = 1 (fp32, no
+ * contraction, h = fp32->fp16 round-half-even).  Page layout (bytes, LSB-first bits), for
+ * (b_H, b_L) = (3, 1):
  *   lo [N/8][d]      byte [j][c] bit k = q(8j+k, c) & 1
  *   hi [N/4][n_sal]  byte [j][r] bits 2k..2k+1 = q(4j+k, sal(r)) >> 1, n_sal = 2*n_hi_pairs,
  *                    salient channels in ascending channel order
  *   S  [N/G][d] fp16, then Z [N/G][d] fp16.
+ * Other widths: lo [N/8][b_L][d] holds q & (2^b_L - 1) of every channel, hi
+ * [N/8][b_H-b_L][n_sal] holds q >> b_L of the salient channels; in a plane of width w the w-bit
+ * fields of tokens 8j..8j+7 of one column form an 8w-bit little-endian stream (token 8j+k at
+ * bits wk..wk+w-1) stored as its w bytes [j][0..w-1].
  * Bit-exact with the reference oracle. */
 pnmix_status pnmix_quantize_k_page(const pnmix_cfg* cfg, int32_t n_pages,
                                    const pnmix_page* pages, const uint32_t* mask, void* stream);
 
-/* Value page quantization and packing ([PNMIX] sec. 2 and kernel-implementation appendix;
- * [SUMMARY]): per token and channel group of g_V channels, Eq. 2 at b_V = 2 bits with the
- * constant rule; stored S = h(s), Z = h(mn).  Layout:
- *   codes [d/4][N]  byte [j][t] = 4 channels of token t a quarter of the head apart:
- *                   channel j + u*d/4 in bits 2u..2u+1 (u = 0..3), so each 2-bit field of
- *                   16 consecutive bytes j covers 16 consecutive channels (one value group)
+/* Value page quantization and packing ([PNMIX] sec. 2 and kernel-implementation appendix:
+ * every 4 consecutive channel values of a token in one byte; [SUMMARY]): per token and channel
+ * group of g_V channels, Eq. 2 at b_V bits with the constant rule (Eq. 7 metadata for b_V = 1);
+ * stored S = h(s), Z = h(mn).  Layout for b_V = 2:
+ *   codes [d/4][N]  byte [m][t] = channels 4m..4m+3 of token t, channel 4m+u in bits 2u..2u+1
+ *                   (the N tokens of one byte column contiguous)
  *   S [d/g_V][N] fp16, then Z [d/g_V][N] fp16 (group-major: one group's N tokens contiguous).
+ * b_V in {1, 4}: codes [d*b_V/8][N], byte [m][t] = the 8/b_V channels (8/b_V) m + u of token t
+ * in bits b_V u ..; b_V = 16: the page is the fp16 rows [N][d].
  * Bit-exact with the reference oracle. */
 pnmix_status pnmix_quantize_v_page(const pnmix_cfg* cfg, int32_t n_pages,
                                    const pnmix_page* pages, void* stream);
@@ -219,6 +231,20 @@ pnmix_status pnmix_decode_attn_paged(const pnmix_cfg* cfg, int32_t B, int32_t ma
                                      const uint16_t* v_res, const pnmix_seq_len* lens,
                                      const uint32_t* mask, float sm_scale, float* out, void* ws,
                                      size_t ws_bytes, void* stream);
+
+/* ---- analysis: dequantized pages ----------------------------------------------------------- */
+
+/* x = S code + Z of every element of n_pages packed key pages, with the stored fp16 S and Z and
+ * one fp32 fma (the exact product plus offset, rounded once) ([PNMIX] sec. 2, Eq. 2: the
+ * reconstruction s q + z).  For inspection and fidelity measurement; decode never forms it.
+ *   pages [n_pages][pnmix_k_page_bytes] u8 (contiguous); mask [n_pages][mask_words], the row
+ *   each page was packed with; out [n_pages][N][d] f32. */
+pnmix_status pnmix_dequant_k_pages(const pnmix_cfg* cfg, int32_t n_pages, const uint8_t* pages,
+                                   const uint32_t* mask, float* out, void* stream);
+/* The same for value pages: pages [n_pages][pnmix_v_page_bytes] u8 -> out [n_pages][N][d] f32
+ * (b_V = 16 pages: the fp16 values). */
+pnmix_status pnmix_dequant_v_pages(const pnmix_cfg* cfg, int32_t n_pages, const uint8_t* pages,
+                                   float* out, void* stream);
 
 /* ---- online cache placement ([PNMIX] sec. 2: new keys and values enter the FP16 residual
  * buffer of N tokens, which is quantized and appended to the cache when full; sec. 5: the

@@ -95,6 +95,8 @@ class Workload:
     G: int
     b_V: int = 2
     g_V: int = 32
+    b_H: int = 3
+    b_L: int = 1
     N_s: int = 32
     N: int = 128
     sigma_ln: float = 1.0

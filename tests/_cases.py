@@ -20,10 +20,10 @@ def say(*a):
 
 
 def cfgs(w: synth.Workload):
-    lc = P.make_cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_V=w.b_V, g_V=w.g_V,
-                    N_s=w.N_s, N=w.N)
-    oc = oracle.Cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_V=w.b_V, g_V=w.g_V,
-                    N_s=w.N_s, N=w.N)
+    lc = P.make_cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_H=w.b_H, b_L=w.b_L,
+                    b_V=w.b_V, g_V=w.g_V, N_s=w.N_s, N=w.N)
+    oc = oracle.Cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_H=w.b_H, b_L=w.b_L,
+                    b_V=w.b_V, g_V=w.g_V, N_s=w.N_s, N=w.N)
     return lc, oc
 
 
@@ -68,8 +68,8 @@ def fill_cache_bulk(w, lc, qp, k, v, T, max_pages=None):
     rest = T - a
     c.k_res.zero_()
     c.v_res.zero_()
-    c.k_res[:, :, :rest] = k[:, :, a:]
-    c.v_res[:, :, :rest] = v[:, :, a:]
+    c.k_res[:, :, :rest] = k[:, :, a:T]
+    c.v_res[:, :, :rest] = v[:, :, a:T]
     c.sink_len, c.n_pages, c.res_len = s, n_pages, rest
     c._sync_lens()
     torch.cuda.synchronize()

@@ -46,10 +46,17 @@ def _cfg(**kw):
     ({"n_hi_pairs": -1}, L.PNMIX_E_INVALID),
     ({"G": 48}, L.PNMIX_E_INVALID),
     ({"G": 16}, L.PNMIX_E_UNSUPPORTED),
-    ({"b_H": 4, "b_L": 2}, L.PNMIX_E_UNSUPPORTED),
-    ({"b_V": 4}, L.PNMIX_E_UNSUPPORTED),
+    ({"b_H": 4, "b_L": 2}, L.PNMIX_OK),
+    ({"b_H": 1, "b_L": 1}, L.PNMIX_OK),
+    ({"b_H": 2, "b_L": 3}, L.PNMIX_E_INVALID),
+    ({"b_H": 5, "b_L": 1}, L.PNMIX_E_UNSUPPORTED),
+    ({"b_L": 0}, L.PNMIX_E_INVALID),
+    ({"b_V": 4}, L.PNMIX_OK),
+    ({"b_V": 16}, L.PNMIX_OK),
+    ({"b_V": 3}, L.PNMIX_E_UNSUPPORTED),
     ({"g_V": 24}, L.PNMIX_E_INVALID),
     ({"g_V": 16}, L.PNMIX_E_UNSUPPORTED),
+    ({"d": 64, "g_V": 16}, L.PNMIX_OK),
     ({"N": 64}, L.PNMIX_E_UNSUPPORTED),
     ({"N_s": -1}, L.PNMIX_E_INVALID),
     ({"d": 32, "g_V": 32, "n_hi_pairs": 8, "pairing": 0, "H_q": 4, "H_kv": 2}, L.PNMIX_OK),
@@ -62,12 +69,14 @@ def test_check_cfg(kw, status):
 
 
 def test_sizes_match_the_oracle(orc):
-    for d, r, G, g_V in ((128, 0.5, 128, 32), (128, 0.4, 64, 32), (32, 0.5, 128, 32),
-                         (64, 0.25, 32, 16)):
+    for d, r, G, g_V, bH, bL, bV in ((128, 0.5, 128, 32, 3, 1, 2), (128, 0.4, 64, 32, 3, 1, 2),
+                                     (32, 0.5, 128, 32, 3, 1, 2), (64, 0.25, 32, 16, 3, 1, 2),
+                                     (128, 0.3, 64, 32, 4, 2, 16), (64, 0.6, 128, 16, 4, 3, 4),
+                                     (128, 0.5, 32, 64, 2, 2, 1), (32, 0.9, 64, 32, 4, 1, 16)):
         n_hi = P.pnmix_hi_pairs(r, d)
         assert n_hi == orc.hi_pairs(r, d)
-        c = _cfg(d=d, n_hi_pairs=n_hi, G=G, g_V=g_V)
-        oc = orc.Cfg(32, 8, d, 1, n_hi, G=G, g_V=g_V)
+        c = _cfg(d=d, n_hi_pairs=n_hi, G=G, g_V=g_V, b_H=bH, b_L=bL, b_V=bV)
+        oc = orc.Cfg(32, 8, d, 1, n_hi, G=G, g_V=g_V, b_H=bH, b_L=bL, b_V=bV)
         assert P.pnmix_k_page_bytes(c) == orc.k_page_bytes(oc)
         assert P.pnmix_v_page_bytes(c) == orc.v_page_bytes(oc)
         assert P.pnmix_mask_words(c) == orc.mask_words(oc)
@@ -86,6 +95,27 @@ def test_decode_plan_queries():
         assert 1 <= s <= min(mp + n16_max, 136)
         assert P.pnmix_decode_workspace_bytes(c, B, mp) >= B * 8 * s * 4 * (128 + 2) * 4
     assert P.pnmix_decode_splits(_cfg(G=48), 1, 10) == 0
+    # the generic kernel (other bit widths): one split per 128-token chunk at most
+    for kw in ({"b_V": 16}, {"b_H": 4, "b_L": 2}, {"d": 64, "g_V": 16}):
+        for B, mp in ((1, 255), (32, 63), (1, 0)):
+            s = P.pnmix_decode_splits(_cfg(**kw), B, mp)
+            assert 1 <= s <= min(mp + 2, 136)
+
+
+def test_score_accepts_a_folded_batch_above_65535():
+    """Layers fold into the batch: Llama-3.1-8B's 32 layers x B = 110 x (32 + 8) heads is 140,800
+    (sequence, head) rows, above the 65,535 limit of a grid's y dimension.  Validation passes;
+    without a device the launch then reports PNMIX_E_HIP."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present (this checks host validation only)")
+    c = _cfg(n_hi_pairs=25, G=64)
+    B = 32 * 110
+    ws = P.pnmix_score_workspace_bytes(c, B, 141)
+    assert ws > 0
+    st = P.lib().pnmix_score_prefill(ctypes.byref(c), B, 141, FAKE, FAKE, None, FAKE, FAKE, ws,
+                                     None)
+    assert st == L.PNMIX_E_HIP, P.pnmix_last_error()
 
 
 FAKE = ctypes.c_void_p(0x10000)

@@ -257,10 +257,15 @@ def test_decode_parity(name):
     del cache, k, v
 
 
-def test_decode_ragged_lengths_and_edges():
+# value groups of 32 channels take the matrix-core decode kernel, 16-channel groups the generic one
+BOTH_KERNELS = pytest.mark.parametrize("g_V", [32, 16], ids=["mfma", "generic"])
+
+
+@BOTH_KERNELS
+def test_decode_ragged_lengths_and_edges(g_V):
     """Per-sequence lengths in one batch: empty, sinks only, partial sinks, residual only, full
     residual (N rows), pages with and without residual, n_pages = max_pages."""
-    w = synth.Workload("ragged", 1, 1, 8, 2, 64, 1, 1e4, 64, 1024, 0.5, 64, g_V=16)
+    w = synth.Workload("ragged", 1, 1, 8, 2, 64, 1, 1e4, 64, 1024, 0.5, 64, g_V=g_V)
     lc, oc = cfgs(w)
     max_pages = 7
     lens_list = [(0, 0, 0), (5, 0, 0), (32, 0, 0), (32, 0, 77), (32, 0, 128), (32, 1, 0),
@@ -488,12 +493,42 @@ def test_paged_decode_equals_contiguous(case):
     torch.cuda.synchronize()
     say(f"[paged] {name} B={B} pages={n_pages} table={mp} blocks={n_blocks}")
     assert torch.equal(out_p, out_c)
+    # against the oracle: the first sequence and the last, and a ragged one (fewer pages, the
+    # same residual rows), each placed by the oracle from the fp16 tokens
+    _, oc = cfgs(w)
+    lens_h = c.lens.cpu().numpy()
+    mask_h = c.mask.cpu().numpy().view(np.uint32)
+    out_h = out_p.cpu().numpy()
+    kh, vh = u16(k), u16(v)
+    picks = sorted({0, B - 1} | ({2} if ragged and B > 2 else set()))
+    res0 = w.N_s + n_pages * w.N
+    for b in picks:
+        s_, npg, r = (int(x) for x in lens_h[b, :3])
+        kp = np.zeros((H, max(npg, 1), kpb), np.uint8)
+        vp = np.zeros((H, max(npg, 1), vpb), np.uint8)
+        for h in range(H):
+            for p in range(npg):
+                a = w.N_s + p * w.N
+                kp[h, p] = oracle.quantize_k_page(oc, kh[b, h, a:a + w.N], mask_h[b, h])
+                vp[h, p] = oracle.quantize_v_page(oc, vh[b, h, a:a + w.N])
+        ks = np.zeros((H, w.N_s, w.d), np.uint16)
+        vs = np.zeros_like(ks)
+        ks[:, :s_], vs[:, :s_] = kh[b, :, :s_], vh[b, :, :s_]
+        kr = np.zeros((H, w.N, w.d), np.uint16)
+        vr = np.zeros_like(kr)
+        kr[:, :r], vr[:, :r] = kh[b, :, res0:res0 + r], vh[b, :, res0:res0 + r]
+        ref = oracle.decode_attn_f64(oc, u16(qd[b]), ks, vs, kp, vp, kr, vr, mask_h[b], s_, npg,
+                                     r, sm_scale(w.d))
+        err = np.abs(out_h[b] - ref).max()
+        say(f"   b={b} lens={s_, npg, r} max|err|={err:.3e}")
+        assert err <= ATOL, (name, b, err)
 
 
-def test_decode_without_pages_both_entry_points():
+@BOTH_KERNELS
+def test_decode_without_pages_both_entry_points(g_V):
     """max_pages = 0 (sinks and residual rows only): both decode entry points, against the
     oracle, with ragged sink and residual counts."""
-    w = synth.Workload("nopages", 1, 1, 8, 2, 64, 1, 1e4, 64, 1024, 0.5, 64, g_V=16)
+    w = synth.Workload("nopages", 1, 1, 8, 2, 64, 1, 1e4, 64, 1024, 0.5, 64, g_V=g_V)
     lc, oc = cfgs(w)
     lens_list = [(0, 0, 0), (7, 0, 0), (32, 0, 0), (32, 0, 1), (32, 0, 128), (32, 0, 65)]
     B = len(lens_list)
@@ -546,11 +581,12 @@ def test_decode_without_pages_both_entry_points():
         assert err <= ATOL, (lens_list[b], err)
 
 
-def test_fused_step_equals_append_then_attend():
+@BOTH_KERNELS
+def test_fused_step_equals_append_then_attend(g_V):
     """pnmix_append_decode_attn (the cache's step) against pnmix_append_kv + pnmix_decode_attn,
     bit for bit, from a 5-token prompt: sinks filling, residual rows, a page flush; then a
     sequence whose residual buffer is full takes no new row."""
-    w = synth.Workload("fused", 1, 2, 8, 2, 64, 1, 1e4, 5, 5 + 200, 0.5, 64, g_V=16)
+    w = synth.Workload("fused", 1, 2, 8, 2, 64, 1, 1e4, 5, 5 + 200, 0.5, 64, g_V=g_V)
     lc, _ = cfgs(w)
     T = w.T
     max_pages = (T - w.N_s) // w.N + 1
@@ -613,3 +649,53 @@ def test_decode_many_splits():
     err = np.abs(out[0].cpu().numpy() - ref).max()
     say(f"   max|err|={err:.3e}")
     assert err <= ATOL
+
+
+FUSED_ORACLE_CASES = [
+    # workload, sampled sequences: one fused step over T - 1 cached tokens -> T tokens
+    ("qwen3-8b-1L-32k", (0,)),
+    ("qwen3-32b-64L-b32-32k", (0, 17, 31)),
+]
+
+
+@pytest.mark.parametrize("wname,picks", FUSED_ORACLE_CASES, ids=[c[0] for c in FUSED_ORACLE_CASES])
+def test_fused_step_against_the_oracle(wname, picks):
+    """pnmix_append_decode_attn (what the benchmark times) at full shape: a cache of T - 1 tokens
+    (bulk filled), then one fused step appends token T - 1 and attends over all T; the outputs of
+    sampled sequences are within 2e-3 of the float64 oracle over the same T tokens, and the new
+    rows and lengths are in place."""
+    w = synth.WORKLOADS[wname]
+    lc, oc = cfgs(w)
+    T = w.T
+    say(f"[fused-oracle] {wname} B={w.B} T={T}")
+    qp, k, v, qd = layer_inputs(w, 12, w.B, T)
+    c = fill_cache_bulk(w, lc, qp, k, v, T - 1, max_pages=(T - w.N_s) // w.N + 1)
+    out = c.step(qd, k[:, :, T - 1].contiguous(), v[:, :, T - 1].contiguous())
+    torch.cuda.synchronize()
+    assert (c.sink_len, c.n_pages, c.res_len) == (w.N_s, w.n_pages, w.res_len)
+    assert torch.equal(c.lens[:, :3].cpu(), torch.tensor([[w.N_s, w.n_pages, w.res_len]] * w.B,
+                                                          dtype=torch.int32))
+    assert torch.equal(c.k_res[:, :, w.res_len - 1], k[:, :, T - 1])
+    out_h = out.cpu().numpy()
+    for b in picks:
+        ref = oracle_decode(w, oc, u16(qp[b]), u16(k[b]), u16(v[b]), u16(qd[b]), T,
+                            sm_scale(w.d))
+        err = np.abs(out_h[b] - ref).max()
+        say(f"   b={b} max|err|={err:.3e}")
+        assert err <= ATOL, (wname, b, err)
+
+
+def test_score_folded_batch_above_65535():
+    """Layers folded into the batch: 1,700 sequences x (32 + 8) heads = 68,000 (sequence, head)
+    rows of Llama-3.1-8B shape, beyond a grid y dimension; sampled sequences bit-exact."""
+    w = synth.WORKLOADS["llama3.1-8b-32L-b110-8k"]
+    lc, oc = cfgs(w)
+    B, P_ = 1700, 24
+    say(f"[score-folded] B={B} P={P_}")
+    qp, k, _, _ = layer_inputs(w, 0, B, P_, P_)
+    sigma, mask = P.pnmix_score_prefill(lc, qp, k)
+    torch.cuda.synchronize()
+    for b in (0, 977, B - 1):
+        _, _, s, m = oracle.score_prefill(oc, u16(qp[b]), u16(k[b]))
+        assert np.array_equal(sigma[b].cpu().numpy().view(np.uint32), s.view(np.uint32)), b
+        assert np.array_equal(mask[b].cpu().numpy().view(np.uint32), m), b

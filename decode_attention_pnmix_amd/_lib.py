@@ -75,6 +75,9 @@ def lib() -> ctypes.CDLL:
         "pnmix_commit_page": (st, [cp, i32, i32, P, P]),
         "pnmix_dequant_k_pages": (st, [cp, i32, P, P, P, P]),
         "pnmix_dequant_v_pages": (st, [cp, i32, P, P, P]),
+        "pnmix_noalloc_scratch_bytes": (sz, []),
+        "pnmix_decode_attn_noalloc": (st, [cp, i32, i32, P, P, P, P, P, P, P, P, P,
+                                           ctypes.c_float, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -89,7 +92,8 @@ EXPORTED = ("pnmix_check_cfg", "pnmix_hi_pairs", "pnmix_mask_words", "pnmix_k_pa
             "pnmix_decode_workspace_bytes", "pnmix_last_error", "pnmix_score_prefill",
             "pnmix_quantize_k_page", "pnmix_quantize_v_page", "pnmix_decode_attn",
             "pnmix_append_kv", "pnmix_commit_page", "pnmix_decode_attn_paged",
-            "pnmix_append_decode_attn", "pnmix_dequant_k_pages", "pnmix_dequant_v_pages")
+            "pnmix_append_decode_attn", "pnmix_dequant_k_pages", "pnmix_dequant_v_pages",
+            "pnmix_noalloc_scratch_bytes", "pnmix_decode_attn_noalloc")
 
 
 def _check(status: int):
@@ -235,6 +239,33 @@ def pnmix_decode_attn(cfg, q, k_sink, v_sink, k_pages, v_pages, k_res, v_res, le
                                    _ptr(v_res), _ptr(lens), _ptr(mask), float(sm_scale),
                                    _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)))
+    return out
+
+
+def pnmix_noalloc_scratch_bytes() -> int:
+    return int(lib().pnmix_noalloc_scratch_bytes())
+
+
+def pnmix_decode_attn_noalloc(cfg, q, k_sink, v_sink, k_pages, v_pages, k_res, v_res, lens, mask,
+                              sm_scale: float, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """pnmix_decode_attn whose split-K partials live in the library's own device array (the call
+    allocates nothing; `out` must be given).  Calls that overlap on one GPU race."""
+    B = q.shape[0]
+    max_pages = k_pages.shape[1]
+    _expect(q, (B, cfg.H_q, cfg.d), _F16, "q")
+    _expect(k_sink, (B, cfg.H_kv, cfg.N_s, cfg.d), _F16, "k_sink")
+    _expect(v_sink, (B, cfg.H_kv, cfg.N_s, cfg.d), _F16, "v_sink")
+    _expect(k_pages, (B, max_pages, cfg.H_kv, pnmix_k_page_bytes(cfg)), _U8, "k_pages")
+    _expect(v_pages, (B, max_pages, cfg.H_kv, pnmix_v_page_bytes(cfg)), _U8, "v_pages")
+    _expect(k_res, (B, cfg.H_kv, cfg.N, cfg.d), _F16, "k_res")
+    _expect(v_res, (B, cfg.H_kv, cfg.N, cfg.d), _F16, "v_res")
+    _expect(lens, (B, 4), _U32, "lens")
+    _expect(mask, (B, cfg.H_kv, pnmix_mask_words(cfg)), _U32, "mask")
+    _expect(out, (B, cfg.H_q, cfg.d), (torch.float32,), "out")
+    _check(lib().pnmix_decode_attn_noalloc(ctypes.byref(cfg), B, max_pages, _ptr(q), _ptr(k_sink),
+                                           _ptr(v_sink), _ptr(k_pages), _ptr(v_pages),
+                                           _ptr(k_res), _ptr(v_res), _ptr(lens), _ptr(mask),
+                                           float(sm_scale), _ptr(out), _stream(stream)))
     return out
 
 

@@ -6,9 +6,17 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "kernels.h"
 #include "pnmix.h"
+
+// Split-K partials of pnmix_decode_attn_noalloc: a device array the library owns, one copy per
+// GPU (each device that loads the library holds its own until the process ends).  Host code
+// never passes this name to a kernel: it is the host-side stand-in of the symbol, and the
+// device address comes from hipGetSymbolAddress (scratch_ptr below).
+static constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -218,6 +226,64 @@ pnmix_status pnmix_append_decode_attn(const pnmix_cfg* c, int32_t B, int32_t max
                                          k_res, v_res, lens, mask, sm_scale, out, ws,
                                          (hipStream_t)stream, nullptr, 0, k_new, v_new, lens_out),
                     "pnmix_append_decode_attn");
+}
+
+// Device address of this GPU's scratch array, looked up once per device with that device
+// current (the first call on the device; later calls reuse it).
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static pnmix_status scratch_ptr(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "pnmix_decode_attn_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PNMIX_E_UNSUPPORTED, "pnmix_decode_attn_noalloc: device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t s = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (s != hipSuccess || !ptr)
+      return hip_status(s != hipSuccess ? s : hipErrorInvalidSymbol,
+                        "pnmix_decode_attn_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PNMIX_OK;
+}
+
+size_t pnmix_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+pnmix_status pnmix_decode_attn_noalloc(const pnmix_cfg* c, int32_t B, int32_t max_pages,
+                                       const uint16_t* q, const uint16_t* k_sink,
+                                       const uint16_t* v_sink, const uint8_t* k_pages,
+                                       const uint8_t* v_pages, const uint16_t* k_res,
+                                       const uint16_t* v_res, const pnmix_seq_len* lens,
+                                       const uint32_t* mask, float sm_scale, float* out,
+                                       void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (B <= 0 || max_pages < 0)
+    return fail(PNMIX_E_INVALID, "B = %d must be positive, max_pages = %d >= 0", B, max_pages);
+  const size_t need = pnmix::decode_plan(*c, B, max_pages).ws_bytes;
+  if (need > kScratchBytes)
+    return fail(PNMIX_E_WORKSPACE,
+                "pnmix_decode_attn_noalloc: B = %d, max_pages = %d need %zu bytes of split-K "
+                "partials, more than the library's %zu-byte scratch (use pnmix_decode_attn with "
+                "a workspace)", B, max_pages, need, kScratchBytes);
+  // the fake workspace pointer only passes the NULL check; the real one replaces it below
+  s = check_decode(c, B, max_pages, q, k_sink, v_sink, k_pages, v_pages, k_res, v_res, lens, mask,
+                   sm_scale, out, reinterpret_cast<void*>(static_cast<uintptr_t>(256)),
+                   kScratchBytes);
+  if (s != PNMIX_OK) return s;
+  void* ws = nullptr;
+  s = scratch_ptr(&ws);
+  if (s != PNMIX_OK) return s;
+  return hip_status(pnmix::launch_decode(*c, B, max_pages, q, k_sink, v_sink, k_pages, v_pages,
+                                         k_res, v_res, lens, mask, sm_scale, out, ws,
+                                         (hipStream_t)stream),
+                    "pnmix_decode_attn_noalloc");
 }
 
 pnmix_status pnmix_decode_attn_paged(const pnmix_cfg* c, int32_t B, int32_t max_blocks,

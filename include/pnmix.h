@@ -209,6 +209,27 @@ pnmix_status pnmix_append_decode_attn(const pnmix_cfg* cfg, int32_t B, int32_t m
                                       const uint32_t* mask, float sm_scale, float* out, void* ws,
                                       size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): pnmix_decode_attn with the same arguments except the
+ * workspace, whose split-K partials go to a device array the library owns instead, one per GPU
+ * (pnmix_noalloc_scratch_bytes() bytes, 32 MiB, held by each GPU the library runs on until the
+ * process ends).  The call allocates nothing (no hipMalloc, no allocating library routine);
+ * its first call on a device looks the array's address up once (hipGetSymbolAddress).
+ * Results are those of pnmix_decode_attn, bit for bit.  A batch whose partials exceed the
+ * array (pnmix_decode_workspace_bytes(cfg, B, max_pages) > pnmix_noalloc_scratch_bytes())
+ * returns PNMIX_E_WORKSPACE before any launch.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (different streams, or threads) race and must be serialised by
+ * the caller.  Nothing in the array needs to start at zero (every partial is written before it
+ * is read). */
+size_t pnmix_noalloc_scratch_bytes(void);
+pnmix_status pnmix_decode_attn_noalloc(const pnmix_cfg* cfg, int32_t B, int32_t max_pages,
+                                       const uint16_t* q, const uint16_t* k_sink,
+                                       const uint16_t* v_sink, const uint8_t* k_pages,
+                                       const uint8_t* v_pages, const uint16_t* k_res,
+                                       const uint16_t* v_res, const pnmix_seq_len* lens,
+                                       const uint32_t* mask, float sm_scale, float* out,
+                                       void* stream);
+
 /* Decode attention over pages held in a shared pool through a block table ([BLOG] "How it
  * composes with paging, GQA and offload": a page of the quantized cache is a fixed-size block
  * carrying its own scales, so quantized pages slot into paged attention's block pool).  Same

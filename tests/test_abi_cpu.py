@@ -102,6 +102,24 @@ def test_decode_plan_queries():
             assert 1 <= s <= min(mp + 2, 136)
 
 
+def test_noalloc_rejects_oversized_batches_before_any_launch():
+    """pnmix_decode_attn_noalloc's partials live in the library's fixed device array: a batch
+    that needs more is refused with PNMIX_E_WORKSPACE and a message, before any HIP call."""
+    lib = P.lib()
+    cap = P.pnmix_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    c = _cfg()
+    big = 4096
+    assert P.pnmix_decode_workspace_bytes(c, big, 255) > cap
+    args = [FAKE] * 9
+    st = lib.pnmix_decode_attn_noalloc(ctypes.byref(c), big, 255, *args, ctypes.c_float(0.088),
+                                       FAKE, None)
+    assert st == L.PNMIX_E_WORKSPACE
+    assert "scratch" in P.pnmix_last_error()
+    assert lib.pnmix_decode_attn_noalloc(ctypes.byref(c), 4, 10, None, *args[1:],
+                                         ctypes.c_float(0.088), FAKE, None) == L.PNMIX_E_INVALID
+
+
 def test_score_accepts_a_folded_batch_above_65535():
     """Layers fold into the batch: Llama-3.1-8B's 32 layers x B = 110 x (32 + 8) heads is 140,800
     (sequence, head) rows, above the 65,535 limit of a grid's y dimension.  Validation passes;

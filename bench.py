@@ -1,10 +1,10 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the PN-Mix key-cache path on one MI355X.
 
-One step = one generation step of every layer through the library: place the new key/value
-rows (pnmix_append_kv), decode attention over sinks + packed pages + fp16 residual
-(pnmix_decode_attn), and -- whenever a residual buffer reaches N tokens -- quantize it into a
-page (pnmix_quantize_k_page / pnmix_quantize_v_page, pnmix_commit_page).  The caches are built
+One step = one generation step of every layer through the library: one fused call per layer
+places the new key/value rows and attends over sinks + packed pages + fp16 residual
+(pnmix_append_decode_attn), and -- whenever a residual buffer reaches N tokens -- it is
+quantized into a page (pnmix_quantize_kv_pages, pnmix_commit_page).  The caches are built
 before timing from seeded synthetic inputs (prefill score of the first P tokens, bulk page
 quantization); W warm-up steps run eagerly, then the K timed steps are captured once in a HIP
 graph and replayed between device synchronisations, so host launch overhead stays out of the
@@ -14,8 +14,10 @@ last-level cache and every step reads HBM.
 
 Prints ONE JSON line: throughput in KV token-heads per second (sum over steps and layers of
 B * cached tokens * H_kv / elapsed), the decode call's roofline (algorithmic bytes per call /
-event-timed duration of the call), page-quantization and prefill-score sub-measurements, and
-the CPU oracle timed on a bounded sample of the same workload.
+event-timed duration of the call: median, p10 and p90 over >= 20 replays), a plain device copy's
+bandwidth beside it, page-quantization and prefill-score sub-measurements, and the CPU oracle
+timed on a bounded sample of the same workload.  The default workload is the largest one that
+fits one GPU: Qwen3-32B shape, 64 layers, B = 32, 32K cached tokens (46 GB of packed cache).
 """
 from __future__ import annotations
 
@@ -27,7 +29,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "qwen3-8b-1L-32k"
+DEFAULT_WORKLOAD = "qwen3-32b-64L-b32-32k"
 
 
 def _say(*a):
@@ -45,48 +47,56 @@ def decode_bytes(cfg, lens, B, kpb, vpb):
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-DECODE_SRC = os.path.join(ROOT, "decode_attention_pnmix_amd", "csrc", "decode.hip")
+CSRC = os.path.join(ROOT, "decode_attention_pnmix_amd", "csrc")
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("decode.hip", "decode_args.h", "common.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_MB = 256  # plain device copy that calibrates the HBM byte counters
 
 
-def _sha(path):
+def _sha(paths):
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, lens):
-    """HBM bytes per decode call from the committed counter summary of this workload, or None
-    when there is none or the decode kernels changed since the counters were taken."""
+def measured_traffic(workload, call_bytes):
+    """HBM bytes per decode call from the committed counter summary of this workload, scaled by
+    the ratio of algorithmic bytes (the call measured here may hold a few more or fewer tokens
+    than the profiled one), or None when there is no summary or the decode kernels changed
+    since the counters were taken."""
     path = os.path.join(PROFILES, f"decode_attn_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("decode_src_sha256_16") != _sha(DECODE_SRC) or t.get("lens") != list(lens):
+    if t.get("decode_src_sha256_16") != _sha(DECODE_SRCS) or not t.get("algorithmic_bytes"):
         return None
-    return t["hbm_bytes_per_call"]
+    return t["hbm_bytes_per_call"] * call_bytes / t["algorithmic_bytes"]
 
 
-def pmc_summary(fetch_dir, write_dir, workload, lens):
-    """Summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE): per
-    dispatch KiB of the decode kernels at the last decode call of the run, each scaled by the
-    ratio of the known bytes of the calibration copy to what the same counter reads for it."""
+def _csv_rows(d, suffix):
     import csv
     import glob
+    out = []
+    for fn in glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True):
+        with open(fn) as f:
+            out += list(csv.DictReader(f))
+    return out
 
-    def rows(d):
-        out = []
-        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            with open(fn) as f:
-                out += list(csv.DictReader(f))
-        out.sort(key=lambda r: int(r["Dispatch_Id"]))
-        return out
 
-    res = {}
+def pmc_summary(fetch_dir, write_dir, workload, lens, call_bytes):
+    """Summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by the ratio of the known bytes of the calibration copy to what the
+    same counter reads for it: the decode call at the last decode of the run (split + merge
+    kernel, the roofline call), and for every pnmix kernel its bytes per workgroup over all its
+    dispatches (a page for the quantizers, a 64-token chunk of one head for the score)."""
+    res, per_kernel = {}, {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rs = [r for r in rows(d) if r["Counter_Name"] == name]
+        rs = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == name]
+        rs.sort(key=lambda r: int(r["Dispatch_Id"]))
         copy = [float(r["Counter_Value"]) for r in rs
                 if "copybuffer" in r["Kernel_Name"].lower() or
                 ("elementwise" in r["Kernel_Name"] and "copy" in r["Kernel_Name"].lower())]
@@ -99,9 +109,38 @@ def pmc_summary(fetch_dir, write_dir, workload, lens):
         res[name] = {"copy_counter_bytes": big, "copy_factor": factor,
                      "decode_kernel_bytes": k, "merge_kernel_bytes": m,
                      "decode_kernel_name": dec[-1]["Kernel_Name"]}
+        for r in rs:
+            kn = r["Kernel_Name"]
+            if "pnmix::" not in kn:
+                continue
+            short = kn.split("(")[0].replace("void ", "")
+            wgs = max(1, int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+            s = per_kernel.setdefault(short, {}).setdefault(name, {"dispatches": 0,
+                                                                   "bytes": 0.0, "wgs": 0})
+            s["dispatches"] += 1
+            s["bytes"] += float(r["Counter_Value"]) * 1024.0 * factor
+            s["wgs"] += wgs
+    for kn, ss in per_kernel.items():
+        for name, s in ss.items():
+            s["bytes_per_workgroup"] = s["bytes"] / max(1, s["wgs"])
     total = sum(res[n]["decode_kernel_bytes"] + res[n]["merge_kernel_bytes"] for n in res)
     return {"workload": workload, "lens": list(lens), "counters": res,
-            "hbm_bytes_per_call": total, "decode_src_sha256_16": _sha(DECODE_SRC)}
+            "algorithmic_bytes": call_bytes, "hbm_bytes_per_call": total,
+            "hbm_over_algorithmic": total / call_bytes if call_bytes else None,
+            "per_kernel": per_kernel, "decode_src_sha256_16": _sha(DECODE_SRCS)}
+
+
+def kt_summary(kt_dir):
+    """Text table of a rocprofv3 --kernel-trace --stats run (its kernel_stats.csv)."""
+    rows = _csv_rows(kt_dir, "kernel_stats.csv")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"{'kernel':72s} {'calls':>7s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} "
+             f"{'time %':>7s}"]
+    for r in rows[:24]:
+        lines.append(f"{r['Name'][:72]:72s} {int(r['Calls']):7d} "
+                     f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):7.2f}")
+    return "\n".join(lines)
 
 
 def build_layer(w, cfg, layer, B, T0, max_pages, steps, dev, P, synth, torch):
@@ -123,8 +162,7 @@ def build_layer(w, cfg, layer, B, T0, max_pages, steps, dev, P, synth, torch):
     if n_pages:
         kj, _ = c.page_jobs(k, s, 0, n_pages)
         _, vj = c.page_jobs(v, s, 0, n_pages)
-        P.pnmix_quantize_k_page(cfg, kj, c.mask)
-        P.pnmix_quantize_v_page(cfg, vj)
+        P.pnmix_quantize_kv_pages(cfg, kj, vj, c.mask)
     a = s + n_pages * w.N
     rest = T0 - a
     c.k_res[:, :, :rest] = k[:, :, a:T0]
@@ -221,17 +259,27 @@ def main():
                     help="run a workload with fewer layers over this many distinct layer copies")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--roofline-reps", type=int, default=5)
+    ap.add_argument("--roofline-reps", type=int, default=24,
+                    help="timed replays of the per-layer decode calls (p10 / median / p90)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"run one plain {COPY_MB} MiB device copy (HBM counter calibration)")
+    ap.add_argument("--profile-step", action="store_true",
+                    help="stop after the decode-call timing (short runs under a profiler)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of this script and exit (no GPU)")
     ap.add_argument("--lens", type=int, nargs=3, metavar=("SINK", "PAGES", "RES"),
                     help="with --pmc-summary: the cache lengths of the profiled decode call")
+    ap.add_argument("--call-bytes", type=int,
+                    help="with --pmc-summary: algorithmic bytes of the profiled decode call")
+    ap.add_argument("--kt-summary", metavar="KT_DIR",
+                    help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
     args = ap.parse_args()
+    if args.kt_summary:
+        print(kt_summary(args.kt_summary))
+        return
     if args.pmc_summary:
         print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload,
-                                     args.lens), indent=1))
+                                     args.lens, args.call_bytes), indent=1))
         return
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -251,8 +299,7 @@ def main():
     dev = "cuda"
     w = synth.WORKLOADS[args.workload]
     cfg = P.make_cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_H=w.b_H, b_L=w.b_L,
-                    b_V=w.b_V, g_V=w.g_V,
-                     N_s=w.N_s, N=w.N)
+                     b_V=w.b_V, g_V=w.g_V, N_s=w.N_s, N=w.N)
     kpb, vpb = P.pnmix_k_page_bytes(cfg), P.pnmix_v_page_bytes(cfg)
     W, K = args.warmup, args.steps
     layers = max(w.layers, args.min_layers)
@@ -279,6 +326,8 @@ def main():
         del raw
         for s in range(c.n_pages, max_pages):  # page jobs of every flush slot, built up front
             c.flush_jobs(s)
+        if layer % 8 == 7:
+            _say(f"[bench] {layer + 1} layers built ({time.perf_counter() - t_build:.1f} s)")
     torch.cuda.synchronize()
     _say(f"[bench] caches built in {time.perf_counter() - t_build:.1f} s")
 
@@ -351,13 +400,15 @@ def main():
         torch.cuda.synchronize()
         if rep:
             durs.append(e0.elapsed_time(e1) * 1e-3 / layers)
-    call_s = float(np.mean(durs))
+    call_s = float(np.median(durs))
+    call_p10, call_p90 = float(np.percentile(durs, 10)), float(np.percentile(durs, 90))
     call_bytes = decode_bytes(cfg, lens_now, w.B, kpb, vpb)
     achieved = call_bytes / call_s / 1e9
-    _say(f"[bench] decode call: {call_bytes / 1e6:.2f} MB in {call_s * 1e6:.2f} us avg "
-         f"(min {np.min(durs) * 1e6:.2f}) -> {achieved:.0f} GB/s")
-    traffic = measured_traffic(w.name, lens_now)
-    _say(f"[bench] decode call lens (sink, pages, residual) = {lens_now}")
+    _say(f"[bench] decode call: {call_bytes / 1e6:.2f} MB in {call_s * 1e6:.2f} us median "
+         f"(p10 {call_p10 * 1e6:.2f}, p90 {call_p90 * 1e6:.2f}) -> {achieved:.0f} GB/s")
+    traffic = measured_traffic(w.name, call_bytes)
+    _say(f"[bench] decode call lens (sink, pages, residual) = {lens_now}, "
+         f"algorithmic bytes {call_bytes}")
     if args.copy_calibration:
         src = torch.empty(COPY_MB * 2**20 // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -365,8 +416,29 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.profile_step:
+        print(json.dumps({"profile_step": True, "workload": w.name, "lens": lens_now,
+                          "call_bytes": call_bytes, "call_us": call_s * 1e6}), flush=True)
+        return
 
-    # ---- page quantization: one bulk launch per kernel over every layer's residual buffers
+    # ---- a plain device-to-device copy of 1 GiB: the HBM rate this machine reaches
+    cp_src = torch.empty(2**28, dtype=torch.float32, device=dev).fill_(1.0)
+    cp_dst = torch.empty_like(cp_src)
+    cts = []
+    for rep in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cp_dst.copy_(cp_src)
+        e1.record()
+        torch.cuda.synchronize()
+        if rep:
+            cts.append(e0.elapsed_time(e1) * 1e-3)
+    copy_GBps = 2 * cp_src.numel() * 4 / float(np.median(cts)) / 1e9
+    del cp_src, cp_dst
+    _say(f"[bench] device copy: {copy_GBps:.0f} GB/s (read + write)")
+
+    # ---- page quantization: one fill event of every layer's residual buffers, key and value
+    # pages in one launch (and, for reference, as two launches)
     n_jobs = layers * w.B * w.H_kv
     scratch_k = torch.empty(n_jobs, kpb, dtype=torch.uint8, device=dev)
     scratch_v = torch.empty(n_jobs, vpb, dtype=torch.uint8, device=dev)
@@ -382,25 +454,34 @@ def main():
             rows.append(j)
     kj = P.page_jobs(srcs_k, w.d, dk, rows, dev)
     vj = P.page_jobs(srcs_v, w.d, dv, rows, dev)
-    qk_t, qv_t = [], []
-    for rep in range(6):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    qkv_t, qk_t, qv_t = [], [], []
+    for rep in range(8):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         e[0].record()
-        P.pnmix_quantize_k_page(cfg, kj, masks)
+        P.pnmix_quantize_kv_pages(cfg, kj, vj, masks)
         e[1].record()
-        P.pnmix_quantize_v_page(cfg, vj)
+        P.pnmix_quantize_k_page(cfg, kj, masks)
         e[2].record()
+        P.pnmix_quantize_v_page(cfg, vj)
+        e[3].record()
         torch.cuda.synchronize()
         if rep:
-            qk_t.append(e[0].elapsed_time(e[1]) * 1e-3)
-            qv_t.append(e[1].elapsed_time(e[2]) * 1e-3)
-    tk, tv = float(np.median(qk_t)), float(np.median(qv_t))
+            qkv_t.append(e[0].elapsed_time(e[1]) * 1e-3)
+            qk_t.append(e[1].elapsed_time(e[2]) * 1e-3)
+            qv_t.append(e[2].elapsed_time(e[3]) * 1e-3)
+    tkv, tk, tv = (float(np.median(x)) for x in (qkv_t, qk_t, qv_t))
     kbytes = n_jobs * (w.N * w.d * 2 + kpb)
     vbytes = n_jobs * (w.N * w.d * 2 + vpb)
-    quant = {"pages_per_launch": n_jobs, "k_us": tk * 1e6, "v_us": tv * 1e6,
-             "k_GBps": kbytes / tk / 1e9, "v_GBps": vbytes / tv / 1e9,
-             "kv_GBps": (kbytes + vbytes) / (tk + tv) / 1e9,
-             "kv_frac_of_peak": (kbytes + vbytes) / (tk + tv) / 1e9 / HBM_PEAK_GBS}
+    quant = {"pages_per_launch": 2 * n_jobs, "kernel": "quantize_kv_kernel (K and V pages in one "
+             "launch)", "kv_us": tkv * 1e6, "kv_us_p10": float(np.percentile(qkv_t, 10)) * 1e6,
+             "kv_us_p90": float(np.percentile(qkv_t, 90)) * 1e6,
+             "kv_GBps": (kbytes + vbytes) / tkv / 1e9,
+             "kv_frac_of_peak": (kbytes + vbytes) / tkv / 1e9 / HBM_PEAK_GBS,
+             "separate_launches": {"k_us": tk * 1e6, "v_us": tv * 1e6,
+                                   "k_GBps": kbytes / tk / 1e9, "v_GBps": vbytes / tv / 1e9}}
+    _say(f"[bench] page quant, {2 * n_jobs} pages in one launch: {tkv * 1e6:.1f} us, "
+         f"{quant['kv_GBps']:.0f} GB/s ({quant['kv_frac_of_peak'] * 100:.1f}%)")
+    del scratch_k, scratch_v
 
     # ---- prefill score of one layer's prompt batch (and the long prefill if the workload has one)
     score = {}
@@ -428,8 +509,17 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and sample:
-        threads = max(1, min(16, os.cpu_count() or 1))
+        host_cpus = os.cpu_count() or 1
+        try:
+            affinity = len(os.sched_getaffinity(0))
+        except AttributeError:
+            affinity = host_cpus
+        # the machine's CPU share for one GPU caps the pool (OMP_NUM_THREADS states it there)
+        share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or affinity
+        threads = max(1, min(affinity, share))
         cpu = cpu_baseline(w, sample, args.cpu_seconds, threads)
+        cpu["host_cpus"] = host_cpus
+        cpu["affinity_cpus"] = affinity
 
     line = {
         "metric": "decode-attn KV tokens·heads/s & % of HBM peak; K/V page-quant GB/s",
@@ -446,14 +536,18 @@ def main():
         "data": "synthetic (seeded; log-normal persistent pair outliers, RoPE, V ~ N(0,1))",
         "config": {"workload": w.name, "layers": w.layers, "layer_copies_per_step": layers,
                    "global_batch": w.B, "kv_tokens_at_first_timed_step": w.T, "H_q": w.H_q,
-                   "H_kv": w.H_kv, "head_dim": w.d, "r": w.r, "G": w.G, "b_H": 3, "b_L": 1,
-                   "b_V": w.b_V, "g_V": w.g_V, "N_s": w.N_s, "N": w.N,
+                   "H_kv": w.H_kv, "head_dim": w.d, "r": w.r, "G": w.G, "b_H": w.b_H,
+                   "b_L": w.b_L, "b_V": w.b_V, "g_V": w.g_V, "N_s": w.N_s, "N": w.N,
                    "parallelism": "single GPU", "timed": "one HIP graph of K steps"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "pnmix_decode_attn = decode_kernel (page and fp16 splits) + "
-                               "decode_merge_kernel, one call",
-                     "bytes_per_call": call_bytes, "avg_call_us": call_s * 1e6},
+                               "decode_merge_kernel, one call per layer",
+                     "bytes_per_call": call_bytes, "avg_call_us": call_s * 1e6,
+                     "call_us_p10": call_p10 * 1e6, "call_us_p90": call_p90 * 1e6,
+                     "timed_replays": len(durs), "lens": list(lens_now),
+                     "device_copy_GBps": copy_GBps,
+                     "frac_of_device_copy": achieved / copy_GBps},
         "page_quant": quant,
         "prefill_score": score,
         "cpu_baseline": cpu,

@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         "pnmix_score_prefill": (st, [cp, i32, i32, P, P, P, P, P, sz, P]),
         "pnmix_quantize_k_page": (st, [cp, i32, P, P, P]),
         "pnmix_quantize_v_page": (st, [cp, i32, P, P]),
+        "pnmix_quantize_kv_pages": (st, [cp, i32, P, P, P, P]),
         "pnmix_decode_attn": (st, [cp, i32, i32, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P,
                                    sz, P]),
         "pnmix_decode_attn_paged": (st, [cp, i32, i32, P, P, P, P, P, ctypes.c_int64, P, P, P,
@@ -93,7 +94,8 @@ EXPORTED = ("pnmix_check_cfg", "pnmix_hi_pairs", "pnmix_mask_words", "pnmix_k_pa
             "pnmix_quantize_k_page", "pnmix_quantize_v_page", "pnmix_decode_attn",
             "pnmix_append_kv", "pnmix_commit_page", "pnmix_decode_attn_paged",
             "pnmix_append_decode_attn", "pnmix_dequant_k_pages", "pnmix_dequant_v_pages",
-            "pnmix_noalloc_scratch_bytes", "pnmix_decode_attn_noalloc")
+            "pnmix_noalloc_scratch_bytes", "pnmix_decode_attn_noalloc",
+            "pnmix_quantize_kv_pages")
 
 
 def _check(status: int):
@@ -209,6 +211,15 @@ def pnmix_quantize_k_page(cfg, jobs: torch.Tensor, mask: torch.Tensor, stream=No
 def pnmix_quantize_v_page(cfg, jobs: torch.Tensor, stream=None) -> None:
     _check(lib().pnmix_quantize_v_page(ctypes.byref(cfg), jobs.shape[0], _ptr(jobs),
                                        _stream(stream)))
+
+
+def pnmix_quantize_kv_pages(cfg, kjobs: torch.Tensor, vjobs: torch.Tensor, mask: torch.Tensor,
+                            stream=None) -> None:
+    """Key and value page jobs (same count) in one launch."""
+    if kjobs.shape != vjobs.shape:
+        raise ValueError("pnmix: key and value job arrays differ in shape")
+    _check(lib().pnmix_quantize_kv_pages(ctypes.byref(cfg), kjobs.shape[0], _ptr(kjobs),
+                                         _ptr(vjobs), _ptr(mask), _stream(stream)))
 
 
 def pnmix_decode_attn(cfg, q, k_sink, v_sink, k_pages, v_pages, k_res, v_res, lens, mask,

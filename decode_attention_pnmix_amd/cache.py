@@ -93,8 +93,7 @@ class PNMixLayerCache:
         if n_full:
             kj, _ = self.page_jobs(k, s, 0, n_full)
             _, vj = self.page_jobs(v, s, 0, n_full)
-            L.pnmix_quantize_k_page(cfg, kj, self.mask)
-            L.pnmix_quantize_v_page(cfg, vj)
+            L.pnmix_quantize_kv_pages(cfg, kj, vj, self.mask)
             torch.cuda.current_stream().synchronize()  # jobs reference k, v
         rest = P - s - n_full * cfg.N
         a = s + n_full * cfg.N
@@ -129,8 +128,7 @@ class PNMixLayerCache:
         if n_full:
             kj, _ = self.page_jobs(k, s, 0, n_full)
             _, vj = self.page_jobs(v, s, 0, n_full)
-            L.pnmix_quantize_k_page(cfg, kj, self.mask)
-            L.pnmix_quantize_v_page(cfg, vj)
+            L.pnmix_quantize_kv_pages(cfg, kj, vj, self.mask)
             torch.cuda.current_stream().synchronize()  # jobs reference k, v
         a = s + n_full * cfg.N
         rest = T - a
@@ -175,8 +173,7 @@ class PNMixLayerCache:
         if self.n_pages >= self.max_pages:
             raise RuntimeError("cache capacity exhausted")
         kj, vj = self.flush_jobs(self.n_pages)
-        L.pnmix_quantize_k_page(cfg, kj, self.mask)
-        L.pnmix_quantize_v_page(cfg, vj)
+        L.pnmix_quantize_kv_pages(cfg, kj, vj, self.mask)
         L.pnmix_commit_page(cfg, self.max_pages, self.lens)
         self.n_pages += 1
         self.res_len = 0

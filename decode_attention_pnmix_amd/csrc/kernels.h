@@ -17,6 +17,8 @@ hipError_t launch_quantize_k(const pnmix_cfg& c, int n_pages, const pnmix_page* 
                              const uint32_t* mask, hipStream_t stream);
 hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* pages,
                              hipStream_t stream);
+hipError_t launch_quantize_kv(const pnmix_cfg& c, int n_pages, const pnmix_page* kjobs,
+                              const pnmix_page* vjobs, const uint32_t* mask, hipStream_t stream);
 hipError_t launch_dequant_k(const pnmix_cfg& c, int n_pages, const uint8_t* pages,
                             const uint32_t* mask, float* out, hipStream_t stream);
 hipError_t launch_dequant_v(const pnmix_cfg& c, int n_pages, const uint8_t* pages, float* out,

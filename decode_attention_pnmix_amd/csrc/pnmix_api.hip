@@ -156,6 +156,20 @@ pnmix_status pnmix_quantize_v_page(const pnmix_cfg* c, int32_t n_pages, const pn
                     "pnmix_quantize_v_page");
 }
 
+pnmix_status pnmix_quantize_kv_pages(const pnmix_cfg* c, int32_t n_pages,
+                                     const pnmix_page* k_pages, const pnmix_page* v_pages,
+                                     const uint32_t* mask, void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (n_pages < 0) return fail(PNMIX_E_INVALID, "n_pages = %d < 0", n_pages);
+  if (n_pages == 0) return ok();
+  if (!k_pages || !v_pages || !mask)
+    return fail(PNMIX_E_INVALID, "k_pages, v_pages and mask must be non-NULL");
+  return hip_status(pnmix::launch_quantize_kv(*c, n_pages, k_pages, v_pages, mask,
+                                              (hipStream_t)stream),
+                    "pnmix_quantize_kv_pages");
+}
+
 // Argument checks shared by the contiguous decode entry points (before any HIP call).
 static pnmix_status check_decode(const pnmix_cfg* c, int32_t B, int32_t max_pages,
                                  const uint16_t* q, const uint16_t* k_sink,

@@ -131,18 +131,27 @@ __device__ __forceinline__ uint32_t code_bits_h(uint32_t w, bool high, float nmn
   return __float_as_uint(__builtin_amdgcn_fmed3f(y, 0.0f, L) + kRound);
 }
 
+// LDS of one key page: (min, max) fp16 per octet and channel, (min, 1/s) per group and
+// channel, the upper-bit plane staging, the salient ranks.
 template <int D>
-__global__ void __launch_bounds__(2 * D) quantize_k_kernel(const pnmix_page* __restrict__ jobs,
-                                                          const uint32_t* __restrict__ mask,
-                                                          int pairing, int n_hi, int G,
-                                                          int words) {
+struct KLds {
+  static constexpr int part = 0;
+  static constexpr int meta = part + kOctets * D * 4;
+  static constexpr int hi = meta + (kN / 32) * D * 8;
+  static constexpr int rank = hi + (kN / 4) * D;
+  static constexpr int bytes = rank + D;
+};
+
+template <int D>
+__device__ __forceinline__ void quantize_k_page(const pnmix_page& job,
+                                                const uint32_t* __restrict__ mask, int pairing,
+                                                int n_hi, int G, int words, uint8_t* lds) {
   constexpr int NB = D / 8;
-  __shared__ __align__(16) uint32_t part[kOctets * D];  // (min, max) fp16 per octet, channel
-  __shared__ __align__(16) float2 meta[(kN / 32) * D];  // (min, 1/s) per group, channel
-  __shared__ __align__(16) uint8_t hi_s[(kN / 4) * D];  // upper-bit plane staging
-  __shared__ __align__(8) int8_t rank_s[D];
+  uint32_t* part = reinterpret_cast<uint32_t*>(lds + KLds<D>::part);
+  float2* meta = reinterpret_cast<float2*>(lds + KLds<D>::meta);
+  uint8_t* hi_s = lds + KLds<D>::hi;
+  int8_t* rank_s = reinterpret_cast<int8_t*>(lds + KLds<D>::rank);
   const int tid = threadIdx.x, b = tid % NB, k = tid / NB;
-  const pnmix_page job = jobs[blockIdx.x];
   const int n_sal = 2 * n_hi;
   uint8_t* lo = job.dst;
   uint8_t* hi = lo + kN * D / 8;
@@ -253,20 +262,37 @@ __global__ void __launch_bounds__(2 * D) quantize_k_kernel(const pnmix_page* __r
     reinterpret_cast<uint4*>(hi)[i] = reinterpret_cast<const uint4*>(hi_s)[i];
 }
 
+template <int D>
+__global__ void __launch_bounds__(2 * D) quantize_k_kernel(const pnmix_page* __restrict__ jobs,
+                                                          const uint32_t* __restrict__ mask,
+                                                          int pairing, int n_hi, int G,
+                                                          int words) {
+  __shared__ __align__(16) uint8_t lds[KLds<D>::bytes];
+  quantize_k_page<D>(jobs[blockIdx.x], mask, pairing, n_hi, G, words, lds);
+}
+
 // Byte [m][t] of a value page holds channels 4m..4m+3 of token t (channel 4m+u in bits
 // 2u..2u+1); the LDS copy of the code bytes keeps rows [m] of N bytes at a stride of kVRow
 // words, which spreads the rows of one store over the banks.
 constexpr int kVRow = kN / 4 + 2;
 
+// LDS of one value page: (min, max) fp16 per token and 8-channel block, (min, 1/s) per token
+// and group (<= 4), the page's code bytes [d/4][N] at a row stride of kVRow words.
 template <int D>
-__global__ void __launch_bounds__(2 * D) quantize_v_kernel(const pnmix_page* __restrict__ jobs,
-                                                          int g_V) {
+struct VLds {
+  static constexpr int part = 0;
+  static constexpr int meta = part + kN * (D / 8) * 4;
+  static constexpr int cw = meta + kN * 4 * 8;
+  static constexpr int bytes = cw + (D / 4) * kVRow * 4;
+};
+
+template <int D>
+__device__ __forceinline__ void quantize_v_page(const pnmix_page& job, int g_V, uint8_t* lds) {
   constexpr int NB = D / 8;
-  __shared__ __align__(16) uint32_t part[kN * NB];      // (min, max) fp16 per token, block
-  __shared__ __align__(16) float2 meta[kN * 4];         // (min, 1/s) per token, group (<= 4)
-  __shared__ __align__(16) uint32_t cw[(D / 4) * kVRow]; // the page's code bytes [d/4][N]
+  uint32_t* part = reinterpret_cast<uint32_t*>(lds + VLds<D>::part);
+  float2* meta = reinterpret_cast<float2*>(lds + VLds<D>::meta);
+  uint32_t* cw = reinterpret_cast<uint32_t*>(lds + VLds<D>::cw);
   const int tid = threadIdx.x, b = tid % NB, k = tid / NB;
-  const pnmix_page job = jobs[blockIdx.x];
   const int ng = D / g_V;
   uint8_t* codes = job.dst;
   uint16_t* S = reinterpret_cast<uint16_t*>(codes + kN * D / 4);  // [ng][N]
@@ -336,6 +362,31 @@ __global__ void __launch_bounds__(2 * D) quantize_v_kernel(const pnmix_page* __r
     const uint2 hi2 = *reinterpret_cast<const uint2*>(src + 2);
     reinterpret_cast<uint4*>(codes)[tid] = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
   }
+}
+
+template <int D>
+__global__ void __launch_bounds__(2 * D) quantize_v_kernel(const pnmix_page* __restrict__ jobs,
+                                                          int g_V) {
+  __shared__ __align__(16) uint8_t lds[VLds<D>::bytes];
+  quantize_v_page<D>(jobs[blockIdx.x], g_V, lds);
+}
+
+// Key and value pages in one launch: workgroup 2i takes key job i, workgroup 2i + 1 value job
+// i, in one LDS allocation the size of the larger of the two, so the launch's last round is
+// shared by both kinds of page.
+template <int D>
+__global__ void __launch_bounds__(2 * D) quantize_kv_kernel(const pnmix_page* __restrict__ kjobs,
+                                                           const pnmix_page* __restrict__ vjobs,
+                                                           const uint32_t* __restrict__ mask,
+                                                           int pairing, int n_hi, int G,
+                                                           int words, int g_V) {
+  constexpr int bytes = KLds<D>::bytes > VLds<D>::bytes ? KLds<D>::bytes : VLds<D>::bytes;
+  __shared__ __align__(16) uint8_t lds[bytes];
+  const int i = blockIdx.x >> 1;
+  if (blockIdx.x & 1)
+    quantize_v_page<D>(vjobs[i], g_V, lds);
+  else
+    quantize_k_page<D>(kjobs[i], mask, pairing, n_hi, G, words, lds);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -549,6 +600,32 @@ hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* 
     default: PNMIX_QV(128) break;
   }
 #undef PNMIX_QV
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_kv(const pnmix_cfg& c, int n_pages, const pnmix_page* kjobs,
+                              const pnmix_page* vjobs, const uint32_t* mask, hipStream_t stream) {
+  if (n_pages == 0) return hipSuccess;
+  if (!(c.b_H == 3 && c.b_L == 1 && c.b_V == 2)) {  // the generic kernels: two launches
+    const hipError_t e = launch_quantize_k(c, n_pages, kjobs, mask, stream);
+    return e != hipSuccess ? e : launch_quantize_v(c, n_pages, vjobs, stream);
+  }
+  const int words = (c.d / 2 + 31) / 32;
+  const dim3 grid(2 * n_pages);
+  switch (c.d) {
+    case 32:
+      hipLaunchKernelGGL(quantize_kv_kernel<32>, grid, dim3(64), 0, stream, kjobs, vjobs, mask,
+                         c.pairing, c.n_hi_pairs, c.G, words, c.g_V);
+      break;
+    case 64:
+      hipLaunchKernelGGL(quantize_kv_kernel<64>, grid, dim3(128), 0, stream, kjobs, vjobs, mask,
+                         c.pairing, c.n_hi_pairs, c.G, words, c.g_V);
+      break;
+    default:
+      hipLaunchKernelGGL(quantize_kv_kernel<128>, grid, dim3(256), 0, stream, kjobs, vjobs, mask,
+                         c.pairing, c.n_hi_pairs, c.G, words, c.g_V);
+      break;
+  }
   return hipGetLastError();
 }
 

@@ -163,6 +163,15 @@ pnmix_status pnmix_quantize_k_page(const pnmix_cfg* cfg, int32_t n_pages,
 pnmix_status pnmix_quantize_v_page(const pnmix_cfg* cfg, int32_t n_pages,
                                    const pnmix_page* pages, void* stream);
 
+/* Key and value pages in one call: pnmix_quantize_k_page on k_pages and pnmix_quantize_v_page
+ * on v_pages (n_pages jobs each, device arrays; mask as for the key jobs), with the same bytes
+ * out, in one launch whose workgroups alternate between key and value pages (the residual
+ * buffer's flush, [PNMIX] sec. 2, quantizes both at once).  Settings other than
+ * (b_H, b_L, b_V) = (3, 1, 2) run as two launches. */
+pnmix_status pnmix_quantize_kv_pages(const pnmix_cfg* cfg, int32_t n_pages,
+                                     const pnmix_page* k_pages, const pnmix_page* v_pages,
+                                     const uint32_t* mask, void* stream);
+
 /* Decode-step GQA attention straight over the packed cache ([PNMIX] Eq. 1, kernel-implementation
  * appendix: sink region, quantized region, residual region, dequantization in registers;
  * [FLASH] split-K partials merged by online log-sum-exp).

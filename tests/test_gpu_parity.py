@@ -104,7 +104,13 @@ def _quant_compare(w, lc, oc, src_gpu, mask_rows_gpu, sample, label):
     vj = P.page_jobs(srcs, w.d, [vd.data_ptr() + i * vpb for i in range(n)], range(n), "cuda")
     P.pnmix_quantize_k_page(lc, kj, mask_rows_gpu)
     P.pnmix_quantize_v_page(lc, vj)
+    # the same jobs as one launch of key and value pages: the same bytes
+    kd2, vd2 = torch.zeros_like(kd), torch.zeros_like(vd)
+    kj2 = P.page_jobs(srcs, w.d, [kd2.data_ptr() + i * kpb for i in range(n)], range(n), "cuda")
+    vj2 = P.page_jobs(srcs, w.d, [vd2.data_ptr() + i * vpb for i in range(n)], range(n), "cuda")
+    P.pnmix_quantize_kv_pages(lc, kj2, vj2, mask_rows_gpu)
     torch.cuda.synchronize()
+    assert torch.equal(kd, kd2) and torch.equal(vd, vd2), f"{label}: one-launch K+V pages differ"
     sh = u16(src_gpu[sample])
     mh = mask_rows_gpu[sample].cpu().numpy().view(np.uint32)
     kg = kd[sample].cpu().numpy()

@@ -97,10 +97,12 @@ def pmc_summary(fetch_dir, write_dir, workload, lens, call_bytes):
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rs = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == name]
         rs.sort(key=lambda r: int(r["Dispatch_Id"]))
-        copy = [float(r["Counter_Value"]) for r in rs
-                if "copybuffer" in r["Kernel_Name"].lower() or
-                ("elementwise" in r["Kernel_Name"] and "copy" in r["Kernel_Name"].lower())]
-        big = max(copy) * 1024.0  # the calibration copy is the largest copy of the run
+        # the calibration copy is the first copy dispatched after the last decode call (the run
+        # makes it right there with --copy-calibration; input generation makes larger copies)
+        last = max(i for i, r in enumerate(rs) if "decode_merge_kernel" in r["Kernel_Name"])
+        copy = [float(r["Counter_Value"]) for r in rs[last + 1:]
+                if "copybuffer" in r["Kernel_Name"].lower() or "copy" in r["Kernel_Name"].lower()]
+        big = copy[0] * 1024.0
         factor = COPY_MB * 2**20 / big
         dec = [r for r in rs if "decode_kernel" in r["Kernel_Name"]]
         mrg = [r for r in rs if "decode_merge_kernel" in r["Kernel_Name"]]

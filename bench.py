@@ -251,6 +251,56 @@ def cpu_baseline(w, sample, seconds, threads):
                                         f"{t_score:.3f} s wall (single-threaded)"}}
 
 
+def prefill_timing(w, cfg, P, synth, torch, np, reps=6):
+    """The prompt of one layer, scored and its full pages quantized: score then one launch of key
+    and value pages (pnmix_score_prefill + pnmix_quantize_kv_pages) against the one-pass
+    pnmix_prefill_fused; median of `reps` event-timed runs each, for the workload's prompt at
+    its batch and its long prompt at B = 1 if it has one."""
+    dev = "cuda"
+    out = {}
+    for (Bs, Ps) in ([(w.B, w.P)] + ([(1, w.prefill_score_P)] if w.prefill_score_P else [])):
+        sq = synth.pair_scales(w.H_q, w.d // 2, w.sigma_ln, dev, w.name, 0, "q")
+        sk = synth.pair_scales(w.H_kv, w.d // 2, w.sigma_ln, dev, w.name, 0, "k")
+        qpp = synth.rope_tokens(sq, Bs, torch.arange(Ps, device=dev), w.d, w.pairing,
+                                w.rope_base, dev, w.name, "prefill", "q")
+        kpp = synth.rope_tokens(sk, Bs, torch.arange(Ps, device=dev), w.d, w.pairing,
+                                w.rope_base, dev, w.name, "prefill", "k")
+        vpp = synth.values(Bs, w.H_kv, Ps, w.d, dev, w.name, "prefill")
+        n_full = max(0, (Ps - w.N_s) // w.N)
+        c = P.PNMixLayerCache(cfg, Bs, max(n_full, 1), dev)
+        kj = vj = None
+        if n_full:
+            kj, _ = c.page_jobs(kpp, w.N_s, 0, n_full)
+            _, vj = c.page_jobs(vpp, w.N_s, 0, n_full)
+        ws_s = torch.empty(P.pnmix_score_workspace_bytes(cfg, Bs, Ps), dtype=torch.uint8,
+                           device=dev)
+        ws_f = torch.empty(P.pnmix_prefill_fused_workspace_bytes(cfg, Bs, Ps), dtype=torch.uint8,
+                           device=dev)
+        tu, tf = [], []
+        for rep in range(reps + 1):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            _, m = P.pnmix_score_prefill(cfg, qpp, kpp, ws=ws_s, want_sigma=False)
+            if n_full:
+                c.mask.copy_(m)
+                P.pnmix_quantize_kv_pages(cfg, kj, vj, c.mask)
+            e[1].record()
+            P.pnmix_prefill_fused(cfg, qpp, kpp, vpp, c.k_pages, c.v_pages, mask=c.mask,
+                                  ws=ws_f, want_sigma=False)
+            e[2].record()
+            torch.cuda.synchronize()
+            if rep:
+                tu.append(e[0].elapsed_time(e[1]) * 1e3)
+                tf.append(e[1].elapsed_time(e[2]) * 1e3)
+        nb_read = Bs * Ps * (w.H_q + 2 * w.H_kv) * w.d * 2
+        out[f"B{Bs}_P{Ps}"] = {"pages_per_kv_head": n_full,
+                               "score_then_quantize_us": float(np.median(tu)),
+                               "fused_us": float(np.median(tf)),
+                               "fused_GBps_of_qkv_read": nb_read / float(np.median(tf)) / 1e3}
+        del qpp, kpp, vpp, c
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +323,9 @@ def main():
                     help="with --pmc-summary: the cache lengths of the profiled decode call")
     ap.add_argument("--call-bytes", type=int,
                     help="with --pmc-summary: algorithmic bytes of the profiled decode call")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time the prompt's scoring and page quantization (fused and unfused) "
+                         "for the workload's prompts and exit")
     ap.add_argument("--kt-summary", metavar="KT_DIR",
                     help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
     args = ap.parse_args()
@@ -302,6 +355,10 @@ def main():
     w = synth.WORKLOADS[args.workload]
     cfg = P.make_cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_H=w.b_H, b_L=w.b_L,
                      b_V=w.b_V, g_V=w.g_V, N_s=w.N_s, N=w.N)
+    if args.prefill_only:
+        print(json.dumps({"workload": w.name, "prefill": prefill_timing(w, cfg, P, synth, torch,
+                                                                        np)}), flush=True)
+        return
     kpb, vpb = P.pnmix_k_page_bytes(cfg), P.pnmix_v_page_bytes(cfg)
     W, K = args.warmup, args.steps
     layers = max(w.layers, args.min_layers)
@@ -486,6 +543,7 @@ def main():
     del scratch_k, scratch_v
 
     # ---- prefill score of one layer's prompt batch (and the long prefill if the workload has one)
+    prefill = prefill_timing(w, cfg, P, synth, torch, np)
     score = {}
     for (Bs, Ps) in ([(w.B, w.P)] + ([(1, w.prefill_score_P)] if w.prefill_score_P else [])):
         sq = synth.pair_scales(w.H_q, w.d // 2, w.sigma_ln, dev, w.name, 0, "q")
@@ -552,6 +610,7 @@ def main():
                      "frac_of_device_copy": achieved / copy_GBps},
         "page_quant": quant,
         "prefill_score": score,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -11,6 +11,7 @@ from ._lib import (PAIRS_ADJACENT, PAIRS_SPLIT_HALF, PnmixError, lib, make_cfg, 
                    pnmix_dequant_v_pages, pnmix_noalloc_scratch_bytes,
                    pnmix_hi_pairs, pnmix_k_page_bytes,
                    pnmix_last_error, pnmix_mask_words, pnmix_quantize_k_page,
+                   pnmix_prefill_fused, pnmix_prefill_fused_workspace_bytes,
                    pnmix_quantize_kv_pages, pnmix_quantize_v_page, pnmix_score_prefill,
                    pnmix_score_workspace_bytes,
                    pnmix_v_page_bytes)
@@ -25,5 +26,6 @@ __all__ = [
     "pnmix_score_workspace_bytes", "pnmix_v_page_bytes", "pnmix_append_kv", "pnmix_commit_page",
     "pnmix_append_decode_attn", "pnmix_dequant_k_pages", "pnmix_dequant_v_pages",
     "pnmix_decode_attn_noalloc", "pnmix_noalloc_scratch_bytes", "pnmix_quantize_kv_pages",
+    "pnmix_prefill_fused", "pnmix_prefill_fused_workspace_bytes",
     "PNMixLayerCache",
 ]

@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         "pnmix_quantize_k_page": (st, [cp, i32, P, P, P]),
         "pnmix_quantize_v_page": (st, [cp, i32, P, P]),
         "pnmix_quantize_kv_pages": (st, [cp, i32, P, P, P, P]),
+        "pnmix_prefill_fused_workspace_bytes": (sz, [cp, i32, i32]),
+        "pnmix_prefill_fused": (st, [cp, i32, i32, P, P, P, P, P, P, P, i32, P, sz, P]),
         "pnmix_decode_attn": (st, [cp, i32, i32, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P,
                                    sz, P]),
         "pnmix_decode_attn_paged": (st, [cp, i32, i32, P, P, P, P, P, ctypes.c_int64, P, P, P,
@@ -95,7 +97,8 @@ EXPORTED = ("pnmix_check_cfg", "pnmix_hi_pairs", "pnmix_mask_words", "pnmix_k_pa
             "pnmix_append_kv", "pnmix_commit_page", "pnmix_decode_attn_paged",
             "pnmix_append_decode_attn", "pnmix_dequant_k_pages", "pnmix_dequant_v_pages",
             "pnmix_noalloc_scratch_bytes", "pnmix_decode_attn_noalloc",
-            "pnmix_quantize_kv_pages")
+            "pnmix_quantize_kv_pages", "pnmix_prefill_fused_workspace_bytes",
+            "pnmix_prefill_fused")
 
 
 def _check(status: int):
@@ -188,6 +191,39 @@ def pnmix_score_prefill(cfg, q: torch.Tensor, k: torch.Tensor, sigma: torch.Tens
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _check(lib().pnmix_score_prefill(ctypes.byref(cfg), B, P, _ptr(q), _ptr(k), _ptr(sigma),
                                      _ptr(mask), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
+    return sigma, mask
+
+
+def pnmix_prefill_fused_workspace_bytes(cfg, B: int, P: int) -> int:
+    return int(lib().pnmix_prefill_fused_workspace_bytes(ctypes.byref(cfg), B, P))
+
+
+def pnmix_prefill_fused(cfg, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        k_pages: torch.Tensor, v_pages: torch.Tensor,
+                        sigma: torch.Tensor | None = None, mask: torch.Tensor | None = None,
+                        ws: torch.Tensor | None = None, want_sigma: bool = True, stream=None):
+    """Score the prompt and quantize its full pages into slots 0.. of k_pages / v_pages
+    [B][max_pages][H_kv][bytes], reading the keys once.  q [B][H_q][P][d], k, v [B][H_kv][P][d]
+    fp16 -> (sigma [B][H_kv][d/2] f32, mask [B][H_kv][words])."""
+    B, _, P, _ = q.shape
+    _expect(q, (B, cfg.H_q, P, cfg.d), _F16, "q")
+    _expect(k, (B, cfg.H_kv, P, cfg.d), _F16, "k")
+    _expect(v, (B, cfg.H_kv, P, cfg.d), _F16, "v")
+    max_pages = k_pages.shape[1]
+    _expect(k_pages, (B, max_pages, cfg.H_kv, pnmix_k_page_bytes(cfg)), _U8, "k_pages")
+    _expect(v_pages, (B, max_pages, cfg.H_kv, pnmix_v_page_bytes(cfg)), _U8, "v_pages")
+    dev = q.device
+    if mask is None:
+        mask = torch.empty(B, cfg.H_kv, pnmix_mask_words(cfg), dtype=torch.int32, device=dev)
+    if sigma is None and want_sigma:
+        sigma = torch.empty(B, cfg.H_kv, cfg.d // 2, dtype=torch.float32, device=dev)
+    need = pnmix_prefill_fused_workspace_bytes(cfg, B, P)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib().pnmix_prefill_fused(ctypes.byref(cfg), B, P, _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(sigma), _ptr(mask), _ptr(k_pages), _ptr(v_pages),
+                                     max_pages, _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream(stream)))
     return sigma, mask
 

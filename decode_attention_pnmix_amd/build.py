@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpnmix.so")
 SOURCES = ["pnmix_api.hip", "score.hip", "quant.hip", "decode.hip", "decode_generic.hip",
-           "cache_ops.hip"]
+           "prefill.hip", "cache_ops.hip"]
 
 # -ffp-contract=off: no FMA contraction (bit-exact quantizer and score).
 # packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 generated from fp32 code.

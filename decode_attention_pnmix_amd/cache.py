@@ -75,22 +75,28 @@ class PNMixLayerCache:
         return kj, vj
 
     # -- policy --------------------------------------------------------------------------------
-    def prefill(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
-        """Score the prompt once (Eq. 6), keep sinks, quantize full pages, keep the rest fp16."""
+    def prefill(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fused: bool = False):
+        """Score the prompt once (Eq. 6), keep sinks, quantize full pages, keep the rest fp16.
+        fused: score and quantize the prompt's pages in one pass over the keys
+        (pnmix_prefill_fused, same bytes; (b_H, b_L, b_V) = (3, 1, 2) only)."""
         cfg = self.cfg
         P = k.shape[2]
         if not (k.is_contiguous() and v.is_contiguous()):
             raise ValueError("prefill keys and values must be contiguous [B][H_kv][P][d]")
-        self.sigma, mask = L.pnmix_score_prefill(cfg, q, k)
-        self.mask.copy_(mask)
-        self.n_score_calls += 1
         s = min(P, cfg.N_s)
-        self.k_sink[:, :, :s] = k[:, :, :s]
-        self.v_sink[:, :, :s] = v[:, :, :s]
         n_full = (P - s) // cfg.N
         if n_full > self.max_pages:
             raise ValueError("prompt exceeds the cache capacity")
-        if n_full:
+        if fused:
+            self.sigma, mask = L.pnmix_prefill_fused(cfg, q, k, v, self.k_pages, self.v_pages)
+            self.mask.copy_(mask)
+        else:
+            self.sigma, mask = L.pnmix_score_prefill(cfg, q, k)
+            self.mask.copy_(mask)
+        self.n_score_calls += 1
+        self.k_sink[:, :, :s] = k[:, :, :s]
+        self.v_sink[:, :, :s] = v[:, :, :s]
+        if n_full and not fused:
             kj, _ = self.page_jobs(k, s, 0, n_full)
             _, vj = self.page_jobs(v, s, 0, n_full)
             L.pnmix_quantize_kv_pages(cfg, kj, vj, self.mask)

@@ -14,6 +14,7 @@
 namespace pnmix {
 
 constexpr int kWave = 64;
+constexpr int kN = 128;  // page and residual length (tokens)
 
 __device__ __forceinline__ float h2f(uint16_t u) {
   return static_cast<float>(__builtin_bit_cast(_Float16, u));

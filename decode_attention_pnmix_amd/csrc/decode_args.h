@@ -5,11 +5,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
 #include "pnmix.h"
 
 namespace pnmix {
 
-constexpr int kN = 128;  // page and residual length
 
 struct DecodeArgs {
   const uint16_t* q;

@@ -12,6 +12,16 @@ namespace pnmix {
 hipError_t launch_score(const pnmix_cfg& c, int B, int P, const uint16_t* q, const uint16_t* k,
                         float* sigma, uint32_t* mask, void* ws, hipStream_t stream);
 size_t score_workspace_bytes(const pnmix_cfg& c, int B, int P);
+hipError_t launch_score_chunks(const pnmix_cfg& c, int B, int P, const uint16_t* q,
+                               const uint16_t* k, float* chunk_sums, int cover_lo, int cover_hi,
+                               hipStream_t stream);
+hipError_t launch_score_select(const pnmix_cfg& c, int B, int P, const float* chunk_sums,
+                               float* sigma, uint32_t* mask, hipStream_t stream);
+size_t prefill_workspace_bytes(const pnmix_cfg& c, int B, int P);
+hipError_t launch_prefill_fused(const pnmix_cfg& c, int B, int P, const uint16_t* q,
+                                const uint16_t* k, const uint16_t* v, float* sigma,
+                                uint32_t* mask, uint8_t* k_pages, uint8_t* v_pages,
+                                int max_pages, void* ws, hipStream_t stream);
 
 hipError_t launch_quantize_k(const pnmix_cfg& c, int n_pages, const pnmix_page* pages,
                              const uint32_t* mask, hipStream_t stream);

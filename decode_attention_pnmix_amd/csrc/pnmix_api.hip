@@ -134,6 +134,39 @@ pnmix_status pnmix_score_prefill(const pnmix_cfg* c, int32_t B, int32_t P, const
                     "pnmix_score_prefill");
 }
 
+size_t pnmix_prefill_fused_workspace_bytes(const pnmix_cfg* c, int32_t B, int32_t P) {
+  if (check(c) != PNMIX_OK || B <= 0 || P <= 0) return 0;
+  return pnmix::prefill_workspace_bytes(*c, B, P);
+}
+
+pnmix_status pnmix_prefill_fused(const pnmix_cfg* c, int32_t B, int32_t P, const uint16_t* q,
+                                 const uint16_t* k, const uint16_t* v, float* sigma,
+                                 uint32_t* mask, uint8_t* k_pages, uint8_t* v_pages,
+                                 int32_t max_pages, void* ws, size_t ws_bytes, void* stream) {
+  pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (c->b_H != 3 || c->b_L != 1 || c->b_V != 2)
+    return fail(PNMIX_E_UNSUPPORTED,
+                "fused prefill serves (b_H, b_L, b_V) = (3, 1, 2); for other widths call "
+                "pnmix_score_prefill and pnmix_quantize_kv_pages");
+  if (B <= 0 || P <= 0 || max_pages < 0)
+    return fail(PNMIX_E_INVALID, "B = %d, P = %d must be positive, max_pages = %d >= 0", B, P,
+                max_pages);
+  if ((long long)B * (c->H_q + c->H_kv) > 0x7FFFFFFFLL || (P + 63) / 64 > 65535)
+    return fail(PNMIX_E_UNSUPPORTED, "B * (H_q + H_kv) >= 2^31 or P > 65535 * 64");
+  const int n_full = P > c->N_s ? (P - c->N_s) / c->N : 0;
+  if (n_full > max_pages)
+    return fail(PNMIX_E_INVALID, "the prompt fills %d pages, max_pages = %d", n_full, max_pages);
+  if (!q || !k || !v || !mask || !ws || (n_full > 0 && (!k_pages || !v_pages)))
+    return fail(PNMIX_E_INVALID, "q, k, v, mask, ws (and the page arrays) must be non-NULL");
+  const size_t need = pnmix::prefill_workspace_bytes(*c, B, P);
+  if (ws_bytes < need)
+    return fail(PNMIX_E_WORKSPACE, "fused prefill workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(pnmix::launch_prefill_fused(*c, B, P, q, k, v, sigma, mask, k_pages, v_pages,
+                                                max_pages, ws, (hipStream_t)stream),
+                    "pnmix_prefill_fused");
+}
+
 pnmix_status pnmix_quantize_k_page(const pnmix_cfg* c, int32_t n_pages, const pnmix_page* pages,
                                    const uint32_t* mask, void* stream) {
   pnmix_status s = check(c);

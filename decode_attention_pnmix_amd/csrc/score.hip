@@ -21,17 +21,21 @@ constexpr int kChunk = 64;
 
 constexpr int kSub = 32;  // tokens staged in LDS at a time
 
+// Key chunks cover_lo..cover_hi are skipped when the caller computes them elsewhere (the fused
+// prefill's page workgroups); cover_lo > cover_hi skips none.
 __global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           float* __restrict__ chunk_sums,
                                                           int H_q, int H_kv, int d, int pairing,
-                                                          int P, int n_chunks) {
+                                                          int P, int n_chunks, int cover_lo,
+                                                          int cover_hi) {
   __shared__ __align__(16) uint16_t tile[kSub * 128];  // kSub token rows of up to 128 fp16
   const int seq_head = blockIdx.x;  // b * (H_q + H_kv) + head (grid x: no 65535 limit)
   const int chunk = blockIdx.y;
   const int H = H_q + H_kv;
   const int b = seq_head / H;
   const int head = seq_head % H;
+  if (head >= H_q && chunk >= cover_lo && chunk <= cover_hi) return;  // whole workgroup
   const int np = d / 2;
   const int i = threadIdx.x;
   const uint16_t* src = head < H_q ? q + ((int64_t)b * H_q + head) * P * d
@@ -128,19 +132,30 @@ __global__ void __launch_bounds__(256) score_select_kernel(const float* __restri
   }
 }
 
-hipError_t launch_score(const pnmix_cfg& c, int B, int P, const uint16_t* q, const uint16_t* k,
-                        float* sigma, uint32_t* mask, void* ws, hipStream_t stream) {
+hipError_t launch_score_chunks(const pnmix_cfg& c, int B, int P, const uint16_t* q,
+                               const uint16_t* k, float* chunk_sums, int cover_lo, int cover_hi,
+                               hipStream_t stream) {
   const int n_chunks = (P + kChunk - 1) / kChunk;
-  float* chunk_sums = static_cast<float*>(ws);
   dim3 g1(B * (c.H_q + c.H_kv), n_chunks);
   hipLaunchKernelGGL(score_chunks_kernel, g1, dim3(64), 0, stream, q, k, chunk_sums, c.H_q,
-                     c.H_kv, c.d, c.pairing, P, n_chunks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                     c.H_kv, c.d, c.pairing, P, n_chunks, cover_lo, cover_hi);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_select(const pnmix_cfg& c, int B, int P, const float* chunk_sums,
+                               float* sigma, uint32_t* mask, hipStream_t stream) {
+  const int n_chunks = (P + kChunk - 1) / kChunk;
   const int words = (c.d / 2 + 31) / 32;
   hipLaunchKernelGGL(score_select_kernel, dim3(B * c.H_kv), dim3(256), 0, stream, chunk_sums,
                      sigma, mask, c.H_q, c.H_kv, c.d, P, n_chunks, c.n_hi_pairs, words);
   return hipGetLastError();
+}
+
+hipError_t launch_score(const pnmix_cfg& c, int B, int P, const uint16_t* q, const uint16_t* k,
+                        float* sigma, uint32_t* mask, void* ws, hipStream_t stream) {
+  float* chunk_sums = static_cast<float*>(ws);
+  const hipError_t e = launch_score_chunks(c, B, P, q, k, chunk_sums, 1, 0, stream);
+  return e != hipSuccess ? e : launch_score_select(c, B, P, chunk_sums, sigma, mask, stream);
 }
 
 size_t score_workspace_bytes(const pnmix_cfg& c, int B, int P) {

@@ -129,6 +129,25 @@ pnmix_status pnmix_score_prefill(const pnmix_cfg* cfg, int32_t B, int32_t P, con
                                  const uint16_t* k, float* sigma, uint32_t* mask, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* Prefill in one pass over the keys: pnmix_score_prefill (sigma, mask) and the quantization of
+ * the prompt's full pages (tokens N_s + N p .. N_s + N p + N - 1 of every (sequence, KV head),
+ * p < n_full = (P - N_s) / N) into page slots 0..n_full-1, with the mask just computed ([PNMIX]
+ * sec. 5: the salient pairs are chosen once at prefill and every page uses them).  Same outputs
+ * bit for bit as pnmix_score_prefill followed by pnmix_quantize_kv_pages on those pages, but the
+ * keys are read once: the page workgroups also form the score's key chunk sums and keep both
+ * encodings a channel can take until the mask is known.  Sinks and residual rows are the
+ * caller's (the rows are copied as they are).  (b_H, b_L, b_V) = (3, 1, 2) only.
+ *   q [B][H_q][P][d], k, v [B][H_kv][P][d] fp16; sigma [B][H_kv][d/2] f32 or NULL;
+ *   mask [B][H_kv][mask_words] out; k_pages, v_pages [B][max_pages][H_kv][page bytes] out
+ *   (slots 0..n_full-1 written; may be NULL when n_full = 0);
+ *   ws: pnmix_prefill_fused_workspace_bytes(cfg, B, P) bytes (score chunk sums and the
+ *   candidate encodings, about 12 KB per page). */
+size_t pnmix_prefill_fused_workspace_bytes(const pnmix_cfg* cfg, int32_t B, int32_t P);
+pnmix_status pnmix_prefill_fused(const pnmix_cfg* cfg, int32_t B, int32_t P, const uint16_t* q,
+                                 const uint16_t* k, const uint16_t* v, float* sigma,
+                                 uint32_t* mask, uint8_t* k_pages, uint8_t* v_pages,
+                                 int32_t max_pages, void* ws, size_t ws_bytes, void* stream);
+
 /* Key page quantization and H3/L1 packing ([PNMIX] sec. 2 Eq. 2 and kernel-implementation
  * appendix; [REPRO] Eq. 7, constant groups, H3/L1 packing).
  *   pages [n_pages] DEVICE array of jobs; mask [rows][mask_words] (row = job.mask_row).

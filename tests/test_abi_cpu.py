@@ -120,6 +120,24 @@ def test_noalloc_rejects_oversized_batches_before_any_launch():
                                          ctypes.c_float(0.088), FAKE, None) == L.PNMIX_E_INVALID
 
 
+def test_prefill_fused_validation_before_launch():
+    lib = P.lib()
+    c = _cfg()
+    B, P_ = 2, 32 + 3 * 128 + 5
+    ws = P.pnmix_prefill_fused_workspace_bytes(c, B, P_)
+    assert ws >= P.pnmix_score_workspace_bytes(c, B, P_) + B * 8 * 3 * (128 * 128 // 2)
+
+    def call(cfg=c, max_pages=3, ws_bytes=ws, k_pages=FAKE):
+        return lib.pnmix_prefill_fused(ctypes.byref(cfg), B, P_, FAKE, FAKE, FAKE, None, FAKE,
+                                       k_pages, FAKE, max_pages, FAKE, ws_bytes, None)
+
+    assert call(cfg=_cfg(b_V=4)) == L.PNMIX_E_UNSUPPORTED
+    assert call(max_pages=2) == L.PNMIX_E_INVALID  # the prompt fills 3 pages
+    assert call(ws_bytes=ws - 1) == L.PNMIX_E_WORKSPACE
+    assert call(k_pages=None) == L.PNMIX_E_INVALID
+    assert P.pnmix_last_error()
+
+
 def test_score_accepts_a_folded_batch_above_65535():
     """Layers fold into the batch: Llama-3.1-8B's 32 layers x B = 110 x (32 + 8) heads is 140,800
     (sequence, head) rows, above the 65,535 limit of a grid's y dimension.  Validation passes;

@@ -705,3 +705,73 @@ def test_score_folded_batch_above_65535():
         _, _, s, m = oracle.score_prefill(oc, u16(qp[b]), u16(k[b]))
         assert np.array_equal(sigma[b].cpu().numpy().view(np.uint32), s.view(np.uint32)), b
         assert np.array_equal(mask[b].cpu().numpy().view(np.uint32), m), b
+
+
+# ----------------------------------------------------------------- fused prefill (one key read)
+
+PREFILL_CASES = [
+    # id, workload, B, P
+    ("qwen3-8b-P141-B32", "qwen3-8b-36L-b32-8k", 32, 141),   # no full page: score only
+    ("qwen3-8b-ragged-P", "qwen3-8b-1L-32k", 2, None),        # several P, see below
+    ("tiny-d32", "tiny", 3, 32 + 2 * 128 + 40),
+    ("llama-G64-P2000", "llama3.1-8b-32L-b110-8k", 2, 2000),
+]
+
+
+def _prefill_check(w, B, P_):
+    lc, oc = cfgs(w)
+    qp, k, v, _ = layer_inputs(w, 13, B, P_, P_)
+    n_full = max(0, (P_ - w.N_s) // w.N)
+    mp = max(n_full, 1)
+    kp1 = torch.zeros(B, mp, w.H_kv, P.pnmix_k_page_bytes(lc), dtype=torch.uint8, device="cuda")
+    vp1 = torch.zeros(B, mp, w.H_kv, P.pnmix_v_page_bytes(lc), dtype=torch.uint8, device="cuda")
+    sig_f, mask_f = P.pnmix_prefill_fused(lc, qp, k, v, kp1, vp1)
+    # the unfused sequence: score, then both page kinds in one launch
+    sig_u, mask_u = P.pnmix_score_prefill(lc, qp, k)
+    c = P.PNMixLayerCache(lc, B, mp)
+    c.mask.copy_(mask_u)
+    if n_full:
+        kj, _ = c.page_jobs(k, w.N_s, 0, n_full)
+        _, vj = c.page_jobs(v, w.N_s, 0, n_full)
+        P.pnmix_quantize_kv_pages(lc, kj, vj, c.mask)
+    torch.cuda.synchronize()
+    assert torch.equal(sig_f.view(torch.int32), sig_u.view(torch.int32))
+    assert torch.equal(mask_f, mask_u)
+    assert torch.equal(kp1[:, :n_full], c.k_pages[:, :n_full])
+    assert torch.equal(vp1[:, :n_full], c.v_pages[:, :n_full])
+    # against the oracle: the mask of sampled sequences and some of their pages
+    mh = mask_f.cpu().numpy().view(np.uint32)
+    kh, vh = u16(k), u16(v)
+    for b in sorted({0, B - 1}):
+        _, _, s, m = oracle.score_prefill(oc, u16(qp[b]), kh[b])
+        assert np.array_equal(sig_f[b].cpu().numpy().view(np.uint32), s.view(np.uint32)), b
+        assert np.array_equal(mh[b], m), b
+        for p in sorted({0, n_full - 1, n_full // 2}) if n_full else []:
+            for h in (0, w.H_kv - 1):
+                a = w.N_s + p * w.N
+                assert np.array_equal(kp1[b, p, h].cpu().numpy(),
+                                      oracle.quantize_k_page(oc, kh[b, h, a:a + w.N], m[h])), (b, p, h)
+                assert np.array_equal(vp1[b, p, h].cpu().numpy(),
+                                      oracle.quantize_v_page(oc, vh[b, h, a:a + w.N])), (b, p, h)
+    return n_full
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_fused(case):
+    name, wname, B, P_ = case
+    w = synth.WORKLOADS[wname]
+    # prompt lengths around the chunk and page boundaries: pages end mid-chunk or on a chunk
+    # boundary, and the chunks after the last page may be empty, partial or full
+    lengths = [P_] if P_ else [32 + 128, 32 + 128 + 1, 32 + 2 * 128 + 31, 32 + 2 * 128 + 32,
+                               32 + 2 * 128 + 33, 32 + 3 * 128 + 95, 32 + 3 * 128 + 96, 31, 33]
+    for L_ in lengths:
+        n_full = _prefill_check(w, B, L_)
+        say(f"[prefill-fused] {name} B={B} P={L_} pages={n_full}")
+
+
+def test_prefill_fused_long_prompt():
+    """The 16K-token prompt at B = 1 (Llama-3.1-8B shape, G = 64, r = 0.4): 127 pages per KV head."""
+    w = synth.WORKLOADS["llama3.1-8b-32L-b110-8k"]
+    n_full = _prefill_check(w, 1, w.prefill_score_P)
+    say(f"[prefill-fused] llama 16K pages={n_full}")
+    assert n_full == (w.prefill_score_P - w.N_s) // w.N

@@ -145,6 +145,54 @@ def kt_summary(kt_dir):
     return "\n".join(lines)
 
 
+SQ_PER_WAVE = ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
+               "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY")
+SQ_INSTS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VMEM")
+
+
+def sq_summary(dirs):
+    """Text table of rocprofv3 --pmc runs of this script (SQ_ and TA_ counters) for every pnmix
+    kernel, summed over its dispatches: the per-wave counters (quad-cycles) as fractions of the
+    waves' lifetime SQ_WAVE_CYCLES, instructions per wave, LDS bank-conflict cycles per active
+    LDS cycle, MFMA-busy cycles per SQ-busy cycle, and the raw sums."""
+    sums, meta = {}, {}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            kn = r["Kernel_Name"]
+            if "pnmix::" not in kn:
+                continue
+            short = kn.split("(")[0].replace("void ", "").replace("pnmix::", "")
+            s = sums.setdefault(short, {})
+            s[r["Counter_Name"]] = s.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            m = meta.setdefault(short, {"dispatches": {}, "vgpr": r.get("VGPR_Count", "?"),
+                                        "agpr": r.get("Accum_VGPR_Count", "?"),
+                                        "lds": r.get("LDS_Block_Size", "?")})
+            m["dispatches"].setdefault(d, set()).add(r["Dispatch_Id"])
+    lines = []
+    for kn in sorted(sums, key=lambda k: -sums[k].get("SQ_WAVE_CYCLES", 0.0)):
+        s, m = sums[kn], meta[kn]
+        lines.append(f"{kn}")
+        nd = max(len(x) for x in m["dispatches"].values())
+        lines.append(f"  dispatches per run {nd}  vgpr {m['vgpr']}  agpr {m['agpr']}  "
+                     f"lds {m['lds']}")
+        wc = s.get("SQ_WAVE_CYCLES")
+        if wc:
+            lines.append("  per-wave fraction of lifetime: " + "  ".join(
+                f"{c[3:].lower()} {s[c] / wc:.3f}" for c in SQ_PER_WAVE if c in s))
+        nw = s.get("SQ_WAVES")
+        if nw:
+            lines.append("  instructions per wave: " + "  ".join(
+                f"{c[9:].lower()} {s[c] / nw:.1f}" for c in SQ_INSTS if c in s))
+        if s.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in s:
+            lines.append(f"  lds bank-conflict cycles / active lds cycles: "
+                         f"{s['SQ_LDS_BANK_CONFLICT'] / s['SQ_ACTIVE_INST_LDS']:.3f}")
+        if s.get("SQ_BUSY_CYCLES") and "SQ_VALU_MFMA_BUSY_CYCLES" in s:
+            lines.append(f"  mfma busy cycles / sq busy cycles: "
+                         f"{s['SQ_VALU_MFMA_BUSY_CYCLES'] / s['SQ_BUSY_CYCLES']:.3f}")
+        lines.append("  sums: " + "  ".join(f"{c} {v:.4g}" for c, v in sorted(s.items())))
+    return "\n".join(lines)
+
+
 def build_layer(w, cfg, layer, B, T0, max_pages, steps, dev, P, synth, torch):
     """Cache of one layer holding tokens [0, T0) and the inputs of `steps` decode steps."""
     npairs = w.d // 2
@@ -328,9 +376,14 @@ def main():
                          "for the workload's prompts and exit")
     ap.add_argument("--kt-summary", metavar="KT_DIR",
                     help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--sq-summary", nargs="+", metavar="PMC_DIR",
+                    help="print the SQ/TA counter table of rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
     if args.kt_summary:
         print(kt_summary(args.kt_summary))
+        return
+    if args.sq_summary:
+        print(sq_summary(args.sq_summary))
         return
     if args.pmc_summary:
         print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload,

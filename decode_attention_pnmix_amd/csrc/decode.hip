@@ -215,8 +215,9 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 // top digit, c[3] = sum_t B_t from the ones row; every partial is exact in int32 and the
 // three terms are non-negative (no cancellation in fp32)
 __device__ __forceinline__ float combine_pv(const v4i& c) {
-  const int off = c[3] << 7;
-  const int lo = (c[0] + off) + ((c[1] + off) << 8);
+  // (c0 + 128 c3) + 256 (c1 + 128 c3) = c0 + 256 c1 + 32896 c3: the sum over the two low
+  // digits, in [0, 2^31) (0 <= c3 < 2^16: a 24-bit product)
+  const int lo = c[0] + (c[1] << 8) + (int)__umul24((uint32_t)c[3], 32896u);
   return __builtin_fmaf((float)c[2], 65536.0f, (float)lo);
 }
 // bytes 0..2 of four words, transposed: out[d] byte i = byte d of y[i]
@@ -560,9 +561,10 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   constexpr int UK = (NT * D + 63) / 64;   // LSB prep units per lane
   constexpr int NTV = D / 16;              // p.V column tiles of 16 channels
   constexpr int NBLK = D / 32;             // blocks of 8 value-byte columns (32 channels)
-  // value loads after q.K and key prefetch after p.V, only where prefetching both sides a page
-  // ahead would spill (the 8-head tiles with one or two key groups fit it in registers)
-  constexpr bool kLate = NT >= 2;
+  // Both sides of the next page are fetched a page ahead (the keys once q.K is done, the
+  // values once p.V is done) where that fits in registers: one head tile, or two with one key
+  // group.  Elsewhere the values are fetched after q.K and the next keys after p.V.
+  constexpr bool kLate = !(NT == 1 || (NT == 2 && KG == 1));
 
   const int lane = threadIdx.x & 63;
   const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
@@ -656,23 +658,23 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       zv[kg] = bload8(krs, zOff + 2 * (kg * D + 4 * (lane % JL)), so);
     }
   };
-  // Value side of one page: scales and offsets of this lane's q.K keys (8 oct + b) per group;
-  // code bytes of its p.V tile columns per K-step.
+  // Value side of one page: the scales and offsets of keys 8 oct + b in the value group of
+  // block qb (the lanes of row bk hold block bk's; the other rows fetch them across lanes when
+  // the block's digits are formed); code bytes of this lane's p.V tile columns per K-step.
   const uint32_t vS = kN * D / 4 + 2 * 8 * oct;  // S [NGV][N] fp16 after the codes, then Z
-  v4u sS[4], zZ[4];
+  // value groups are 32 << vg_shift channels: block bk belongs to group bk >> vg_shift and
+  // starts one where (bk & vg_mask) == 0
+  const int vg_shift = __builtin_ctz((uint32_t)a.g_V) - 5;
+  const int vg_mask = (1 << vg_shift) - 1;
+  const int gq = min(qb, NBLK - 1) >> vg_shift;
+  v4u sSo, zZo;
   v4u cv[NBLK][2];
   auto load_v = [&](int pgv, int64_t blk, bool valid) {
     uint32_t vso;
     const rsrc_t vrs_p = page_rsrc(a.v_pages, a.vpb, vrs, pgv, blk, valid, vso);
     const rsrc_t vrs = vrs_p;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // groups past NGV repeat the last one: the page maximum is unchanged and the per-group
-      // loops stop at NGV
-      const int gc = min(g, NGV - 1);
-      sS[g] = bload16(vrs, vS + 2 * gc * kN, vso);
-      zZ[g] = bload16(vrs, vS + 2 * (NGV + gc) * kN, vso);
-    }
+    sSo = bload16(vrs, vS + 2 * gq * kN, vso);
+    zZo = bload16(vrs, vS + 2 * (NGV + gq) * kN, vso);
 #pragma unroll
     for (int bk = 0; bk < NBLK; ++bk)
 #pragma unroll
@@ -693,18 +695,18 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
   // o = 0.  (No early exit: a branch that stores its partial early would force waits for all
   // loads in flight at the point where it rejoins.)
 
-  // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NGV][16][kWS] bytes (one head tile at a time);
-  // bias [KG][NH] f32; head maxima [NH] f32; scaled queries [NH][D] f32.
+  // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NT][16][kWS] bytes (one
+  // value group at a time);
+  // bias [KG][NH] f32; scaled queries [NH][D] f32.
   uint8_t* T = lds;
   uint8_t* W = lds + a.lds_T;
-  float* biasl = reinterpret_cast<float*>(W + NGV * 16 * kWS);
-  float* qm = biasl + 4 * NH;
-  float* qs = qm + NH;
+  float* biasl = reinterpret_cast<float*>(W + NT * 16 * kWS);
+  float* qs = biasl + 4 * NH;
 
   // ---- once per split: clear the digit table, salient ranks, scaled queries
   for (int i = lane * 16; i < a.lds_T; i += 64 * 16) *reinterpret_cast<v4u*>(T + i) = v4u{0, 0, 0, 0};
   // p.V digit rows (head, 3) are all ones: their sums are the column sums of the value codes
-  for (int i = lane; i < NGV * 4 * (kN / 16); i += 64) {
+  for (int i = lane; i < NT * 4 * (kN / 16); i += 64) {
     const int r = i / (kN / 16), c16 = i % (kN / 16);
     *reinterpret_cast<v4u*>(W + (4 * r + 3) * kWS + 16 * c16) =
         v4u{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
@@ -729,39 +731,30 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     hoff[k][0] = o[0] | (o[1] << 16);
     hoff[k][1] = o[2] | (o[3] << 16);
   }
-  // scaled queries go to LDS (qs) and are read back per page; the registers keep only the
-  // per-unit head maxima
-  float qmaxu[UK];
+  // scaled queries go to LDS (qs) and are read back per page; the registers keep only their
+  // largest magnitude over the group's heads
+  float qmax = 0.0f;
 #pragma unroll
   for (int k = 0; k < UK; ++k) {
     const int u = lane + 64 * k;
     const v4f q4 = v4f{f16lo(qq[k].x), f16hi(qq[k].x), f16lo(qq[k].y), f16hi(qq[k].y)} * a.qscale;
-    float mx = fmaxf(fmaxf(fabsf(q4[0]), fabsf(q4[1])), fmaxf(fabsf(q4[2]), fabsf(q4[3])));
-    qmaxu[k] = group_max<(JL < 64 ? JL : 64)>(mx);
+    qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(q4[0]), fabsf(q4[1])), fmaxf(fabsf(q4[2]), fabsf(q4[3]))));
     if (u < NT * D) *reinterpret_cast<v4f*>(qs + 4 * u) = q4;
   }
-#pragma unroll
-  for (int k = 0; k < UK; ++k) {
-    const int u = lane + 64 * k;
-    if (u < NT * D && (u % JL) == 0) qm[u / JL] = qmaxu[k];
-  }
-  wave_sync();
-  // max |qt| of the head this lane has in the q.K output (head 4t + lane/16)
-  float qmaxC[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) qmaxC[t] = qm[4 * t + lane / 16];
+  qmax = wave_max_nonneg(qmax);
 
   // running softmax state of head 4t + lane/16; p.V accumulators per 16-channel tile (C
-  // layout: column lane % 16), value-offset sums per group
+  // layout: column lane % 16), value-offset sums per value group (kept at the group's first
+  // block of 32 channels; the other blocks' entries stay zero)
   float m_run[NT], l_run[NT];
-  float zacc[NT][4];
+  float zacc[NT][NBLK];
   float acc[NT][NTV];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     m_run[t] = -INFINITY;
     l_run[t] = 0.0f;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) zacc[t][g] = 0.0f;
+    for (int bk = 0; bk < NBLK; ++bk) zacc[t][bk] = 0.0f;
 #pragma unroll
     for (int v = 0; v < NTV; ++v) acc[t][v] = 0.0f;
   }
@@ -778,13 +771,16 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     }
     smax = wave_max_u32(max(smax & 0xFFFFu, smax >> 16));
     const float Smax = (float)__builtin_bit_cast(_Float16, (uint16_t)smax);
-    // 2^sigma with |qt S 2^sigma| < 2^30 for every channel of the head
-    auto sigma_of = [&](float qmax) -> int {
+    // 2^sigma with |qt S 2^sigma| < 2^30 for every channel of every head of the group (one
+    // fixed point for the page: a head with smaller queries keeps fewer of the 30 bits, its
+    // logits the same absolute resolution 2^-sigma per term)
+    int sigma = 0;
+    {
       const float M = qmax * Smax;
-      if (!(M > 0.0f)) return 0;
       const int e = (int)((__builtin_bit_cast(uint32_t, M) >> 23) & 0xFF) - 127;
-      return min(max(29 - e, -126), 126);
-    };
+      if (M > 0.0f) sigma = min(max(29 - e, -126), 126);
+    }
+    const float sc = pow2i(sigma), inv2s = pow2i(-sigma);
 
     // ---- digit table, LSB part, and the Z bias of each head
 #pragma unroll
@@ -792,19 +788,21 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
       const int u = lane + 64 * k;
       const int hu = u / JL, j = u % JL;
       const bool ok = u < NT * D;
-      const float sc = pow2i(sigma_of(qmaxu[k]));
       const v4f qv = ok ? *reinterpret_cast<const v4f*>(qs + 4 * u) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      const v4f qsc = qv * sc;  // exact: a power of two
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
-        const float s4[4] = {f16lo(sv[kg].x), f16hi(sv[kg].x), f16lo(sv[kg].y), f16hi(sv[kg].y)};
-        const float z4[4] = {f16lo(zv[kg].x), f16hi(zv[kg].x), f16lo(zv[kg].y), f16hi(zv[kg].y)};
+        // qt 2^sigma S rounded once (fp16 S widened exactly inside the mixed-precision fma)
+        const float m4[4] = {fma_mix_lo(qsc[0], sv[kg].x, 0.0f), fma_mix_hi(qsc[1], sv[kg].x, 0.0f),
+                             fma_mix_lo(qsc[2], sv[kg].y, 0.0f), fma_mix_hi(qsc[3], sv[kg].y, 0.0f)};
         uint32_t y[4], dg[4];
         float bz = 0.0f;
+        bz = fma_mix_lo(qv[0], zv[kg].x, bz);
+        bz = fma_mix_hi(qv[1], zv[kg].x, bz);
+        bz = fma_mix_lo(qv[2], zv[kg].y, bz);
+        bz = fma_mix_hi(qv[3], zv[kg].y, bz);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          y[i] = digits4((int)((qv[i] * sc) * s4[i]));
-          bz = __builtin_fmaf(qv[i], z4[i], bz);
-        }
+        for (int i = 0; i < 4; ++i) y[i] = digits4((int)m4[i]);
         transpose4(y, dg);
         bz = group_sum<(JL < 64 ? JL : 64)>(bz);
         if (ok) {
@@ -839,12 +837,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
           A[kg][t][ks] = *reinterpret_cast<const v4i*>(T + ((kg * NT + t) * 16 + (lane & 15)) * TL +
                                                        64 * ks + 16 * qb);
     }
-    float inv2s[NT], bias[NT];
+    float bias[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      inv2s[t] = pow2i(-sigma_of(qmaxC[t]));
-      bias[t] = biasl[kg_lane * NH + 4 * t + qb];
-    }
+    for (int t = 0; t < NT; ++t) bias[t] = biasl[kg_lane * NH + 4 * t + qb];
 
     // ---- q.K: tile b holds keys 8 oct + b; the lane's q.K output head is 4t + qb
     v4u wH0[KHM], wH1[KHM];
@@ -878,7 +873,7 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
             c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[kg][t][KL + ks], bH[ks], c, 0, 0, 0);    \
           csel = (KG == 1 || kg == kg_lane) ? c : csel;                                        \
         }                                                                                      \
-        lg[t][BB] = __builtin_fmaf(combine4(csel), inv2s[t] * kInvSL[BB], bias[t]);            \
+        lg[t][BB] = __builtin_fmaf(combine4(csel), inv2s * kInvSL[BB], bias[t]);               \
       }                                                                                        \
     }
     PNMIX_QK_TILE(0) PNMIX_QK_TILE(1) PNMIX_QK_TILE(2) PNMIX_QK_TILE(3)
@@ -900,14 +895,12 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     // reach 2^22 itself, and byte 2 of x then stays below 128 (never the int8 sign bit).
     uint32_t svm2 = 0u;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) svm2 = pk_max_u16(svm2, sS[g][e]);  // S >= 0: bit order
+    for (int e = 0; e < 4; ++e) svm2 = pk_max_u16(svm2, sSo[e]);  // S >= 0: bit order
     const float svmax = wave_max_nonneg(fmaxf(f16lo(svm2), f16hi(svm2)));
 
-    // ---- per head tile: online softmax, value-offset term on the vector ALU, digits of w to
-    // LDS, then p.V.  The tiles take turns on one digit table W, which keeps a wave's LDS slice
-    // small enough for two waves per SIMD with two head tiles.
+    // ---- online softmax of every head tile: pw = p 2^sh (the p.V fixed-point scale of the
+    // head), the running maximum, sum and rescaled accumulators
+    float pw[NT][8], inv_sv[NT], pscl[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       float pm = lg[t][0];
@@ -925,51 +918,76 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         sh = min(max(21 - e, -126), 126);
       }
       const float sv2 = pow2i(sh);
-      float p[8], pw[8], ps = 0.0f;
+      inv_sv[t] = pow2i(-sh);
+      pscl[t] = inv_sv[t] * vfw;
+      float ps = 0.0f;
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
-        p[bb] = __builtin_amdgcn_exp2f(lg[t][bb] - mn);
-        ps += p[bb];
-        pw[bb] = p[bb] * sv2;
+        const float p = __builtin_amdgcn_exp2f(lg[t][bb] - mn);
+        ps += p;
+        pw[t][bb] = p * sv2;
       }
       l_run[t] = l_run[t] * alpha + ps;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (g >= NGV) break;
-        const v4u zz = zZ[g], ss = sS[g];
-        float zs = zacc[t][g] * alpha;
-        uint32_t x[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          zs = fma_mix_lo(p[2 * e], zz[e], zs);
-          zs = fma_mix_hi(p[2 * e + 1], zz[e], zs);
-          // 2^23 + x in the float's bits: x in bytes 0..2 (byte 2 <= 64)
-          x[2 * e] = __builtin_bit_cast(uint32_t, fma_mix_lo(pw[2 * e], ss[e], kTwo23));
-          x[2 * e + 1] = __builtin_bit_cast(uint32_t, fma_mix_hi(pw[2 * e + 1], ss[e], kTwo23));
-        }
-        zacc[t][g] = zs;
-        uint32_t d0[3], d1[3];
-        transpose3(x, d0);
-        transpose3(x + 4, d1);
-        // digit rows 0, 1 as int8 u - 128 (the ones row 3 restores the offset); row 2 as is
-        uint8_t* row = W + (g * 16 + 4 * qb) * kWS + 8 * oct;
-        *reinterpret_cast<uint2*>(row) = make_uint2(d0[0] ^ 0x80808080u, d1[0] ^ 0x80808080u);
-        *reinterpret_cast<uint2*>(row + kWS) = make_uint2(d0[1] ^ 0x80808080u, d1[1] ^ 0x80808080u);
-        *reinterpret_cast<uint2*>(row + 2 * kWS) = make_uint2(d0[2], d1[2]);
-      }
       if (__any(alpha != 1.0f)) {
 #pragma unroll
         for (int v = 0; v < NTV; ++v) acc[t][v] *= alpha;
-      }
-      wave_sync();  // the w digits of this tile are in LDS
-
-      // ---- p.V: tile v = (block bk = v / 2, field pair f = v % 2): column n is channel
-      // 4 (8 bk + n % 8) + f + 2 (n / 8), 32 channels of one value group; rows (head, digit),
-      // K = 64 keys
 #pragma unroll
-      for (int v = 0; v < NTV; ++v) {
-        const int bk = v / 2, f = v % 2;
-        const int g = (32 * bk) / a.g_V;
+        for (int bk = 0; bk < NBLK; ++bk) zacc[t][bk] *= alpha;
+      }
+    }
+
+    // ---- p.V per block of 32 channels (one value group, or part of one): where a group
+    // starts, the digits of w = p S of every head tile go to the digit table W and the group's
+    // offset term sum_t p Z is accumulated on the vector ALU; then tile v = (bk, field pair f)
+    // of every head tile: column n is channel 4 (8 bk + n % 8) + f + 2 (n / 8); rows (head,
+    // digit); K = 64 keys.  The masked value codes (B operand) are formed once per tile and
+    // serve every head tile.
+#pragma unroll
+    for (int bk = 0; bk < NBLK; ++bk) {
+      if (bk == 0 || (bk & vg_mask) == 0) {
+        // block bk's scales and offsets from the lanes of row bk (same octet)
+        v4u ss, zz;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int src = 4 * ((lane & 15) + 16 * bk);
+          ss[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sSo[e]);
+          zz[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)zZo[e]);
+        }
+        if (bk) wave_sync();  // the previous group's rows of W are read
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float zs = 0.0f;
+          uint32_t x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            zs = fma_mix_lo(pw[t][2 * e], zz[e], zs);
+            zs = fma_mix_hi(pw[t][2 * e + 1], zz[e], zs);
+            // 2^23 + x in the float's bits: x in bytes 0..2 (byte 2 <= 64)
+            x[2 * e] = __builtin_bit_cast(uint32_t, fma_mix_lo(pw[t][2 * e], ss[e], kTwo23));
+            x[2 * e + 1] = __builtin_bit_cast(uint32_t, fma_mix_hi(pw[t][2 * e + 1], ss[e], kTwo23));
+          }
+          zacc[t][bk] = __builtin_fmaf(zs, inv_sv[t], zacc[t][bk]);
+          uint32_t d0[3], d1[3];
+          transpose3(x, d0);
+          transpose3(x + 4, d1);
+          // digit rows 0, 1 as int8 u - 128 (the ones row 3 restores the offset); row 2 as is
+          uint8_t* row = W + (t * 16 + 4 * qb) * kWS + 8 * oct;
+          *reinterpret_cast<uint2*>(row) = make_uint2(d0[0] ^ 0x80808080u, d1[0] ^ 0x80808080u);
+          *reinterpret_cast<uint2*>(row + kWS) = make_uint2(d0[1] ^ 0x80808080u, d1[1] ^ 0x80808080u);
+          *reinterpret_cast<uint2*>(row + 2 * kWS) = make_uint2(d0[2], d1[2]);
+        }
+        wave_sync();  // the w digits of this group are in LDS
+      }
+      v4i A0[NT], A1[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint8_t* wrow = W + (t * 16 + (lane & 15)) * kWS + 16 * qb;
+        A0[t] = *reinterpret_cast<const v4i*>(wrow);
+        A1[t] = *reinterpret_cast<const v4i*>(wrow + 64);
+      }
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int v = 2 * bk + f;
         v4i Bv[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -977,16 +995,14 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 #pragma unroll
           for (int e = 0; e < 4; ++e) Bv[ks][e] = (int)((f == 0 ? w[e] : (w[e] >> 2)) & vmask);
         }
-        const float fw = vfw;
-        const uint8_t* wrow = W + (g * 16 + (lane & 15)) * kWS + 16 * qb;
-        const v4i A0 = *reinterpret_cast<const v4i*>(wrow);
-        const v4i A1 = *reinterpret_cast<const v4i*>(wrow + 64);
-        v4i c = v4i{0, 0, 0, 0};
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, Bv[0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, Bv[1], c, 0, 0, 0);
-        acc[t][v] = __builtin_fmaf(combine_pv(c), pow2i(-sh) * fw, acc[t][v]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          v4i c = v4i{0, 0, 0, 0};
+          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0[t], Bv[0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1[t], Bv[1], c, 0, 0, 0);
+          acc[t][v] = __builtin_fmaf(combine_pv(c), pscl[t], acc[t][v]);
+        }
       }
-      if (t + 1 < NT) wave_sync();  // the next tile rewrites W
     }
     if constexpr (kLate) {
       load_k(pg + step, blk_next, more);
@@ -1001,17 +1017,19 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const float lt = row_sum16(l_run[t]);
-    float zs[4];
+    // the offset sum of each block's value group (held by the group's first block)
+    float zs[NBLK];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) zs[g] = row_sum16(zacc[t][g]);
+    for (int bk = 0; bk < NBLK; ++bk) {
+      zs[bk] = row_sum16(zacc[t][bk]);
+      if (bk > 0 && (bk & vg_mask) != 0) zs[bk] = zs[bk - 1];
+    }
     const int hh = 4 * t + qb;
     if (hh < ng) {
 #pragma unroll
       for (int v = 0; v < NTV; ++v) {
         const int c = 4 * (8 * (v / 2) + (lane & 7)) + (v % 2) + 2 * ((lane >> 3) & 1);
-        const int gi = c / a.g_V;
-        const float zsg = gi == 0 ? zs[0] : gi == 1 ? zs[1] : gi == 2 ? zs[2] : zs[3];
-        po.o(hh * D + c, acc[t][v] + zsg);
+        po.o(hh * D + c, acc[t][v] + zs[v / 2]);
       }
       if ((lane & 15) == 0) {
         po.ml(hh, m_run[t], lt);
@@ -1210,8 +1228,8 @@ static size_t lds_T_bytes(const pnmix_cfg& c) {
 
 static size_t lds_bytes(const pnmix_cfg& c) {
   const int NT = n_tiles(c);
-  const size_t W = (size_t)(c.d / c.g_V) * 16 * kWS;  // one table, shared by the head tiles
-  return lds_T_bytes(c) + W + 4 * 4 * NT * 4 + 4 * NT * 4 + (size_t)4 * NT * c.d * 4;
+  const size_t W = (size_t)NT * 16 * kWS;  // one value group's rows of every head tile
+  return lds_T_bytes(c) + W + 4 * 4 * NT * 4 + (size_t)4 * NT * c.d * 4;
 }
 
 static size_t lds_fp16_bytes(const pnmix_cfg& c) {

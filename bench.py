@@ -164,17 +164,14 @@ def sq_summary(dirs):
             short = kn.split("(")[0].replace("void ", "").replace("pnmix::", "")
             s = sums.setdefault(short, {})
             s[r["Counter_Name"]] = s.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-            m = meta.setdefault(short, {"dispatches": {}, "vgpr": r.get("VGPR_Count", "?"),
-                                        "agpr": r.get("Accum_VGPR_Count", "?"),
-                                        "lds": r.get("LDS_Block_Size", "?")})
+            m = meta.setdefault(short, {"dispatches": {}, "lds": r.get("LDS_Block_Size", "?")})
             m["dispatches"].setdefault(d, set()).add(r["Dispatch_Id"])
     lines = []
     for kn in sorted(sums, key=lambda k: -sums[k].get("SQ_WAVE_CYCLES", 0.0)):
         s, m = sums[kn], meta[kn]
         lines.append(f"{kn}")
         nd = max(len(x) for x in m["dispatches"].values())
-        lines.append(f"  dispatches per run {nd}  vgpr {m['vgpr']}  agpr {m['agpr']}  "
-                     f"lds {m['lds']}")
+        lines.append(f"  dispatches per run {nd}  static lds {m['lds']}")
         wc = s.get("SQ_WAVE_CYCLES")
         if wc:
             lines.append("  per-wave fraction of lifetime: " + "  ".join(

@@ -133,12 +133,14 @@ def pmc_summary(fetch_dir, write_dir, workload, lens, call_bytes):
 
 
 def kt_summary(kt_dir):
-    """Text table of a rocprofv3 --kernel-trace --stats run (its kernel_stats.csv)."""
+    """Text table of a rocprofv3 --kernel-trace --stats run (its kernel_stats.csv): the 16
+    kernels with the most time, then every other pnmix kernel."""
     rows = _csv_rows(kt_dir, "kernel_stats.csv")
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    rows = rows[:16] + [r for r in rows[16:] if "pnmix::" in r["Name"]]
     lines = [f"{'kernel':72s} {'calls':>7s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} "
              f"{'time %':>7s}"]
-    for r in rows[:24]:
+    for r in rows:
         lines.append(f"{r['Name'][:72]:72s} {int(r['Calls']):7d} "
                      f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
                      f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):7.2f}")

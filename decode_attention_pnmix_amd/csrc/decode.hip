@@ -30,10 +30,9 @@
 // * p.V runs on the int8 matrix cores too.  w = p S_tg per (head, key, value group) becomes
 //   fixed point below 2^22 with a per-head power-of-two scale set from that head's largest p on
 //   the page times the page's largest value scale (so the result does not depend on how pages
-//   are split); its three base-256 digits go to an LDS table whose rows are (head, digit), plus
-//   one row of ones per head whose product is the column sum of the codes (it restores the
-//   offset of the two lower digits, stored as u - 128).  The B operand is again the packed value
-//   byte masked in place.  A byte holds 4 consecutive channels of one token (byte column m =
+//   are split); its three base-256 digits (the two lower ones balanced, in [-128, 127]) go to an
+//   LDS table whose rows are (head, digit).  The B operand is again the packed value byte
+//   masked in place.  A byte holds 4 consecutive channels of one token (byte column m =
 //   channels 4m..4m+3, the N tokens of a column contiguous), so a tile takes 8 byte columns
 //   (32 channels, inside one value group of g_V >= 32) and two of their four 2-bit fields:
 //   column n < 8 reads byte column n with field f, column n >= 8 byte column n - 8 with field
@@ -55,7 +54,9 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 constexpr int kMergeSplits = 136;  // the planner's cap: beyond it the merge costs more than it saves
 constexpr int kWS = kN + 16;     // row stride of the p.V digit table (rows on distinct banks)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kTwo23 = 8388608.0f;  // y + 2^23 rounds y in [0, 2^23) to an integer (RNE)
+// y + 2^23 + 0x8080 rounds y in [0, 2^23 - 0x8080) to an integer (RNE) and leaves y + 0x8080
+// in the low 23 bits of the float: bytes 0 and 1 xor 0x80 are y's balanced base-256 digits
+constexpr float kTwo23b = 8421504.0f;
 
 
 template <int D, int KH>
@@ -193,16 +194,14 @@ __device__ __forceinline__ float combine4(const v4i& c) {
   const int lo = c[0] + (c[1] << 8), hi = c[2] + (c[3] << 8);
   return __builtin_fmaf((float)hi, 65536.0f, (float)lo);
 }
-// a * f16(low or high half of h) + c in one v_fma_mix_f32 (exact widening, one rounding)
+// a * f16(low or high half of h) + c with one rounding (the fp16 operand widens exactly); the
+// compiler selects v_fma_mix_f32 for it and keeps track of its hazards (an inline-asm form
+// would not get the wait state a transcendental result needs before its use)
 __device__ __forceinline__ float fma_mix_lo(float a, uint32_t h, float c) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(h), "v"(c));
-  return r;
+  return __builtin_fmaf(a, f16lo(h), c);
 }
 __device__ __forceinline__ float fma_mix_hi(float a, uint32_t h, float c) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(h), "v"(c));
-  return r;
+  return __builtin_fmaf(a, f16hi(h), c);
 }
 typedef uint16_t v2u16 __attribute__((ext_vector_type(2)));
 // packed max of two pairs of non-negative fp16 values through their bit patterns (which order
@@ -211,13 +210,11 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2u16, a),
                                                                 __builtin_bit_cast(v2u16, b)));
 }
-// sum_t x_t B_t from the p.V digit sums: c[0], c[1] of digits stored as u - 128, c[2] of the
-// top digit, c[3] = sum_t B_t from the ones row; every partial is exact in int32 and the
-// three terms are non-negative (no cancellation in fp32)
+// sum_t x_t B_t from the p.V digit sums: c[0], c[1] of the balanced low digits, c[2] of the
+// top digit (c[3], the fourth row of each head, is not used); c[0] + 256 c[1] is exact in
+// int32 (|c[d]| < 2^20)
 __device__ __forceinline__ float combine_pv(const v4i& c) {
-  // (c0 + 128 c3) + 256 (c1 + 128 c3) = c0 + 256 c1 + 32896 c3: the sum over the two low
-  // digits, in [0, 2^31) (0 <= c3 < 2^16: a 24-bit product)
-  const int lo = c[0] + (c[1] << 8) + (int)__umul24((uint32_t)c[3], 32896u);
+  const int lo = c[0] + (c[1] << 8);
   return __builtin_fmaf((float)c[2], 65536.0f, (float)lo);
 }
 // bytes 0..2 of four words, transposed: out[d] byte i = byte d of y[i]
@@ -705,12 +702,6 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 
   // ---- once per split: clear the digit table, salient ranks, scaled queries
   for (int i = lane * 16; i < a.lds_T; i += 64 * 16) *reinterpret_cast<v4u*>(T + i) = v4u{0, 0, 0, 0};
-  // p.V digit rows (head, 3) are all ones: their sums are the column sums of the value codes
-  for (int i = lane; i < NT * 4 * (kN / 16); i += 64) {
-    const int r = i / (kN / 16), c16 = i % (kN / 16);
-    *reinterpret_cast<v4u*>(W + (4 * r + 3) * kWS + 16 * c16) =
-        v4u{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
-  }
   // Upper-bit digit rows: the digits of a salient channel are the same words as its LSB digits
   // (same qt S product), placed at the channel's salient rank.  Each LSB prep unit scatters the
   // digit bytes of its salient channels there; hoff[k] holds, for the unit's 4 channels, the
@@ -891,8 +882,9 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     // ---- p.V fixed point, per head: x = rne(p S 2^sh) with 2^sh above the head's largest
     // p on this page times the page's largest value scale, so 0 <= x <= 2^22 (22 bits relative
     // to the page's own largest term, whatever the running maximum of earlier pages).  The
-    // bound has a bit of headroom: top is a rounded product and x rounds once more, so x can
-    // reach 2^22 itself, and byte 2 of x then stays below 128 (never the int8 sign bit).
+    // bound has headroom: top is a rounded product and p 2^sh and x round once more each, so x
+    // can reach 2^22 (and a few units more); the top digit of x + 0x8080 then stays at most 65,
+    // far below the int8 sign bit.
     uint32_t svm2 = 0u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) svm2 = pk_max_u16(svm2, sSo[e]);  // S >= 0: bit order
@@ -917,17 +909,17 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
         if (top > 0.0f) e = (int)((__builtin_bit_cast(uint32_t, top) >> 23) & 0xFF) - 127;
         sh = min(max(21 - e, -126), 126);
       }
-      const float sv2 = pow2i(sh);
       inv_sv[t] = pow2i(-sh);
       pscl[t] = inv_sv[t] * vfw;
+      // p 2^sh = 2^(lg - (mn - sh)) in one exp2; the sum of p is that of p 2^sh times 2^-sh
+      const float msh = mn - (float)sh;
       float ps = 0.0f;
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
-        const float p = __builtin_amdgcn_exp2f(lg[t][bb] - mn);
-        ps += p;
-        pw[t][bb] = p * sv2;
+        pw[t][bb] = __builtin_amdgcn_exp2f(lg[t][bb] - msh);
+        ps += pw[t][bb];
       }
-      l_run[t] = l_run[t] * alpha + ps;
+      l_run[t] = __builtin_fmaf(ps, inv_sv[t], l_run[t] * alpha);
       if (__any(alpha != 1.0f)) {
 #pragma unroll
         for (int v = 0; v < NTV; ++v) acc[t][v] *= alpha;
@@ -962,15 +954,15 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
           for (int e = 0; e < 4; ++e) {
             zs = fma_mix_lo(pw[t][2 * e], zz[e], zs);
             zs = fma_mix_hi(pw[t][2 * e + 1], zz[e], zs);
-            // 2^23 + x in the float's bits: x in bytes 0..2 (byte 2 <= 64)
-            x[2 * e] = __builtin_bit_cast(uint32_t, fma_mix_lo(pw[t][2 * e], ss[e], kTwo23));
-            x[2 * e + 1] = __builtin_bit_cast(uint32_t, fma_mix_hi(pw[t][2 * e + 1], ss[e], kTwo23));
+            // x + 0x8080 in the float's bits 0..22 (byte 2 <= 65)
+            x[2 * e] = __builtin_bit_cast(uint32_t, fma_mix_lo(pw[t][2 * e], ss[e], kTwo23b));
+            x[2 * e + 1] = __builtin_bit_cast(uint32_t, fma_mix_hi(pw[t][2 * e + 1], ss[e], kTwo23b));
           }
           zacc[t][bk] = __builtin_fmaf(zs, inv_sv[t], zacc[t][bk]);
           uint32_t d0[3], d1[3];
           transpose3(x, d0);
           transpose3(x + 4, d1);
-          // digit rows 0, 1 as int8 u - 128 (the ones row 3 restores the offset); row 2 as is
+          // digit rows 0, 1: the balanced digits (bytes xor 0x80); row 2: the top digit
           uint8_t* row = W + (t * 16 + 4 * qb) * kWS + 8 * oct;
           *reinterpret_cast<uint2*>(row) = make_uint2(d0[0] ^ 0x80808080u, d1[0] ^ 0x80808080u);
           *reinterpret_cast<uint2*>(row + kWS) = make_uint2(d0[1] ^ 0x80808080u, d1[1] ^ 0x80808080u);

@@ -94,7 +94,11 @@ __device__ __forceinline__ uint32_t code_bits(float x, float mn, float inv, floa
   return __float_as_uint(__builtin_amdgcn_fmed3f(y, 0.0f, L) + kRound);
 }
 // f16(low or high half of w) - mn in one v_fma_mix_f32 (w widened exactly, times 1, plus -mn:
-// the single rounding of the fp32 subtraction), then the rest of code_bits.
+// the single rounding of the fp32 subtraction), then the rest of code_bits.  Written out
+// because the compiler turns fma(x, 1, c) into a conversion and a subtraction.  The compiler
+// does not add wait states for an inline-asm consumer, so both operands must come from loads
+// or plain VALU results (here: the loaded fp16 words and the negated group minimum), never
+// straight from a transcendental instruction.
 __device__ __forceinline__ float sub_lo(uint32_t w, float nmn) {
   float r;
   asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(nmn));

@@ -20,6 +20,30 @@ __device__ __forceinline__ float h2f(uint16_t u) {
   return static_cast<float>(__builtin_bit_cast(_Float16, u));
 }
 
+// IEEE square root, round to nearest even, of a = 0, a normal float, +inf or NaN (no input
+// below 2^-96 other than 0, so the hardware estimate needs no pre-scaling).  v_sqrt_f32 is
+// within one ulp of the root r; the neighbours s - ulp and s + ulp decide: a <= (s - ulp) s
+// puts r below the midpoint under s, a > (s + ulp) s above the midpoint over s (each residual
+// one fma, exact enough to sign the difference).
+__device__ __forceinline__ float sqrt_rn(float a) {
+  const float s = __builtin_amdgcn_sqrtf(a);
+  const float sd = __builtin_bit_cast(float, __builtin_bit_cast(int, s) - 1);
+  const float su = __builtin_bit_cast(float, __builtin_bit_cast(int, s) + 1);
+  const float vd = __builtin_fmaf(-sd, s, a);
+  const float vu = __builtin_fmaf(-su, s, a);
+  float r = vd <= 0.0f ? sd : s;
+  r = vu > 0.0f ? su : r;
+  return r;
+}
+
+// ||(x, y)|| of one RoPE pair of fp16 values in fp32: both squares are exact, their sum rounds
+// once and the square root once (the same value as sqrtf(x * x + y * y) for finite x, y; the
+// squares' sum is 0 or at least 2^-48).
+__device__ __forceinline__ float pair_norm(uint16_t x, uint16_t y) {
+  const float xf = h2f(x), yf = h2f(y);
+  return sqrt_rn(__builtin_fmaf(xf, xf, __builtin_fmaf(yf, yf, 0.0f)));
+}
+
 // fp32 -> fp16, round to nearest even (v_cvt_f16_f32 under the default rounding mode), with
 // fp16 subnormals.
 __device__ __forceinline__ uint16_t f2h(float f) {

@@ -86,11 +86,7 @@ __global__ void __launch_bounds__(2 * D) prefill_k_pages_kernel(PrefillArgs a) {
       const int te = min(kChunkTokens * (c + 1), a.P);
       float s = 0.0f;
       for (int t = kChunkTokens * c; t < te; ++t) {
-        const float x = h2f(tile[(t - tok0) * D + ch0]);
-        const float y = h2f(tile[(t - tok0) * D + ch1]);
-        const float xx = x * x;
-        const float yy = y * y;
-        s = s + sqrtf(xx + yy);
+        s = s + pair_norm(tile[(t - tok0) * D + ch0], tile[(t - tok0) * D + ch1]);
       }
       const int64_t head = (int64_t)b * (a.H_q + a.H_kv) + a.H_q + h;
       a.chunk_sums[(head * a.n_chunks + c) * NP + i] = s;

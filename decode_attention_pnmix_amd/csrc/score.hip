@@ -5,9 +5,9 @@
 // floor(r d/2) pairs of each KV head form a bit mask stored once (Korean summary page,
 // "무엇과 다른가": B x L x H_kv x d/2 bits).
 //
-// Two passes.  Pass 1 gives each (sequence, head, 64-token chunk) one wave; the wave stages 32
-// token rows at a time in LDS with 16-byte loads, and lane i owns RoPE pair i and adds its pair
-// norms over the chunk in ascending token order.  Pass 2 gives each (sequence, KV head) one
+// Two passes.  Pass 1 gives each (sequence, head, 64-token chunk) one wave; the wave stages the
+// chunk's token rows in LDS with 16-byte loads all in flight at once, and lane i owns RoPE pair
+// i and adds its pair norms over the chunk in ascending token order.  Pass 2 gives each (sequence, KV head) one
 // workgroup: its waves add the chunk sums of one head each in ascending chunk order (the loads
 // go out 32 chunks at a time), divide by P, then wave 0 forms sigma, ranks the pairs through
 // LDS and writes the mask with a wave ballot.  The summation order is fixed, so sigma and the
@@ -19,62 +19,60 @@ namespace pnmix {
 
 constexpr int kChunk = 64;
 
-constexpr int kSub = 32;  // tokens staged in LDS at a time
-
 // Key chunks cover_lo..cover_hi are skipped when the caller computes them elsewhere (the fused
-// prefill's page workgroups); cover_lo > cover_hi skips none.
+// prefill's page workgroups); cover_lo > cover_hi skips none.  D is the head dim (row offsets
+// in the LDS tile are then immediates).
+template <int D>
 __global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           float* __restrict__ chunk_sums,
-                                                          int H_q, int H_kv, int d, int pairing,
+                                                          int H_q, int H_kv, int pairing,
                                                           int P, int n_chunks, int cover_lo,
                                                           int cover_hi) {
-  __shared__ __align__(16) uint16_t tile[kSub * 128];  // kSub token rows of up to 128 fp16
+  __shared__ __align__(16) uint16_t tile[kChunk * D];  // the chunk's token rows
   const int seq_head = blockIdx.x;  // b * (H_q + H_kv) + head (grid x: no 65535 limit)
   const int chunk = blockIdx.y;
   const int H = H_q + H_kv;
   const int b = seq_head / H;
   const int head = seq_head % H;
   if (head >= H_q && chunk >= cover_lo && chunk <= cover_hi) return;  // whole workgroup
-  const int np = d / 2;
+  constexpr int np = D / 2;
+  constexpr int kLoads = kChunk * D / 8 / 64;  // 16-byte loads per lane for a full chunk
   const int i = threadIdx.x;
-  const uint16_t* src = head < H_q ? q + ((int64_t)b * H_q + head) * P * d
-                                   : k + ((int64_t)b * H_kv + (head - H_q)) * P * d;
+  const uint16_t* src = head < H_q ? q + ((int64_t)b * H_q + head) * P * D
+                                   : k + ((int64_t)b * H_kv + (head - H_q)) * P * D;
   const int c0 = pairing == PNMIX_PAIRS_ADJACENT ? 2 * i : i;
   const int c1 = pairing == PNMIX_PAIRS_ADJACENT ? 2 * i + 1 : i + np;
   const int t0 = chunk * kChunk;
-  const int t1 = min(t0 + kChunk, P);
-  // The wave copies kSub token rows at a time into LDS with 16-byte loads (the rows of a
-  // (sequence, head) are contiguous; d * 2 bytes is a multiple of 16), or with 2-byte loads when
-  // the rows are not 16-byte aligned; then lane i adds the norms of pair i over those tokens in
-  // ascending order, as before.
-  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
-  float s = 0.0f;
-  for (int ts = t0; ts < t1; ts += kSub) {
-    const int rows = min(kSub, t1 - ts);
-    const uint16_t* g = src + (int64_t)ts * d;
-    if (vec) {
-      const int n16 = rows * d / 8;
-      for (int x = i; x < n16; x += 64)
-        reinterpret_cast<uint4*>(tile)[x] = reinterpret_cast<const uint4*>(g)[x];
-    } else {
-      for (int x = i; x < rows * d; x += 64) tile[x] = g[x];
-    }
-    __syncthreads();
-    if (i < np) {
-#pragma unroll 8
-      for (int t = 0; t < rows; ++t) {
-        const float x = h2f(tile[t * d + c0]);
-        const float y = h2f(tile[t * d + c1]);
-        const float a = x * x;
-        const float bb = y * y;
-        s = s + sqrtf(a + bb);
-      }
-    }
-    __syncthreads();  // the tile is refilled
+  const int rows = min(kChunk, P - t0);
+  const uint16_t* g = src + (int64_t)t0 * D;
+  // The chunk's rows go to LDS in one round: a full chunk of 16-byte-aligned rows (the rows of
+  // a (sequence, head) are contiguous; D * 2 bytes is a multiple of 16) with every load issued
+  // before the first store, a partial or unaligned one element by element.  Then lane i adds the
+  // norms of pair i over the chunk's tokens in ascending order.
+  if (rows == kChunk && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+    uint4 v[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) v[j] = reinterpret_cast<const uint4*>(g)[i + 64 * j];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) reinterpret_cast<uint4*>(tile)[i + 64 * j] = v[j];
+  } else {
+    for (int x = i; x < rows * D; x += 64) tile[x] = g[x];
   }
-  if (i < np) chunk_sums[((int64_t)seq_head * n_chunks + chunk) * np + i] = s;
+  __syncthreads();
+  float s = 0.0f;
+  if (i < np) {
+    if (rows == kChunk) {
+#pragma unroll 8
+      for (int t = 0; t < kChunk; ++t) s = s + pair_norm(tile[t * D + c0], tile[t * D + c1]);
+    } else {
+      for (int t = 0; t < rows; ++t) s = s + pair_norm(tile[t * D + c0], tile[t * D + c1]);
+    }
+    chunk_sums[((int64_t)seq_head * n_chunks + chunk) * np + i] = s;
+  }
 }
+
+constexpr int kSelLoads = 32;  // chunk-sum loads in flight per lane
 
 __global__ void __launch_bounds__(256) score_select_kernel(const float* __restrict__ chunk_sums,
                                                            float* __restrict__ sigma,
@@ -95,14 +93,15 @@ __global__ void __launch_bounds__(256) score_select_kernel(const float* __restri
     const int head = r < ng ? h * ng + r : H_q + h;
     if (lane < np) {
       const float* cs = chunk_sums + ((int64_t)(seq * H + head) * n_chunks) * np + lane;
-      // the adds stay in ascending chunk order; the loads go out 32 at a time
+      // the adds stay in ascending chunk order; the loads go out kSelLoads at a time
       float s = 0.0f;
-      for (int c0 = 0; c0 < n_chunks; c0 += 32) {
-        float v[32];
+      for (int c0 = 0; c0 < n_chunks; c0 += kSelLoads) {
+        float v[kSelLoads];
 #pragma unroll
-        for (int j = 0; j < 32; ++j) v[j] = c0 + j < n_chunks ? cs[(int64_t)(c0 + j) * np] : 0.0f;
+        for (int j = 0; j < kSelLoads; ++j)
+          v[j] = c0 + j < n_chunks ? cs[(int64_t)(c0 + j) * np] : 0.0f;
 #pragma unroll
-        for (int j = 0; j < 32; ++j)
+        for (int j = 0; j < kSelLoads; ++j)
           if (c0 + j < n_chunks) s = s + v[j];
       }
       means[r][lane] = s / (float)P;
@@ -137,8 +136,22 @@ hipError_t launch_score_chunks(const pnmix_cfg& c, int B, int P, const uint16_t*
                                hipStream_t stream) {
   const int n_chunks = (P + kChunk - 1) / kChunk;
   dim3 g1(B * (c.H_q + c.H_kv), n_chunks);
-  hipLaunchKernelGGL(score_chunks_kernel, g1, dim3(64), 0, stream, q, k, chunk_sums, c.H_q,
-                     c.H_kv, c.d, c.pairing, P, n_chunks, cover_lo, cover_hi);
+  switch (c.d) {
+    case 32:
+      hipLaunchKernelGGL(score_chunks_kernel<32>, g1, dim3(64), 0, stream, q, k, chunk_sums,
+                         c.H_q, c.H_kv, c.pairing, P, n_chunks, cover_lo, cover_hi);
+      break;
+    case 64:
+      hipLaunchKernelGGL(score_chunks_kernel<64>, g1, dim3(64), 0, stream, q, k, chunk_sums,
+                         c.H_q, c.H_kv, c.pairing, P, n_chunks, cover_lo, cover_hi);
+      break;
+    case 128:
+      hipLaunchKernelGGL(score_chunks_kernel<128>, g1, dim3(64), 0, stream, q, k, chunk_sums,
+                         c.H_q, c.H_kv, c.pairing, P, n_chunks, cover_lo, cover_hi);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -46,9 +46,10 @@ __global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __rest
   const int t0 = chunk * kChunk;
   const int rows = min(kChunk, P - t0);
   const uint16_t* g = src + (int64_t)t0 * D;
-  // The chunk's rows go to LDS in one round: a full chunk of 16-byte-aligned rows (the rows of
-  // a (sequence, head) are contiguous; D * 2 bytes is a multiple of 16) with every load issued
-  // before the first store, a partial or unaligned one element by element.  Then lane i adds the
+  // The chunk's rows go to LDS: a full chunk of 16-byte-aligned rows (the rows of a (sequence,
+  // head) are contiguous; D * 2 bytes is a multiple of 16) in one round, every load issued
+  // before the first store; the last, partial chunk of a prompt with 16-byte loads in a loop;
+  // unaligned rows element by element.  Then lane i adds the
   // norms of pair i over the chunk's tokens in ascending order.
   if (rows == kChunk && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
     uint4 v[kLoads];
@@ -56,6 +57,9 @@ __global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __rest
     for (int j = 0; j < kLoads; ++j) v[j] = reinterpret_cast<const uint4*>(g)[i + 64 * j];
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) reinterpret_cast<uint4*>(tile)[i + 64 * j] = v[j];
+  } else if ((reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+    for (int x = i; x < rows * D / 8; x += 64)
+      reinterpret_cast<uint4*>(tile)[x] = reinterpret_cast<const uint4*>(g)[x];
   } else {
     for (int x = i; x < rows * D; x += 64) tile[x] = g[x];
   }

@@ -19,23 +19,26 @@ namespace pnmix {
 
 constexpr int kChunk = 64;
 
-// Key chunks cover_lo..cover_hi are skipped when the caller computes them elsewhere (the fused
-// prefill's page workgroups); cover_lo > cover_hi skips none.  D is the head dim (row offsets
-// in the LDS tile are then immediates).
+// Key chunks that lie wholly inside one of the first skip_pages pages of N tokens after skip_Ns
+// sinks are skipped: the fused prefill's page workgroups add them up (skip_pages = 0 skips
+// none).  D is the head dim (row offsets in the LDS tile are then immediates).
 template <int D>
 __global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           float* __restrict__ chunk_sums,
                                                           int H_q, int H_kv, int pairing,
-                                                          int P, int n_chunks, int cover_lo,
-                                                          int cover_hi) {
+                                                          int P, int n_chunks, int skip_Ns,
+                                                          int skip_pages) {
   __shared__ __align__(16) uint16_t tile[kChunk * D];  // the chunk's token rows
   const int seq_head = blockIdx.x;  // b * (H_q + H_kv) + head (grid x: no 65535 limit)
   const int chunk = blockIdx.y;
   const int H = H_q + H_kv;
   const int b = seq_head / H;
   const int head = seq_head % H;
-  if (head >= H_q && chunk >= cover_lo && chunk <= cover_hi) return;  // whole workgroup
+  if (head >= H_q && skip_pages > 0) {  // whole workgroup
+    const int u = chunk * kChunk - skip_Ns;
+    if (u >= 0 && u + kChunk <= kN * skip_pages && (u % kN) + kChunk <= kN) return;
+  }
   constexpr int np = D / 2;
   constexpr int kLoads = kChunk * D / 8 / 64;  // 16-byte loads per lane for a full chunk
   const int i = threadIdx.x;
@@ -136,22 +139,22 @@ __global__ void __launch_bounds__(256) score_select_kernel(const float* __restri
 }
 
 hipError_t launch_score_chunks(const pnmix_cfg& c, int B, int P, const uint16_t* q,
-                               const uint16_t* k, float* chunk_sums, int cover_lo, int cover_hi,
-                               hipStream_t stream) {
+                               const uint16_t* k, float* chunk_sums, int skip_Ns,
+                               int skip_pages, hipStream_t stream) {
   const int n_chunks = (P + kChunk - 1) / kChunk;
   dim3 g1(B * (c.H_q + c.H_kv), n_chunks);
   switch (c.d) {
     case 32:
       hipLaunchKernelGGL(score_chunks_kernel<32>, g1, dim3(64), 0, stream, q, k, chunk_sums,
-                         c.H_q, c.H_kv, c.pairing, P, n_chunks, cover_lo, cover_hi);
+                         c.H_q, c.H_kv, c.pairing, P, n_chunks, skip_Ns, skip_pages);
       break;
     case 64:
       hipLaunchKernelGGL(score_chunks_kernel<64>, g1, dim3(64), 0, stream, q, k, chunk_sums,
-                         c.H_q, c.H_kv, c.pairing, P, n_chunks, cover_lo, cover_hi);
+                         c.H_q, c.H_kv, c.pairing, P, n_chunks, skip_Ns, skip_pages);
       break;
     case 128:
       hipLaunchKernelGGL(score_chunks_kernel<128>, g1, dim3(64), 0, stream, q, k, chunk_sums,
-                         c.H_q, c.H_kv, c.pairing, P, n_chunks, cover_lo, cover_hi);
+                         c.H_q, c.H_kv, c.pairing, P, n_chunks, skip_Ns, skip_pages);
       break;
     default:
       return hipErrorInvalidValue;
@@ -171,7 +174,7 @@ hipError_t launch_score_select(const pnmix_cfg& c, int B, int P, const float* ch
 hipError_t launch_score(const pnmix_cfg& c, int B, int P, const uint16_t* q, const uint16_t* k,
                         float* sigma, uint32_t* mask, void* ws, hipStream_t stream) {
   float* chunk_sums = static_cast<float*>(ws);
-  const hipError_t e = launch_score_chunks(c, B, P, q, k, chunk_sums, 1, 0, stream);
+  const hipError_t e = launch_score_chunks(c, B, P, q, k, chunk_sums, 0, 0, stream);
   return e != hipSuccess ? e : launch_score_select(c, B, P, chunk_sums, sigma, mask, stream);
 }
 

@@ -769,6 +769,17 @@ def test_prefill_fused(case):
         say(f"[prefill-fused] {name} B={B} P={L_} pages={n_full}")
 
 
+@pytest.mark.parametrize("n_s", [0, 16, 64, 96])
+def test_prefill_fused_sink_offsets(n_s):
+    """Sink counts that put the pages on, or off, the 64-token chunk grid: the page workgroups
+    add up exactly the key chunks lying inside their page and the score kernel the others."""
+    import dataclasses
+    w = dataclasses.replace(synth.WORKLOADS["qwen3-8b-1L-32k"], name=f"sinks{n_s}", N_s=n_s)
+    for L_ in (n_s + 3 * 128 + 40, n_s + 2 * 128):
+        n_full = _prefill_check(w, 2, L_)
+        say(f"[prefill-fused] N_s={n_s} P={L_} pages={n_full}")
+
+
 def test_prefill_fused_long_prompt():
     """The 16K-token prompt at B = 1 (Llama-3.1-8B shape, G = 64, r = 0.4): 127 pages per KV head."""
     w = synth.WORKLOADS["llama3.1-8b-32L-b110-8k"]

@@ -18,9 +18,10 @@
 //   logit(h, t) = sum_c (qt_hc S_c) code_tc + sum_c qt_hc Z_c,   qt = q * sm_scale * log2(e)
 //   o(h, c)    += sum_t (p_ht S_tg) code_tc + sum_t p_ht Z_tg
 // * q.K runs on the int8 matrix cores (v_mfma_i32_16x16x64_i8).  The per-page products
-//   qt_hc S_c become 32-bit fixed point (a per-head power-of-two scale from max|qt| max S) and are
-//   split into four signed base-256 digits: rows of the A operand are (head, digit), columns of
-//   the B operand are 16 keys, K is 64 channels.  The B operand is the packed code itself: the
+//   qt_hc S_c become 32-bit fixed point (one power-of-two scale per page for the GQA group,
+//   from the group's max|qt| and the page's max S) and are split into four signed base-256
+//   digits: rows of the A operand are (head, digit), columns of the B operand are 16 keys, K is
+//   64 channels.  The B operand is the packed code itself: the
 //   LSB plane byte of (channel, 8 tokens) and the upper-bit plane byte of (salient channel,
 //   4 tokens) are masked in place, one bit field per MFMA, so a tile holds the keys 8i + b of a
 //   page (i = 0..15) and a 16-byte load of either plane feeds eight tiles.  The upper-bit rows

@@ -695,11 +695,11 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 
   // LDS: q.K digit table T [KG][NT][16][TL] bytes; p.V digit table W [NT][16][kWS] bytes (one
   // value group at a time);
-  // bias [KG][NH] f32; scaled queries [NH][D] f32.
+  // bias [KG][NH][2] f32 (a head's sums over its two 16-lane rows); scaled queries [NH][D] f32.
   uint8_t* T = lds;
   uint8_t* W = lds + a.lds_T;
   float* biasl = reinterpret_cast<float*>(W + NT * 16 * kWS);
-  float* qs = biasl + 4 * NH;
+  float* qs = biasl + 2 * 4 * NH;
 
   // ---- once per split: clear the digit table, salient ranks, scaled queries
   for (int i = lane * 16; i < a.lds_T; i += 64 * 16) *reinterpret_cast<v4u*>(T + i) = v4u{0, 0, 0, 0};
@@ -796,13 +796,15 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
 #pragma unroll
         for (int i = 0; i < 4; ++i) y[i] = digits4((int)m4[i]);
         transpose4(y, dg);
-        bz = group_sum<(JL < 64 ? JL : 64)>(bz);
+        // sums over the unit's lanes of one head within a 16-lane row (DPP only); a head
+        // spanning two rows leaves its two row sums in LDS and the reader adds them
+        bz = group_sum<(JL < 16 ? JL : 16)>(bz);
         if (ok) {
           const int t = hu / 4, hl = hu % 4;
           uint8_t* row = T + ((kg * NT + t) * 16 + 4 * hl) * TL + 4 * j;
 #pragma unroll
           for (int d = 0; d < 4; ++d) *reinterpret_cast<uint32_t*>(row + d * TL) = dg[d];
-          if (j == 0) biasl[kg * NH + hu] = bz;
+          if (j % (JL < 16 ? JL : 16) == 0) biasl[2 * (kg * NH + hu) + (j >> 4)] = bz;
         }
         // the same digit words at the salient ranks of the upper-bit rows
         uint8_t* tb = T + kg * NT * 16 * TL;
@@ -831,7 +833,10 @@ __device__ void page_split(const DecodeArgs& a, uint8_t* lds, int split, int64_t
     }
     float bias[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) bias[t] = biasl[kg_lane * NH + 4 * t + qb];
+    for (int t = 0; t < NT; ++t) {
+      const float* bp = biasl + 2 * (kg_lane * NH + 4 * t + qb);
+      bias[t] = JL > 16 ? bp[0] + bp[1] : bp[0];
+    }
 
     // ---- q.K: tile b holds keys 8 oct + b; the lane's q.K output head is 4t + qb
     v4u wH0[KHM], wH1[KHM];
@@ -1222,7 +1227,7 @@ static size_t lds_T_bytes(const pnmix_cfg& c) {
 static size_t lds_bytes(const pnmix_cfg& c) {
   const int NT = n_tiles(c);
   const size_t W = (size_t)NT * 16 * kWS;  // one value group's rows of every head tile
-  return lds_T_bytes(c) + W + 4 * 4 * NT * 4 + (size_t)4 * NT * c.d * 4;
+  return lds_T_bytes(c) + W + 2 * 4 * 4 * NT * 4 + (size_t)4 * NT * c.d * 4;
 }
 
 static size_t lds_fp16_bytes(const pnmix_cfg& c) {

@@ -302,9 +302,11 @@ def prefill_timing(w, cfg, P, synth, torch, np, reps=6):
     """The prompt of one layer, scored and its full pages quantized: score then one launch of key
     and value pages (pnmix_score_prefill + pnmix_quantize_kv_pages) against the one-pass
     pnmix_prefill_fused; median of `reps` event-timed runs each, for the workload's prompt at
-    its batch and its long prompt at B = 1 if it has one."""
+    its batch and its long prompt at B = 1 if it has one.  The fused entry point packs the
+    (b_H, b_L, b_V) = (3, 1, 2) widths only; other widths time the two-step sequence alone."""
     dev = "cuda"
     out = {}
+    fused = (w.b_H, w.b_L, w.b_V) == (3, 1, 2)
     for (Bs, Ps) in ([(w.B, w.P)] + ([(1, w.prefill_score_P)] if w.prefill_score_P else [])):
         sq = synth.pair_scales(w.H_q, w.d // 2, w.sigma_ln, dev, w.name, 0, "q")
         sk = synth.pair_scales(w.H_kv, w.d // 2, w.sigma_ln, dev, w.name, 0, "k")
@@ -321,8 +323,8 @@ def prefill_timing(w, cfg, P, synth, torch, np, reps=6):
             _, vj = c.page_jobs(vpp, w.N_s, 0, n_full)
         ws_s = torch.empty(P.pnmix_score_workspace_bytes(cfg, Bs, Ps), dtype=torch.uint8,
                            device=dev)
-        ws_f = torch.empty(P.pnmix_prefill_fused_workspace_bytes(cfg, Bs, Ps), dtype=torch.uint8,
-                           device=dev)
+        ws_f = torch.empty(P.pnmix_prefill_fused_workspace_bytes(cfg, Bs, Ps) if fused else 256,
+                           dtype=torch.uint8, device=dev)
         tu, tf = [], []
         for rep in range(reps + 1):
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -332,8 +334,9 @@ def prefill_timing(w, cfg, P, synth, torch, np, reps=6):
                 c.mask.copy_(m)
                 P.pnmix_quantize_kv_pages(cfg, kj, vj, c.mask)
             e[1].record()
-            P.pnmix_prefill_fused(cfg, qpp, kpp, vpp, c.k_pages, c.v_pages, mask=c.mask,
-                                  ws=ws_f, want_sigma=False)
+            if fused:
+                P.pnmix_prefill_fused(cfg, qpp, kpp, vpp, c.k_pages, c.v_pages, mask=c.mask,
+                                      ws=ws_f, want_sigma=False)
             e[2].record()
             torch.cuda.synchronize()
             if rep:
@@ -341,9 +344,11 @@ def prefill_timing(w, cfg, P, synth, torch, np, reps=6):
                 tf.append(e[1].elapsed_time(e[2]) * 1e3)
         nb_read = Bs * Ps * (w.H_q + 2 * w.H_kv) * w.d * 2
         out[f"B{Bs}_P{Ps}"] = {"pages_per_kv_head": n_full,
-                               "score_then_quantize_us": float(np.median(tu)),
-                               "fused_us": float(np.median(tf)),
-                               "fused_GBps_of_qkv_read": nb_read / float(np.median(tf)) / 1e3}
+                               "score_then_quantize_us": float(np.median(tu))}
+        if fused:
+            out[f"B{Bs}_P{Ps}"].update({"fused_us": float(np.median(tf)),
+                                        "fused_GBps_of_qkv_read":
+                                            nb_read / float(np.median(tf)) / 1e3})
         del qpp, kpp, vpp, c
     return out
 
@@ -375,6 +380,11 @@ def main():
                          "for the workload's prompts and exit")
     ap.add_argument("--kt-summary", metavar="KT_DIR",
                     help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--bits", type=int, nargs=3, metavar=("B_H", "B_L", "B_V"),
+                    help="run the workload with these key and value bit widths (the sweep of the "
+                         "PN-Mix paper's bit-width appendix; any width but (3, 1, 2) takes the "
+                         "generic decode kernel)")
+    ap.add_argument("--gv", type=int, help="value group size g_V for --bits (default: the workload's)")
     ap.add_argument("--sq-summary", nargs="+", metavar="PMC_DIR",
                     help="print the SQ/TA counter table of rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
@@ -405,6 +415,12 @@ def main():
         sys.exit(1)
     dev = "cuda"
     w = synth.WORKLOADS[args.workload]
+    if args.bits or args.gv:
+        import dataclasses
+        bh, bl, bv = args.bits or (w.b_H, w.b_L, w.b_V)
+        gv = args.gv or w.g_V
+        w = dataclasses.replace(w, name=f"{w.name}-h{bh}l{bl}v{bv}g{gv}", b_H=bh, b_L=bl, b_V=bv,
+                                g_V=gv)
     cfg = P.make_cfg(w.H_q, w.H_kv, w.d, w.pairing, w.n_hi_pairs, G=w.G, b_H=w.b_H, b_L=w.b_L,
                      b_V=w.b_V, g_V=w.g_V, N_s=w.N_s, N=w.N)
     if args.prefill_only:
@@ -653,8 +669,11 @@ def main():
                    "parallelism": "single GPU", "timed": "one HIP graph of K steps"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "pnmix_decode_attn = decode_kernel (page and fp16 splits) + "
-                               "decode_merge_kernel, one call per layer",
+                     "kernel": ("pnmix_decode_attn = decode_kernel (page and fp16 splits) + "
+                                "decode_merge_kernel, one call per layer"
+                                if (w.b_H, w.b_L, w.b_V) == (3, 1, 2) and w.g_V >= 32 else
+                                "pnmix_decode_attn = decode_generic_kernel (vector ALU, every "
+                                "chunk of 128 tokens) + decode_merge_kernel, one call per layer"),
                      "bytes_per_call": call_bytes, "avg_call_us": call_s * 1e6,
                      "call_us_p10": call_p10 * 1e6, "call_us_p90": call_p90 * 1e6,
                      "timed_replays": len(durs), "lens": list(lens_now),

@@ -110,17 +110,30 @@ DEC_CASES = [
     ("h3l1-v16", 3, 1, 16, 128, 32, 128, 8, 2, 40),
     ("h3l1-v2-gV16", 3, 1, 2, 64, 16, 64, 8, 2, 2),
     ("h3l1-v2-gV16-d32", 3, 1, 2, 128, 16, 32, 6, 2, 1),
+    # (r, pairing) other than (0.5, split-half): upper-plane rows of 38 bytes (2-byte aligned),
+    # no upper plane, every channel salient; 4-bit and 3-bit LSB planes; adjacent pairs
+    ("h4l1-v2-r03", 4, 1, 2, 64, 32, 128, 16, 2, 2, 0.3, 1),
+    ("h2l1-v16-r0", 2, 1, 16, 128, 64, 128, 8, 2, 2, 0.0, 1),
+    ("h3l2-v4-r1-adj", 3, 2, 4, 64, 32, 64, 16, 4, 2, 1.0, 0),
+    ("h4l4-v2-d32", 4, 4, 2, 64, 16, 32, 8, 1, 3, 0.5, 1),
+    ("h3l3-v1-adj", 3, 3, 1, 128, 32, 128, 4, 2, 2, 0.5, 0),
+    ("h4l3-v16-r07", 4, 3, 16, 64, 32, 128, 24, 4, 2, 0.7, 1),
+    # 16 query heads per KV head with 32-token groups and fp16 values: the tables exceed 64 KiB
+    # of LDS and the vector-ALU kernel serves the call
+    ("h4l1-v16-ng16-G32", 4, 1, 16, 32, 32, 128, 32, 2, 1),
 ]
 
 
 @pytest.mark.parametrize("case", DEC_CASES, ids=[c[0] for c in DEC_CASES])
 def test_generic_decode(case):
-    name, bH, bL, bV, G, g_V, d, H_q, H_kv, B = case
+    name, bH, bL, bV, G, g_V, d, H_q, H_kv, B = case[:10]
+    r, pairing = case[10:] if len(case) > 10 else (0.5, 1)
     T = 32 + 5 * 128 + 77
-    w = _wl(name, d=d, H_q=H_q, H_kv=H_kv, G=G, g_V=g_V, bH=bH, bL=bL, bV=bV, B=B, T=T)
+    w = _wl(name, d=d, H_q=H_q, H_kv=H_kv, r=r, G=G, g_V=g_V, bH=bH, bL=bL, bV=bV, B=B, T=T,
+            pairing=pairing)
     lc, oc = cfgs(w)
     splits = P.pnmix_decode_splits(lc, B, w.n_pages)
-    say(f"[decode-generic] {name} B={B} splits={splits}")
+    say(f"[decode-generic] {name} B={B} splits={splits} n_hi={lc.n_hi_pairs}")
     qp, k, v, qd = layer_inputs(w, 6, B, T)
     cache = fill_cache_bulk(w, lc, qp, k, v, T)
     out = cache.attend(qd)

@@ -80,7 +80,7 @@ struct ValuChunk {
   float* l_run;
   float* alph;
 
-  __device__ void run(int kind, int T, const uint16_t* krows, const uint16_t* vrows, int t_new,
+  __device__ __forceinline__ void run(int kind, int T, const uint16_t* krows, const uint16_t* vrows, int t_new,
                       const uint8_t* kb, const uint8_t* vb, const uint8_t* vpage, const int* rank,
                       float (&o)[NO]) const {
     const int tid = threadIdx.x;
@@ -363,7 +363,9 @@ constexpr float kTwo23b = 8421504.0f;
 struct GLayout {
   int KSL, KSH, KS, TLB;                      // K-steps of 64 columns: LSB plane, upper plane
   int kOffH, kOffS, kOffZ, vOffS, vOffZ, VRS;  // page offsets; LDS row stride of fp16 values
-  int qs, st, zero, kb, vb, u, pv, total;     // LDS regions
+  int qs, st, zero, kb, vb, u, pv;           // LDS regions of a page
+  int vr, p16, pv16;                          // LDS regions of an fp16 row chunk (over kb..)
+  int total;
 };
 __host__ __device__ inline GLayout glayout(int D, int ng, int KG, int NGV, int n_sal, int bL,
                                            int wH, int bV, int64_t kpb, int64_t vpb) {
@@ -386,16 +388,19 @@ __host__ __device__ inline GLayout glayout(int D, int ng, int KG, int NGV, int n
   L.vb = L.kb + (int)round16((size_t)kpb) + 64;
   const int vbytes = bV == 16 ? kN * L.VRS : (int)round16((size_t)vpb) + 64;
   L.u = L.vb + (int)round16((size_t)vbytes);
-  // region u: T (pages, until the logits are done), then W or P plus the page's p.V sums; the
-  // fp16 row chunks' logits
+  // region u: T (until the logits are done), then W or P plus the page's p.V sums
   const int tb = KG * 4 * ng * L.TLB;
-  const int lgb = ng * kN * 4;
   const int wt = (int)round16(bV == 16 ? (size_t)2 * ng * kPRow : (size_t)NGV * 3 * ng * kWRow);
   const int pvb = ng * D * 4;
   L.pv = L.u + wt;
-  int ub = tb > lgb ? tb : lgb;
-  ub = ub > wt + pvb ? ub : wt + pvb;
-  L.total = L.u + (int)round16((size_t)ub);
+  const int ub = tb > wt + pvb ? tb : wt + pvb;
+  const int tp = L.u + (int)round16((size_t)ub);
+  // fp16 row chunks: the value rows (row stride VRS), p halves, p.V sums, over the page regions
+  L.vr = L.kb;
+  L.p16 = L.vr + (int)round16((size_t)kN * L.VRS);
+  L.pv16 = L.p16 + (int)round16((size_t)2 * ng * kPRow);
+  const int tr = L.pv16 + (int)round16((size_t)pvb);
+  L.total = tp > tr ? tp : tr;
   return L;
 }
 static GLayout glayout_cfg(const pnmix_cfg& c) {
@@ -504,7 +509,6 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
   uint32_t* smaxv = reinterpret_cast<uint32_t*>(st + 536);  // [2] largest value S
   uint32_t* qmaxp = reinterpret_cast<uint32_t*>(st + 538);  // max |qt|
   int16_t* crank = reinterpret_cast<int16_t*>(st + 540);    // [128] channel of salient rank r
-  float* lg = reinterpret_cast<float*>(lds + L.u);
   float* pvb = reinterpret_cast<float*>(lds + L.pv);         // [n_g][D] this page's p.V
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, n = lane & 15, kq = lane >> 4;
@@ -541,12 +545,157 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
   }
   __syncthreads();
   const float qmax = __builtin_bit_cast(float, *qmaxp);
-  const VC vc{a, bh, qs, lg, m_run, l_run, alph};
+  constexpr int NCT = D / 16;  // p.V column tiles of 16 channels
+
+  // p.V over 128 fp16 value rows (LDS, row stride VRS, from byte offset vbase) with p split
+  // into fp16 halves (rows (head, part) of stride kPRow from pbase): job (column tile ct, block
+  // of 8 heads hb8) on v_mfma_f32_16x16x32_f16, K = 32 tokens per step; sums to pvbase [n_g][D]
+  auto pv_fp16 = [&](int vbase, int pbase, int pvbase) {
+    constexpr int NH8 = (NG + 7) / 8;
+    float* pvo = reinterpret_cast<float*>(lds + pvbase);
+    for (int job = wv; job < NCT * NH8; job += 4) {
+      const int ct = job % NCT, hb8 = job / NCT;
+      const int c = 16 * ct + n;
+      const int hh = 8 * hb8 + (n >> 1), part = n & 1;
+      const int prow = hh < ng ? 2 * hh + part : -1;
+      v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        v8h bv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = 32 * ks + 8 * kq + e;
+          bv[e] = *reinterpret_cast<const _Float16*>(lds + vbase + t * L.VRS + 2 * c);
+        }
+        const int ao = (prow < 0 ? L.zero : pbase + prow * kPRow) + 2 * (32 * ks + 8 * kq);
+        const v8h av = *reinterpret_cast<const v8h*>(lds + ao);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+      }
+      // lane (channel c, rows 4 kq + i): head 8 hb8 + 2 kq + i / 2, part i % 2
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int ho = 8 * hb8 + 2 * kq + jj;
+        if (ho < ng) pvo[ho * D + c] = acc[2 * jj] + acc[2 * jj + 1];
+      }
+    }
+  };
+  // accumulators: o = o alpha + this chunk's p.V sums (thread (channel, heads) layout)
+  auto o_update = [&](int pvbase) {
+    const float* pvo = reinterpret_cast<const float*>(lds + pvbase);
+    const int c_pv = tid % D, hb = tid / D;
+#pragma unroll
+    for (int k = 0; k < VC::NO; ++k) {
+      const int hh = hb + k * VC::HS;
+      if (hh < ng) o[k] = __builtin_fmaf(o[k], alph[hh], pvo[hh * D + c_pv]);
+    }
+  };
+
+  // fp16 rows (sinks or residual, T <= 128 of them; row t_new from k_new / v_new): wave wv takes
+  // tokens 32 wv .. 32 wv + 31.  q.K on v_mfma_f32_16x16x32_f16 straight from the key rows (A:
+  // 16 tokens x 32 channels a step) and the fp16 queries (B: head = column; products exact in
+  // fp32), the value rows staged in LDS for pv_fp16.  Tokens past T read row T - 1 and weigh
+  // p = 0.
+  constexpr int KS16 = D / 32;
+  auto rows_chunk = [&](int T, const uint16_t* krows, const uint16_t* vrows, int t_new) {
+    v4u qb[KS16];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)b * a.H_q + (int64_t)h * ng + (n < ng ? n : 0)) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS16; ++ks)
+        qb[ks] = n < ng ? *reinterpret_cast<const v4u*>(qrow + 32 * ks + 8 * kq) : v4u{0, 0, 0, 0};
+    }
+    const int t0 = 32 * wv;
+    const uint16_t* knew = a.k_new + bh * D;
+    const uint16_t* vnew = a.v_new + bh * D;
+    v4u ka[2][KS16];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = min(t0 + 16 * tt + n, T - 1);
+      const uint16_t* kr = t == t_new ? knew : krows + (int64_t)t * D;
+#pragma unroll
+      for (int ks = 0; ks < KS16; ++ks) ka[tt][ks] = *reinterpret_cast<const v4u*>(kr + 32 * ks + 8 * kq);
+    }
+    // value rows t0 .. t0 + 31: 16-byte piece u = lane + 64 j is row u / (D / 8), piece u % (D / 8)
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      const int u = lane + 64 * j, r = u / (D / 8), qd = u % (D / 8);
+      const int t = min(t0 + r, T - 1);
+      const v4u x = *reinterpret_cast<const v4u*>((t == t_new ? vnew : vrows + (int64_t)t * D) + 8 * qd);
+      uint2* dst = reinterpret_cast<uint2*>(lds + L.vr + (t0 + r) * L.VRS + 16 * qd);
+      dst[0] = make_uint2(x[0], x[1]);
+      dst[1] = make_uint2(x[2], x[3]);
+    }
+    // logits: lane (head n, tokens t0 + 16 tt + 4 kq + i)
+    float lv[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      v4f st = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS16; ++ks)
+        st = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, ka[tt][ks]),
+                                                    __builtin_bit_cast(v8h, qb[ks]), st, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lv[tt][i] = t0 + 16 * tt + 4 * kq + i < T ? st[i] * a.qscale : -INFINITY;
+        mx = fmaxf(mx, lv[tt][i]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool ok = n < ng;
+    if (kq == 0 && ok) wmax[16 * wv + n] = mx;
+    __syncthreads();
+    {
+      const float mp = fmaxf(fmaxf(wmax[n], wmax[16 + n]), fmaxf(wmax[32 + n], wmax[48 + n]));
+      const float mo = m_run[n];
+      // finite: token 0 of wave 0 is a row (T >= 1); waves past T hold -inf
+      const float mn = fmaxf(mo, mp);
+      const float al = mo == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+      if (wv == 0 && kq == 0 && ok) {
+        mnew[n] = mn;
+        shf[n] = 1.0f;
+        alph[n] = al;
+      }
+      float ls = 0.0f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        uint32_t hi[2], lo[2];
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(lv[tt][i] - mn);
+          const float p1 = __builtin_amdgcn_exp2f(lv[tt][i + 1] - mn);
+          ls += p0 + p1;
+          const uint16_t h0 = f2h(p0), h1 = f2h(p1);
+          hi[i / 2] = (uint32_t)h0 | (uint32_t)h1 << 16;
+          lo[i / 2] = (uint32_t)f2h(p0 - h2f(h0)) | (uint32_t)f2h(p1 - h2f(h1)) << 16;
+        }
+        if (ok) {
+          const int t = t0 + 16 * tt + 4 * kq;
+          *reinterpret_cast<uint2*>(lds + L.p16 + 2 * n * kPRow + 2 * t) = make_uint2(hi[0], hi[1]);
+          *reinterpret_cast<uint2*>(lds + L.p16 + (2 * n + 1) * kPRow + 2 * t) = make_uint2(lo[0], lo[1]);
+        }
+      }
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      if (kq == 0 && ok) wl[16 * wv + n] = ls;
+    }
+    __syncthreads();
+    if (tid < ng) {
+      m_run[tid] = mnew[tid];
+      const float ls = (wl[tid] + wl[16 + tid]) + (wl[32 + tid] + wl[48 + tid]);
+      l_run[tid] = __builtin_fmaf(l_run[tid], alph[tid], ls);
+    }
+    pv_fp16(L.vr, L.p16, L.pv16);
+    __syncthreads();
+    o_update(L.pv16);
+    __syncthreads();  // the chunk's LDS is reused by what follows
+  };
 
   // ---- sink rows (chunk 0)
   if (split == 0 && sv.sink_len > 0)
-    vc.run(0, sv.sink_len, a.k_sink + bh * a.N_s * D, a.v_sink + bh * a.N_s * D,
-           sv.new_kind == 0 ? sv.new_row : -1, nullptr, nullptr, nullptr, nullptr, o);
+    rows_chunk(sv.sink_len, a.k_sink + bh * a.N_s * D, a.v_sink + bh * a.N_s * D,
+               sv.new_kind == 0 ? sv.new_row : -1);
 
   // ---- pages (chunks 1 .. n_pages)
   const int S = a.splits;
@@ -607,9 +756,23 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
 
     issue(pg);
     put(0);
-    __syncthreads();
+    // T columns of this thread (fixed for the call): the 4-column unit tc4 = tid % CW4 of the
+    // rows of heads th0, th0 + ths, ... (ths = 256 / CW4 threads per unit; threads past ths * CW4
+    // build none), in every token group; tchan = the unit's four channels (0xFF: none).
     const int CW4 = 16 * L.KS;  // 4-column units of a T row
-    const int e8 = BV16 ? 1 : 8 / bV;
+    const int tc4 = tid % CW4, ths = kGThreads / CW4, th0 = tid / CW4;
+    const bool thi = 4 * tc4 >= 64 * L.KSL;  // an upper-plane unit (factor 2^b_L)
+    uint32_t tchan = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int col = 4 * tc4 + e, r = col - 64 * L.KSL;
+      const int c = !thi ? (col < D ? col : -1) : (r < n_sal ? crank[r] : -1);
+      tchan |= (uint32_t)(c < 0 ? 0xFF : c) << (8 * e);
+    }
+    __syncthreads();
+    const int lgG = __builtin_ctz((uint32_t)a.G);
+    const int lgE = BV16 ? 0 : 3 - __builtin_ctz((uint32_t)bV);  // log2 of codes per value byte
+    const int lgGV = __builtin_ctz((uint32_t)a.g_V);
     const uint32_t vmask = BV16 ? 0u : ((1u << bV) - 1u) * 0x01010101u;
     for (int it = 0; pg < sv.n_pages; pg += S, ++it) {
       const int par = it & 1;
@@ -619,59 +782,59 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
       if (tid == 4) smaxv[par ^ 1] = 0u;
 
       // ---- P1: digit table T [group][head, digit][column] and the key offsets' sums
-      const int nT = KG * ng * CW4;
-      for (int u = tid; u < nT; u += kGThreads) {
-        const int c4 = u % CW4, gh = u / CW4, hh = gh % ng, g = gh / ng;
-        const float sc = p2i(sigma(par, g));
-        uint32_t wd[4];
+      if (th0 < ths) {
+        for (int g = 0; g < KG; ++g) {
+          const float sc = p2i(sigma(par, g)) * (thi ? hiw : 1.0f);
+          float svs[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int col = 4 * c4 + e;
-          int c;
-          float mul = sc;
-          if (col < 64 * L.KSL) {
-            c = col < D ? col : -1;
-          } else {
-            const int r = col - 64 * L.KSL;
-            c = r < n_sal ? crank[r] : -1;
-            mul = sc * hiw;
+          for (int e = 0; e < 4; ++e) {
+            const int c = (tchan >> (8 * e)) & 0xFF;
+            svs[e] = c != 0xFF ? f16_at(lds + L.kb + L.kOffS + 2 * (g * D + c)) : 0.0f;
           }
-          const float qv = c >= 0 ? qs[hh * D + c] * mul : 0.0f;
-          const float sv_ = c >= 0 ? f16_at(lds + L.kb + L.kOffS + 2 * (g * D + c)) : 0.0f;
-          // balanced digits of x (|x| < 2^30): byte d, read as int8, is digit d
-          const int x = (int)__builtin_rintf(qv * sv_);
-          wd[e] = ((uint32_t)x + 0x80808080u) ^ 0x80808080u;
+          for (int hh = th0; hh < ng; hh += ths) {
+            uint32_t wd[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int c = (tchan >> (8 * e)) & 0xFF;
+              const float qv = c != 0xFF ? qs[hh * D + c] * sc : 0.0f;
+              // balanced digits of x (|x| < 2^30): byte d, read as int8, is digit d
+              const int x = (int)__builtin_rintf(qv * svs[e]);
+              wd[e] = ((uint32_t)x + 0x80808080u) ^ 0x80808080u;
+            }
+            // digit d of the four columns -> one dword of row (head, d)
+            const uint32_t t01 = __builtin_amdgcn_perm(wd[1], wd[0], 0x05010400u);
+            const uint32_t t23 = __builtin_amdgcn_perm(wd[3], wd[2], 0x05010400u);
+            const uint32_t u01 = __builtin_amdgcn_perm(wd[1], wd[0], 0x07030602u);
+            const uint32_t u23 = __builtin_amdgcn_perm(wd[3], wd[2], 0x07030602u);
+            uint8_t* tr = lds + L.u + (g * 4 * ng + 4 * hh) * L.TLB + 4 * tc4;
+            *reinterpret_cast<uint32_t*>(tr) = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+            *reinterpret_cast<uint32_t*>(tr + L.TLB) = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
+            *reinterpret_cast<uint32_t*>(tr + 2 * L.TLB) = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
+            *reinterpret_cast<uint32_t*>(tr + 3 * L.TLB) = __builtin_amdgcn_perm(u23, u01, 0x07060302u);
+          }
         }
-        // digit d of the four columns -> one dword of row (head, d)
-        const uint32_t t01 = __builtin_amdgcn_perm(wd[1], wd[0], 0x05010400u);
-        const uint32_t t23 = __builtin_amdgcn_perm(wd[3], wd[2], 0x05010400u);
-        const uint32_t u01 = __builtin_amdgcn_perm(wd[1], wd[0], 0x07030602u);
-        const uint32_t u23 = __builtin_amdgcn_perm(wd[3], wd[2], 0x07030602u);
-        uint8_t* tr = lds + L.u + (g * 4 * ng + 4 * hh) * L.TLB + 4 * c4;
-        *reinterpret_cast<uint32_t*>(tr) = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-        *reinterpret_cast<uint32_t*>(tr + L.TLB) = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
-        *reinterpret_cast<uint32_t*>(tr + 2 * L.TLB) = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
-        *reinterpret_cast<uint32_t*>(tr + 3 * L.TLB) = __builtin_amdgcn_perm(u23, u01, 0x07060302u);
       }
       {
-        constexpr int SL = D / 16;  // channels per lane; 16 lanes per (group, head)
-        const int nZ = KG * ng * 16;
-        for (int u = tid; u < nZ; u += kGThreads) {  // whole 16-lane rows
-          const int gh = u >> 4, s = u & 15, hh = gh % ng, g = gh / ng;
-          float acc = 0.0f;
+        // sum_c qt Z of head tid / 16 (a 16-lane row; D / 16 channels a lane) and every group
+        constexpr int SL = D / 16;
+        const int hh = tid >> 4;
+        if (hh < ng) {  // uniform over the row
+          for (int g = 0; g < KG; ++g) {
+            float acc = 0.0f;
 #pragma unroll
-          for (int e = 0; e < SL; ++e) {
-            const int c = SL * s + e;
-            acc = __builtin_fmaf(qs[hh * D + c], f16_at(lds + L.kb + L.kOffZ + 2 * (g * D + c)), acc);
+            for (int e = 0; e < SL; ++e) {
+              const int c = SL * n + e;
+              acc = __builtin_fmaf(qs[hh * D + c], f16_at(lds + L.kb + L.kOffZ + 2 * (g * D + c)), acc);
+            }
+            acc = rsum16(acc);
+            if (n == 0) zk[16 * g + hh] = acc;
           }
-          acc = rsum16(acc);
-          if (s == 0) zk[16 * g + hh] = acc;
         }
       }
       __syncthreads();
 
       // ---- P2: logits of this wave's 32 tokens (one token group: 32 divides G)
-      const int g2 = (32 * wv) / a.G;
+      const int g2 = (32 * wv) >> lgG;
       const float inv2 = p2i(-sigma(par, g2));
       float lgv[2][NHB];
 #pragma unroll
@@ -782,12 +945,11 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
         const float ls = (wl[tid] + wl[16 + tid]) + (wl[32 + tid] + wl[48 + tid]);
         l_run[tid] = __builtin_fmaf(l_run[tid], alph[tid], ls * shf[tid]);
       }
-      constexpr int NCT = D / 16;
       if constexpr (!BV16) {
         for (int job = wv; job < NCT * NHB; job += 4) {
           const int ct = job % NCT, hb = job / NCT;
-          const int c = 16 * ct + n, g = (16 * ct) / a.g_V;
-          const int mcol = c / e8, fs = bV * (c % e8);
+          const int c = 16 * ct + n, g = (16 * ct) >> lgGV;
+          const int mcol = c >> lgE, fs = bV * (c & ((1 << lgE) - 1));
           const int hh = 4 * hb + (n >> 2), dg = n & 3;
           const int row = (dg == 3 || hh >= ng) ? -1 : g * 3 * ng + 3 * hh + dg;
           v4i acc = v4i{0, 0, 0, 0};
@@ -810,44 +972,12 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
           }
         }
       } else {
-        constexpr int NH8 = (NG + 7) / 8;
-        for (int job = wv; job < NCT * NH8; job += 4) {
-          const int ct = job % NCT, hb8 = job / NCT;
-          const int c = 16 * ct + n;
-          const int hh = 8 * hb8 + (n >> 1), part = n & 1;
-          const int prow = hh < ng ? 2 * hh + part : -1;
-          v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            v8h bv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int t = 32 * ks + 8 * kq + e;
-              bv[e] = *reinterpret_cast<const _Float16*>(lds + L.vb + t * L.VRS + 2 * c);
-            }
-            const int ao = (prow < 0 ? L.zero : L.u + prow * kPRow) + 2 * (32 * ks + 8 * kq);
-            const v8h av = *reinterpret_cast<const v8h*>(lds + ao);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
-          }
-          // lane (channel c, rows 4 kq + i): head 8 hb8 + 2 kq + i / 2, part i % 2
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int ho = 8 * hb8 + 2 * kq + jj;
-            if (ho < ng) pvb[ho * D + c] = acc[2 * jj] + acc[2 * jj + 1];
-          }
-        }
+        pv_fp16(L.vb, L.u, L.pv);
       }
       __syncthreads();
 
       // ---- P5: accumulators; the next page into LDS
-      {
-        const int c_pv = tid % D, hb = tid / D;
-#pragma unroll
-        for (int k = 0; k < VC::NO; ++k) {
-          const int hh = hb + k * VC::HS;
-          if (hh < ng) o[k] = __builtin_fmaf(o[k], alph[hh], pvb[hh * D + c_pv]);
-        }
-      }
+      o_update(L.pv);
       if (nx < sv.n_pages) put(par ^ 1);
       __syncthreads();
     }
@@ -855,8 +985,8 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
 
   // ---- residual rows (chunk n_pages + 1)
   if ((sv.n_pages + 1) % S == split && sv.res_len > 0)
-    vc.run(2, sv.res_len, a.k_res + bh * kN * D, a.v_res + bh * kN * D,
-           sv.new_kind == 1 ? sv.new_row : -1, nullptr, nullptr, nullptr, nullptr, o);
+    rows_chunk(sv.res_len, a.k_res + bh * kN * D, a.v_res + bh * kN * D,
+               sv.new_kind == 1 ? sv.new_row : -1);
 
   write_partial<D, NG>(a, bh, split, o, m_run, l_run);
 }

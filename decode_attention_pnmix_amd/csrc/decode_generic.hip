@@ -446,6 +446,22 @@ __device__ __forceinline__ grsrc_t g_rsrc(const void* base, int64_t bytes) {
 __device__ __forceinline__ v4u g_load16(grsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// maximum over the wave (every lane active): within 16-lane rows by DPP, then across the rows
+template <int CTRL>
+__device__ __forceinline__ uint32_t udpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, udpp<0xB1>(x));
+  x = max(x, udpp<0x4E>(x));
+  x = max(x, udpp<0x124>(x));
+  x = max(x, udpp<0x128>(x));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
 // largest |x| of eight fp16 as its bit pattern (magnitudes order like their bits)
 __device__ __forceinline__ uint32_t hmax8(const v4u& w) {
   uint32_t m = 0;
@@ -719,14 +735,22 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
       for (int j = 0; j < VC16; ++j) rv[j] = g_load16(vr, 16u * (uint32_t)(tid + kGThreads * j));
     };
     // Loaded page to LDS, with the largest key S per token group and the largest value S
+    // (Largest scales: one LDS atomic per wave and group, from a wave reduction; atomics of many
+    // lanes on one address serialise.)
     auto put = [&](int par) {
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         const int off = 16 * (tid + kGThreads * j);
-        if (off < a.kpb) {
-          *reinterpret_cast<v4u*>(lds + L.kb + off) = rk[j];
-          if (off >= L.kOffS && off < L.kOffZ)
-            atomicMax(&smaxk[4 * par + (off - L.kOffS) / (2 * D)], hmax8(rk[j]));
+        if (off < a.kpb) *reinterpret_cast<v4u*>(lds + L.kb + off) = rk[j];
+        const int w0 = 16 * (64 * wv + kGThreads * j);  // this wave's bytes [w0, w0 + 1024)
+        if (w0 < L.kOffZ && w0 + 1024 > L.kOffS) {     // uniform
+          for (int g = 0; g < KG; ++g) {
+            const int g0 = L.kOffS + 2 * D * g;
+            if (w0 < g0 + 2 * D && w0 + 1024 > g0) {
+              const uint32_t m = wave_max_u32(off >= g0 && off < g0 + 2 * D ? hmax8(rk[j]) : 0u);
+              if (lane == 0) atomicMax(&smaxk[4 * par + g], m);
+            }
+          }
         }
       }
 #pragma unroll
@@ -740,7 +764,13 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
             dst[1] = make_uint2(rv[j][2], rv[j][3]);
           } else {
             *reinterpret_cast<v4u*>(lds + L.vb + off) = rv[j];
-            if (off >= L.vOffS && off < L.vOffZ) atomicMax(&smaxv[par], hmax8(rv[j]));
+          }
+        }
+        if constexpr (!BV16) {
+          const int w0 = 16 * (64 * wv + kGThreads * j);
+          if (w0 < L.vOffZ && w0 + 1024 > L.vOffS) {  // uniform
+            const uint32_t m = wave_max_u32(off >= L.vOffS && off < L.vOffZ ? hmax8(rv[j]) : 0u);
+            if (lane == 0) atomicMax(&smaxv[par], m);
           }
         }
       }
@@ -875,6 +905,10 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
       __syncthreads();
 
       // ---- P3: softmax of the page; p.V tables (W digits or P halves) and this wave's sums
+      // byte selectors of the quad transpose: [x.b0, y.b0, x.b2, y.b2] (even lanes) or
+      // [y.b1, x.b1, y.b3, x.b3] (odd), y the neighbour's word; then the same over lane pairs
+      const uint32_t qsel1 = (n & 1) ? 0x03070105u : 0x06020400u;
+      const uint32_t qsel2 = (n & 2) ? 0x03020706u : 0x05040100u;
       const float smv = BV16 ? 0.0f : h2f((uint16_t)smaxv[par]);
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) {
@@ -916,12 +950,13 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
               const float sg = f16_at(lds + L.vb + L.vOffS + 2 * (g * kN + t));
               const float zg = f16_at(lds + L.vb + L.vOffZ + 2 * (g * kN + t));
               const uint32_t xb = fbits(__builtin_fmaf(pw, sg, kTwo23b)) ^ 0x8080u;
-              if (ok) {
-                uint8_t* wr = lds + L.u + (g * 3 * ng + 3 * hh) * kWRow + t;
-                wr[0] = (uint8_t)xb;
-                wr[kWRow] = (uint8_t)(xb >> 8);
-                wr[2 * kWRow] = (uint8_t)(xb >> 16);
-              }
+              // 4 x 4 byte transpose in the lane quad (tokens 4q .. 4q + 3): lane i gets digit i
+              // of the four tokens, one dword of row (head, digit i)
+              const uint32_t s1 = __builtin_amdgcn_perm(udpp<0xB1>(xb), xb, qsel1);
+              const uint32_t dw = __builtin_amdgcn_perm(udpp<0x4E>(s1), s1, qsel2);
+              if (ok && (n & 3) < 3)
+                *reinterpret_cast<uint32_t*>(lds + L.u + (g * 3 * ng + 3 * hh + (n & 3)) * kWRow +
+                                             (t & ~3)) = dw;
               zs[g] = __builtin_fmaf(pw, zg, zs[g]);
             }
           }

@@ -845,9 +845,10 @@ __global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArg
         }
       }
       {
-        // sum_c qt Z of head tid / 16 (a 16-lane row; D / 16 channels a lane) and every group
+        // sum_c qt Z of head 15 - tid / 16 (a 16-lane row; D / 16 channels a lane) and every
+        // group: the last waves, which build the fewest T rows
         constexpr int SL = D / 16;
-        const int hh = tid >> 4;
+        const int hh = 15 - (tid >> 4);
         if (hh < ng) {  // uniform over the row
           for (int g = 0; g < KG; ++g) {
             float acc = 0.0f;

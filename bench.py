@@ -599,8 +599,10 @@ def main():
     tkv, tk, tv = (float(np.median(x)) for x in (qkv_t, qk_t, qv_t))
     kbytes = n_jobs * (w.N * w.d * 2 + kpb)
     vbytes = n_jobs * (w.N * w.d * 2 + vpb)
-    quant = {"pages_per_launch": 2 * n_jobs, "kernel": "quantize_kv_kernel (K and V pages in one "
-             "launch)", "kv_us": tkv * 1e6, "kv_us_p10": float(np.percentile(qkv_t, 10)) * 1e6,
+    qkern = ("quantize_kv_kernel" if (w.b_H, w.b_L, w.b_V) == (3, 1, 2)
+             else "quantize_kv_generic_kernel")
+    quant = {"pages_per_launch": 2 * n_jobs, "kernel": f"{qkern} (K and V pages in one launch)",
+             "kv_us": tkv * 1e6, "kv_us_p10": float(np.percentile(qkv_t, 10)) * 1e6,
              "kv_us_p90": float(np.percentile(qkv_t, 90)) * 1e6,
              "kv_GBps": (kbytes + vbytes) / tkv / 1e9,
              "kv_frac_of_peak": (kbytes + vbytes) / tkv / 1e9 / HBM_PEAK_GBS,

@@ -65,46 +65,83 @@ __global__ void __launch_bounds__(2 * D) quantize_kv_kernel(const pnmix_page* __
 
 // ---------------------------------------------------------------------------------------------
 // Every other bit width: (b_H, b_L) with 1 <= b_L <= b_H <= 4 and b_V in {1, 2, 4, 16} (the
-// bit-width sweep of the PN-Mix paper's Table 14 / Figure 3).  Same arithmetic per group and
-// element as above (exact min / max, group_meta, code_bits), so codes and metadata are again
-// bit-identical to the reference; the layout generalises the appendix's planes: the low b_L
-// bits of every key channel in a plane of width b_L, the upper b_H - b_L bits of the salient
-// channels in a plane of that width (plane_field in common.h describes a plane), and 8 / b_V
-// consecutive channels of one token per value byte.  One workgroup of 256 threads per page, the
-// page staged in LDS; these kernels favour plainness over speed.
+// bit-width sweep of the PN-Mix paper's Table 14 / Figure 3).  The same register tiles, steps
+// and per-element arithmetic as above (exact min / max, group_meta, code_bits_h), so codes and
+// metadata are again bit-identical to the reference; the layout generalises the appendix's
+// planes: the low b_L bits of every key channel in a plane of width b_L, the upper b_H - b_L bits
+// of the salient channels in a plane of that width (a plane stores the w-bit fields of tokens
+// 8j .. 8j + 7 of a column as one 8w-bit little-endian stream in w bytes; plane_field in common.h),
+// and 8 / b_V consecutive channels of one token per value byte.
 
+// byte i of each of four words -> one word (w0's in byte 0)
+__device__ __forceinline__ uint32_t gather_bi(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                              int i) {
+  const uint32_t sel = 0x0c0c0000u | (uint32_t)(4 + i) << 8 | (uint32_t)i;  // [w0.bi, w1.bi, 0, 0]
+  return perm(perm(w3, w2, sel), perm(w1, w0, sel), 0x05040100u);
+}
+
+// LDS of one key page, any widths: (min, max) per octet and channel, (min, 1/s) per group and
+// channel, the upper plane (at most 3 bits: N / 8 octets x 3 bytes x d ranks), salient ranks.
+template <int D>
+struct KWLds {
+  static constexpr int part = 0;
+  static constexpr int meta = part + kOctets * D * 4;
+  static constexpr int hi = meta + (kN / 32) * D * 8;
+  static constexpr int rank = hi + kOctets * 3 * D;
+  static constexpr int bytes = rank + D;
+};
 
 template <int D>
-__global__ void __launch_bounds__(256) quantize_k_generic_kernel(
-    const pnmix_page* __restrict__ jobs, const uint32_t* __restrict__ mask, int pairing, int n_hi,
-    int G, int words, int bH, int bL) {
-  __shared__ __align__(16) uint16_t xs[kN * D];
-  __shared__ __align__(16) uint8_t q[kN * D];
-  __shared__ float2 meta[(kN / 32) * D];
-  __shared__ int rank_s[D];
-  __shared__ int chan_s[D];
-  const int tid = threadIdx.x;
-  const pnmix_page job = jobs[blockIdx.x];
-  const int n_sal = 2 * n_hi, wH = bH - bL, KG = kN / G;
+__device__ __forceinline__ void quantize_k_page_w(const pnmix_page& job,
+                                                  const uint32_t* __restrict__ mask, int pairing,
+                                                  int n_hi, int G, int words, int bH, int bL,
+                                                  uint8_t* lds) {
+  constexpr int NB = D / 8;
+  uint32_t* part = reinterpret_cast<uint32_t*>(lds + KWLds<D>::part);
+  float2* meta = reinterpret_cast<float2*>(lds + KWLds<D>::meta);
+  uint8_t* hi_s = lds + KWLds<D>::hi;
+  int8_t* rank_s = reinterpret_cast<int8_t*>(lds + KWLds<D>::rank);
+  const int tid = threadIdx.x, b = tid % NB, k = tid / NB;
+  const int n_sal = 2 * n_hi, wH = bH - bL;
   uint8_t* lo = job.dst;
   uint8_t* hi = lo + kN * D * bL / 8;
   uint16_t* S = reinterpret_cast<uint16_t*>(hi + kN * n_sal * wH / 8);
-  uint16_t* Z = S + KG * D;
-  stage_page<D>(xs, job.src, job.src_row_stride);
-  const uint32_t* mrow = mask + job.mask_row * words;
-  for (int c = tid; c < D; c += 256) {
-    const int r = salient_rank(mrow, c, D, pairing, n_hi);
-    rank_s[c] = r;
-    if (r >= 0) chan_s[r] = c;
+  uint16_t* Z = S + (kN / G) * D;
+
+  uint4 x[8];
+  load_block(x, job.src, job.src_row_stride, k, b);
+
+  // A: per channel min / max over the 8 tokens
+  {
+    uint32_t pm[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t mn = word(x[0], m), mx = mn;
+#pragma unroll
+      for (int j = 1; j < 8; ++j) {
+        mn = pk_min(mn, word(x[j], m));
+        mx = pk_max(mx, word(x[j], m));
+      }
+      pm[2 * m] = perm(mx, mn, 0x05040100u);
+      pm[2 * m + 1] = perm(mx, mn, 0x07060302u);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(part + k * D + 8 * b);
+    dst[0] = make_uint4(pm[0], pm[1], pm[2], pm[3]);
+    dst[1] = make_uint4(pm[4], pm[5], pm[6], pm[7]);
   }
+  const uint32_t* mrow = mask + job.mask_row * words;
+  if (tid < D) rank_s[tid] = (int8_t)salient_rank(mrow, tid, D, pairing, n_hi);
   __syncthreads();
-  for (int it = tid; it < KG * D; it += 256) {
+
+  // B: one thread per (token group, channel)
+  const int og = G / 8;
+  for (int it = tid; it < (kN / G) * D; it += 2 * D) {
     const int g = it / D, c = it % D;
-    float mn = h2f(xs[(g * G) * D + c]), mx = mn;
-    for (int t = g * G + 1; t < (g + 1) * G; ++t) {
-      const float v = h2f(xs[t * D + c]);
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
+    float mn = lo_f(part[g * og * D + c]), mx = hi_f(part[g * og * D + c]);
+    for (int o = 1; o < og; ++o) {
+      const uint32_t v = part[(g * og + o) * D + c];
+      mn = fminf(mn, lo_f(v));
+      mx = fmaxf(mx, hi_f(v));
     }
     const int L = (1 << (rank_s[c] >= 0 ? bH : bL)) - 1;
     uint16_t s, z;
@@ -113,56 +150,91 @@ __global__ void __launch_bounds__(256) quantize_k_generic_kernel(
     Z[g * D + c] = z;
   }
   __syncthreads();
-  for (int i = tid; i < kN * D; i += 256) {
-    const int t = i / D, c = i % D;
-    const float2 m = meta[(t / G) * D + c];
-    const float L = (float)((1 << (rank_s[c] >= 0 ? bH : bL)) - 1);
-    q[i] = (uint8_t)(code_bits(h2f(xs[i]), m.x, m.y, L) & 0xFFu);
+
+  // C: codes of the thread's 8 channels x 8 tokens, as the bit streams of the two planes
+  const int g = k / og;
+  const uint32_t mL = (1u << bL) - 1u;
+  uint32_t lob[8];  // channel s: the 8 b_L-bit fields of the octet, token j at bit b_L j
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const float2 mt = meta[g * D + 8 * b + s];
+    const int rk = rank_s[8 * b + s];
+    const float L = (float)((1 << (rk >= 0 ? bH : bL)) - 1);
+    uint32_t sl = 0, sh = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t q = code_bits_h(word(x[j], s >> 1), (s & 1) != 0, -mt.x, mt.y, L) & 15u;
+      sl |= (q & mL) << (bL * j);
+      sh |= (q >> bL) << (wH * j);
+    }
+    lob[s] = sl;
+    if (wH > 0 && rk >= 0)
+      for (int i = 0; i < wH; ++i) hi_s[(k * wH + i) * n_sal + rk] = (uint8_t)(sh >> (8 * i));
+  }
+  for (int i = 0; i < bL; ++i) {
+    const uint32_t w0 = gather_bi(lob[0], lob[1], lob[2], lob[3], i);
+    const uint32_t w1 = gather_bi(lob[4], lob[5], lob[6], lob[7], i);
+    *reinterpret_cast<uint2*>(lo + (k * bL + i) * D + 8 * b) = make_uint2(w0, w1);
   }
   __syncthreads();
-  // low plane: unit (octet j, channel c) -> its b_L bytes
-  for (int i = tid; i < (kN / 8) * D; i += 256) {
-    const int j = i / D, c = i % D;
-    uint32_t s = 0;
-    for (int k = 0; k < 8; ++k) s |= ((uint32_t)q[(8 * j + k) * D + c] & ((1u << bL) - 1u)) << (bL * k);
-    for (int b = 0; b < bL; ++b) lo[(j * bL + b) * D + c] = (uint8_t)(s >> (8 * b));
+  if (wH > 0) {
+    const int hi_chunks = kOctets * wH * n_sal / 16;  // 16 w_H n_sal bytes
+    for (int i = tid; i < hi_chunks; i += 2 * D)
+      reinterpret_cast<uint4*>(hi)[i] = reinterpret_cast<const uint4*>(hi_s)[i];
   }
-  // high plane: unit (octet j, salient rank r) -> its b_H - b_L bytes
-  if (wH > 0)
-    for (int i = tid; i < (kN / 8) * n_sal; i += 256) {
-      const int j = i / n_sal, r = i % n_sal, c = chan_s[r];
-      uint32_t s = 0;
-      for (int k = 0; k < 8; ++k) s |= ((uint32_t)q[(8 * j + k) * D + c] >> bL) << (wH * k);
-      for (int b = 0; b < wH; ++b) hi[(j * wH + b) * n_sal + r] = (uint8_t)(s >> (8 * b));
-    }
 }
 
+// LDS of one value page, any widths: (min, max) per token and 8-channel block, (min, 1/s) per
+// token and group (<= 4)
 template <int D>
-__global__ void __launch_bounds__(256) quantize_v_generic_kernel(const pnmix_page* __restrict__ jobs,
-                                                                 int g_V, int bV) {
-  __shared__ __align__(16) uint16_t xs[kN * D];
-  __shared__ float2 meta[kN * 4];
-  const int tid = threadIdx.x;
-  const pnmix_page job = jobs[blockIdx.x];
-  if (bV == 16) {  // values kept in fp16: the page is the rows [N][D]
-    uint16_t* dst = reinterpret_cast<uint16_t*>(job.dst);
-    for (int i = tid; i < kN * D; i += 256) dst[i] = job.src[(int64_t)(i / D) * job.src_row_stride + i % D];
+struct VWLds {
+  static constexpr int part = 0;
+  static constexpr int meta = part + kN * (D / 8) * 4;
+  static constexpr int bytes = meta + kN * 4 * 8;
+};
+
+template <int D, int BV>
+__device__ __forceinline__ void quantize_v_page_w(const pnmix_page& job, int g_V, uint8_t* lds) {
+  constexpr int NB = D / 8;
+  const int tid = threadIdx.x, b = tid % NB, k = tid / NB;
+  uint4 x[8];
+  load_block(x, job.src, job.src_row_stride, k, b);
+  if constexpr (BV == 16) {  // values kept in fp16: the page is the rows [N][D]
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4*>(job.dst + 2 * ((8 * k + j) * D + 8 * b)) = x[j];
     return;
   }
-  const int ng = D / g_V, e = 8 / bV;
+  constexpr int bV = BV == 16 ? 8 : BV, e = 8 / bV;  // code bits; codes per byte
+  uint32_t* part = reinterpret_cast<uint32_t*>(lds + VWLds<D>::part);
+  float2* meta = reinterpret_cast<float2*>(lds + VWLds<D>::meta);
+  const int ng = D / g_V;
   uint8_t* codes = job.dst;
   uint16_t* S = reinterpret_cast<uint16_t*>(codes + kN * D * bV / 8);  // [ng][N]
   uint16_t* Z = S + kN * ng;
-  stage_page<D>(xs, job.src, job.src_row_stride);
+
+  // A: per token min / max over the thread's 8 channels
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t mn2 = pk_min(pk_min(x[j].x, x[j].y), pk_min(x[j].z, x[j].w));
+    const uint32_t mx2 = pk_max(pk_max(x[j].x, x[j].y), pk_max(x[j].z, x[j].w));
+    const _Float16 mn = __builtin_elementwise_min(as_h2(mn2).x, as_h2(mn2).y);
+    const _Float16 mx = __builtin_elementwise_max(as_h2(mx2).x, as_h2(mx2).y);
+    part[(8 * k + j) * NB + b] = (uint32_t)__builtin_bit_cast(uint16_t, mn) |
+                                 ((uint32_t)__builtin_bit_cast(uint16_t, mx) << 16);
+  }
   __syncthreads();
+
+  // B: one thread per (token, channel group)
+  const int bg = g_V / 8;
   const int L = (1 << bV) - 1;
-  for (int it = tid; it < kN * ng; it += 256) {
+  for (int it = tid; it < kN * ng; it += 2 * D) {
     const int t = it % kN, gi = it / kN;
-    float mn = h2f(xs[t * D + gi * g_V]), mx = mn;
-    for (int c = gi * g_V + 1; c < (gi + 1) * g_V; ++c) {
-      const float v = h2f(xs[t * D + c]);
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
+    const uint32_t* pr = part + t * NB + gi * bg;
+    float mn = lo_f(pr[0]), mx = hi_f(pr[0]);
+    for (int o = 1; o < bg; ++o) {
+      mn = fminf(mn, lo_f(pr[o]));
+      mx = fmaxf(mx, hi_f(pr[o]));
     }
     uint16_t s, z;
     meta[t * 4 + gi] = group_meta(mn, mx, L, s, z);
@@ -170,17 +242,63 @@ __global__ void __launch_bounds__(256) quantize_v_generic_kernel(const pnmix_pag
     Z[gi * kN + t] = z;
   }
   __syncthreads();
-  // byte [m][t]: channels e m .. e m + e - 1 of token t
-  for (int i = tid; i < (D / e) * kN; i += 256) {
-    const int m = i / kN, t = i % kN;
-    uint32_t byte = 0;
-    for (int u = 0; u < e; ++u) {
-      const int c = e * m + u;
-      const float2 mt = meta[t * 4 + c / g_V];
-      byte |= (code_bits(h2f(xs[t * D + c]), mt.x, mt.y, (float)L) & 0xFFu) << (bV * u);
+
+  // C: codes of the thread's 8 tokens x 8 channels: channels 8b .. 8b + 7 are the b_V byte
+  // columns 8b / e .. 8b / e + b_V - 1 of each token.  A code is the low byte of its float
+  // 2^23 + q, so the sum of the codes shifted to their fields has the byte in its low 8 bits.
+  const int gi = b / bg;
+  const float Lf = (float)L;
+  static_assert(BV == 1 || BV == 2 || BV == 4 || BV == 16, "value width");
+  uint32_t by[bV][8];  // [byte column 8b / e + h][token]
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float2 mt = meta[(8 * k + t) * 4 + gi];
+    uint32_t cu[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cu[i] = code_bits_h(word(x[t], i >> 1), (i & 1) != 0, -mt.x, mt.y, Lf);
+#pragma unroll
+    for (int h = 0; h < bV; ++h) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int u = 0; u < e; ++u) v += cu[e * h + u] << (bV * u);
+      by[h][t] = v;
     }
-    codes[i] = (uint8_t)byte;
   }
+#pragma unroll
+  for (int h = 0; h < bV; ++h)
+    *reinterpret_cast<uint2*>(codes + (8 * b / e + h) * kN + 8 * k) =
+        make_uint2(gather_b0(by[h][0], by[h][1], by[h][2], by[h][3]),
+                   gather_b0(by[h][4], by[h][5], by[h][6], by[h][7]));
+}
+
+template <int D>
+__global__ void __launch_bounds__(2 * D) quantize_k_generic_kernel(
+    const pnmix_page* __restrict__ jobs, const uint32_t* __restrict__ mask, int pairing, int n_hi,
+    int G, int words, int bH, int bL) {
+  __shared__ __align__(16) uint8_t lds[KWLds<D>::bytes];
+  quantize_k_page_w<D>(jobs[blockIdx.x], mask, pairing, n_hi, G, words, bH, bL, lds);
+}
+
+template <int D, int BV>
+__global__ void __launch_bounds__(2 * D) quantize_v_generic_kernel(const pnmix_page* __restrict__ jobs,
+                                                                   int g_V) {
+  __shared__ __align__(16) uint8_t lds[VWLds<D>::bytes];
+  quantize_v_page_w<D, BV>(jobs[blockIdx.x], g_V, lds);
+}
+
+// key and value pages of any widths in one launch (workgroup 2i: key job i, 2i + 1: value job i)
+template <int D, int BV>
+__global__ void __launch_bounds__(2 * D) quantize_kv_generic_kernel(
+    const pnmix_page* __restrict__ kjobs, const pnmix_page* __restrict__ vjobs,
+    const uint32_t* __restrict__ mask, int pairing, int n_hi, int G, int words, int bH, int bL,
+    int g_V) {
+  constexpr int bytes = KWLds<D>::bytes > VWLds<D>::bytes ? KWLds<D>::bytes : VWLds<D>::bytes;
+  __shared__ __align__(16) uint8_t lds[bytes];
+  const int i = blockIdx.x >> 1;
+  if (blockIdx.x & 1)
+    quantize_v_page_w<D, BV>(vjobs[i], g_V, lds);
+  else
+    quantize_k_page_w<D>(kjobs[i], mask, pairing, n_hi, G, words, bH, bL, lds);
 }
 
 // Dequantized pages for analysis: x = S code + Z with the stored fp16 S and Z, one fma in fp32
@@ -238,7 +356,7 @@ hipError_t launch_quantize_k(const pnmix_cfg& c, int n_pages, const pnmix_page* 
     hipLaunchKernelGGL(quantize_k_kernel<DD>, dim3(n_pages), dim3(2 * DD), 0, stream, pages, mask, \
                        c.pairing, c.n_hi_pairs, c.G, words);                                     \
   else                                                                                           \
-    hipLaunchKernelGGL(quantize_k_generic_kernel<DD>, dim3(n_pages), dim3(256), 0, stream, pages, \
+    hipLaunchKernelGGL(quantize_k_generic_kernel<DD>, dim3(n_pages), dim3(2 * DD), 0, stream, pages, \
                        mask, c.pairing, c.n_hi_pairs, c.G, words, c.b_H, c.b_L);
   switch (c.d) {
     case 32: PNMIX_QK(32) break;
@@ -253,30 +371,47 @@ hipError_t launch_quantize_v(const pnmix_cfg& c, int n_pages, const pnmix_page* 
                              hipStream_t stream) {
   if (n_pages == 0) return hipSuccess;
   const bool fast = c.b_V == 2;
+#define PNMIX_QVW(DD, BB) \
+  hipLaunchKernelGGL((quantize_v_generic_kernel<DD, BB>), dim3(n_pages), dim3(2 * DD), 0, stream, pages, c.g_V);
 #define PNMIX_QV(DD)                                                                             \
   if (fast)                                                                                      \
     hipLaunchKernelGGL(quantize_v_kernel<DD>, dim3(n_pages), dim3(2 * DD), 0, stream, pages, c.g_V); \
-  else                                                                                           \
-    hipLaunchKernelGGL(quantize_v_generic_kernel<DD>, dim3(n_pages), dim3(256), 0, stream, pages, \
-                       c.g_V, c.b_V);
+  else if (c.b_V == 1) { PNMIX_QVW(DD, 1) }                                                      \
+  else if (c.b_V == 4) { PNMIX_QVW(DD, 4) }                                                      \
+  else { PNMIX_QVW(DD, 16) }
   switch (c.d) {
     case 32: PNMIX_QV(32) break;
     case 64: PNMIX_QV(64) break;
     default: PNMIX_QV(128) break;
   }
 #undef PNMIX_QV
+#undef PNMIX_QVW
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_kv(const pnmix_cfg& c, int n_pages, const pnmix_page* kjobs,
                               const pnmix_page* vjobs, const uint32_t* mask, hipStream_t stream) {
   if (n_pages == 0) return hipSuccess;
-  if (!(c.b_H == 3 && c.b_L == 1 && c.b_V == 2)) {  // the generic kernels: two launches
-    const hipError_t e = launch_quantize_k(c, n_pages, kjobs, mask, stream);
-    return e != hipSuccess ? e : launch_quantize_v(c, n_pages, vjobs, stream);
-  }
   const int words = (c.d / 2 + 31) / 32;
   const dim3 grid(2 * n_pages);
+  if (!(c.b_H == 3 && c.b_L == 1 && c.b_V == 2)) {  // any other widths
+#define PNMIX_QKVB(DD, BB)                                                                       \
+    hipLaunchKernelGGL((quantize_kv_generic_kernel<DD, BB>), grid, dim3(2 * DD), 0, stream, kjobs,  \
+                       vjobs, mask, c.pairing, c.n_hi_pairs, c.G, words, c.b_H, c.b_L, c.g_V);
+#define PNMIX_QKVW(DD)                                                                           \
+    if (c.b_V == 1) { PNMIX_QKVB(DD, 1) }                                                        \
+    else if (c.b_V == 2) { PNMIX_QKVB(DD, 2) }                                                   \
+    else if (c.b_V == 4) { PNMIX_QKVB(DD, 4) }                                                   \
+    else { PNMIX_QKVB(DD, 16) }
+    switch (c.d) {
+      case 32: PNMIX_QKVW(32) break;
+      case 64: PNMIX_QKVW(64) break;
+      default: PNMIX_QKVW(128) break;
+    }
+#undef PNMIX_QKVW
+#undef PNMIX_QKVB
+    return hipGetLastError();
+  }
   switch (c.d) {
     case 32:
       hipLaunchKernelGGL(quantize_kv_kernel<32>, grid, dim3(64), 0, stream, kjobs, vjobs, mask,

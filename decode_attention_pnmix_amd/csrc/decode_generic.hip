@@ -501,8 +501,13 @@ __device__ __forceinline__ v4u plane_codes(const uint8_t* lds, int plane, int st
   return r;
 }
 
+// Three waves per SIMD where that fits without spills: fp16 values with one head block (its
+// LDS allows three workgroups per CU at d = 128; the compiler would otherwise take 170
+// registers and two)
 template <int D, int NHB, bool BV16>
-__global__ void __launch_bounds__(kGThreads) decode_generic_mma_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kGThreads)
+    __attribute__((amdgpu_waves_per_eu(BV16 && NHB == 1 ? 3 : 2)))
+    decode_generic_mma_kernel(DecodeArgs a) {
   constexpr int NG = 4 * NHB;  // heads of the instantiation (n_g <= NG)
   using VC = ValuChunk<D, NG>;
   extern __shared__ __align__(16) uint8_t lds[];

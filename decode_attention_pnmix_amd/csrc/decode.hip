@@ -1341,20 +1341,33 @@ bool decode_fast_path(const pnmix_cfg& c) {
 }
 
 // Generic kernel plan: one 256-thread workgroup per (sequence, KV head, split) walking chunks
-// of 128 tokens (sinks, pages, residual); enough splits for about eight workgroups per compute
-// unit, at most one per chunk and kMergeSplits in all.
+// of 128 tokens (sinks, pages, residual).  Cost = rounds of resident workgroups x (chunks per
+// split + 1 for the set-up), ties to more splits; at most one split per chunk and kMergeSplits
+// in all.  (Whole rounds matter: with three workgroups per CU, Qwen3-8B at B = 32 (256 items,
+// 65 chunks) runs 116 us at 3 splits (one round) and 152 us at 4 (two, the second a third
+// full).)
 static DecodePlan generic_plan(const pnmix_cfg& c, int B, int max_pages) {
   DecodePlan p;
   const long long items = std::max<long long>((long long)B * c.H_kv, 1);
-  const long long want = (8LL * device_cus() + items - 1) / items;
   const int chunks = max_pages + 2;
-  p.splits = (int)std::max<long long>(1, std::min<long long>(want, std::min(chunks, kMergeSplits)));
+  p.lds_wave = generic_lds_bytes(c);
+  p.lds_bytes = p.lds_wave;
+  const long long resident = (long long)generic_blocks_per_cu(c, p.lds_bytes) * device_cus();
+  int best_s = 1;
+  long long best = -1;
+  for (int s = 1; s <= std::min(chunks, kMergeSplits); ++s) {
+    const long long rounds = (items * s + resident - 1) / resident;
+    const long long cost = rounds * ((chunks + s - 1) / s + 1);
+    if (best < 0 || cost <= best) {
+      best = cost;
+      best_s = s;
+    }
+  }
+  p.splits = best_s;
   p.page_splits = p.splits;
   p.n16 = 0;
   p.nw = 1;
   p.pages_per_split = (max_pages + p.splits - 1) / p.splits;
-  p.lds_wave = generic_lds_bytes(c);
-  p.lds_bytes = p.lds_wave;
   const int ng = c.H_q / c.H_kv;
   const size_t per = (size_t)items * p.splits * ng;
   const size_t o_bytes = (per * c.d * sizeof(float) + 255) & ~(size_t)255;

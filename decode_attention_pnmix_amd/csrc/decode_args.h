@@ -68,5 +68,8 @@ __device__ __forceinline__ void append_slot(const pnmix_seq_len& L, int N_s, int
 // threads, lds bytes of dynamic LDS.
 hipError_t launch_generic_split(const DecodeArgs& a, int d, int B, size_t lds, hipStream_t stream);
 size_t generic_lds_bytes(const pnmix_cfg& c);
+// Workgroups of the generic split kernel that c selects, resident per compute unit with lds
+// bytes of dynamic LDS (at least 1).
+int generic_blocks_per_cu(const pnmix_cfg& c, size_t lds);
 
 }  // namespace pnmix

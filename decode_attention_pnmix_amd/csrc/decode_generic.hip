@@ -1036,11 +1036,32 @@ size_t generic_lds_bytes(const pnmix_cfg& c) {
   return generic_mma(c) ? (size_t)glayout_cfg(c).total : valu_lds_bytes(c);
 }
 
+// The kernel instantiation for head dim D, n_g query heads per KV head, value width b_V and
+// whether the matrix-core kernel's LDS fits (else the vector-ALU kernel), passed to f.
+template <int D, class F>
+static auto with_generic_kernel(int ng, int bV, bool mma, F&& f) {
+  if (mma) {
+    if (bV == 16) {
+      if (ng <= 4) return f(decode_generic_mma_kernel<D, 1, true>);
+      if (ng <= 8) return f(decode_generic_mma_kernel<D, 2, true>);
+      return f(decode_generic_mma_kernel<D, 4, true>);
+    }
+    if (ng <= 4) return f(decode_generic_mma_kernel<D, 1, false>);
+    if (ng <= 8) return f(decode_generic_mma_kernel<D, 2, false>);
+    return f(decode_generic_mma_kernel<D, 4, false>);
+  }
+  if (ng <= 1) return f(decode_generic_valu_kernel<D, 1>);
+  if (ng <= 2) return f(decode_generic_valu_kernel<D, 2>);
+  if (ng <= 4) return f(decode_generic_valu_kernel<D, 4>);
+  if (ng <= 8) return f(decode_generic_valu_kernel<D, 8>);
+  return f(decode_generic_valu_kernel<D, 16>);
+}
+
 template <int D>
 static hipError_t launch_d(const DecodeArgs& a, int B, size_t lds, hipStream_t stream) {
   const dim3 grid(a.splits, B * a.H_kv), block(kGThreads);
-  const int ng = a.n_g;
-  auto go = [&](auto kern) -> hipError_t {
+  return with_generic_kernel<D>(a.n_g, a.b_V, glayout_args(a, D).total <= 65536,
+                                [&](auto kern) -> hipError_t {
     if (lds > 65536) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1048,22 +1069,7 @@ static hipError_t launch_d(const DecodeArgs& a, int B, size_t lds, hipStream_t s
     }
     hipLaunchKernelGGL(kern, grid, block, lds, stream, a);
     return hipGetLastError();
-  };
-  if (glayout_args(a, D).total <= 65536) {
-    if (a.b_V == 16) {
-      if (ng <= 4) return go(decode_generic_mma_kernel<D, 1, true>);
-      if (ng <= 8) return go(decode_generic_mma_kernel<D, 2, true>);
-      return go(decode_generic_mma_kernel<D, 4, true>);
-    }
-    if (ng <= 4) return go(decode_generic_mma_kernel<D, 1, false>);
-    if (ng <= 8) return go(decode_generic_mma_kernel<D, 2, false>);
-    return go(decode_generic_mma_kernel<D, 4, false>);
-  }
-  if (ng <= 1) return go(decode_generic_valu_kernel<D, 1>);
-  if (ng <= 2) return go(decode_generic_valu_kernel<D, 2>);
-  if (ng <= 4) return go(decode_generic_valu_kernel<D, 4>);
-  if (ng <= 8) return go(decode_generic_valu_kernel<D, 8>);
-  return go(decode_generic_valu_kernel<D, 16>);
+  });
 }
 
 hipError_t launch_generic_split(const DecodeArgs& a, int d, int B, size_t lds, hipStream_t stream) {
@@ -1071,6 +1077,27 @@ hipError_t launch_generic_split(const DecodeArgs& a, int d, int B, size_t lds, h
     case 32: return launch_d<32>(a, B, lds, stream);
     case 64: return launch_d<64>(a, B, lds, stream);
     default: return launch_d<128>(a, B, lds, stream);
+  }
+}
+
+template <int D>
+static int blocks_d(const pnmix_cfg& c, size_t lds) {
+  return with_generic_kernel<D>(c.H_q / c.H_kv, c.b_V, generic_mma(c), [&](auto kern) -> int {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kGThreads, lds) != hipSuccess ||
+        n <= 0) {
+      (void)hipGetLastError();
+      return 1;
+    }
+    return n;
+  });
+}
+
+int generic_blocks_per_cu(const pnmix_cfg& c, size_t lds) {
+  switch (c.d) {
+    case 32: return blocks_d<32>(c, lds);
+    case 64: return blocks_d<64>(c, lds);
+    default: return blocks_d<128>(c, lds);
   }
 }
 

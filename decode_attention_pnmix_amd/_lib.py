@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
         "pnmix_v_page_bytes": (sz, [cp]),
         "pnmix_score_workspace_bytes": (sz, [cp, i32, i32]),
         "pnmix_decode_splits": (i32, [cp, i32, i32]),
+        "pnmix_decode_plan": (st, [cp, i32, i32, P]),
         "pnmix_decode_workspace_bytes": (sz, [cp, i32, i32]),
         "pnmix_last_error": (ctypes.c_char_p, []),
         "pnmix_score_prefill": (st, [cp, i32, i32, P, P, P, P, P, sz, P]),
@@ -92,6 +93,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("pnmix_check_cfg", "pnmix_hi_pairs", "pnmix_mask_words", "pnmix_k_page_bytes",
             "pnmix_v_page_bytes", "pnmix_score_workspace_bytes", "pnmix_decode_splits",
+            "pnmix_decode_plan",
             "pnmix_decode_workspace_bytes", "pnmix_last_error", "pnmix_score_prefill",
             "pnmix_quantize_k_page", "pnmix_quantize_v_page", "pnmix_decode_attn",
             "pnmix_append_kv", "pnmix_commit_page", "pnmix_decode_attn_paged",
@@ -161,6 +163,14 @@ def pnmix_score_workspace_bytes(cfg, B: int, P: int) -> int:
 
 def pnmix_decode_splits(cfg, B: int, max_pages: int) -> int:
     return int(lib().pnmix_decode_splits(ctypes.byref(cfg), B, max_pages))
+
+
+def pnmix_decode_plan(cfg, B: int, max_pages: int) -> dict:
+    """The decode split plan: partials per (sequence, KV head), page waves, fp16-row waves (0:
+    their pieces ride on the page waves), waves per workgroup."""
+    out = (ctypes.c_int32 * 4)()
+    _check(lib().pnmix_decode_plan(ctypes.byref(cfg), B, max_pages, out))
+    return {"splits": out[0], "page_splits": out[1], "fp16_splits": out[2], "waves_per_group": out[3]}
 
 
 def pnmix_decode_workspace_bytes(cfg, B: int, max_pages: int) -> int:

@@ -364,8 +364,13 @@ __device__ void write_empty_partial(const DecodeArgs& a, const PartOut& po) {
 
 // -------------------------------------------------------------- fp16 sink + residual split
 
-// One wave over the 64-token chunks chunk, chunk + n_chunk_splits, ... of the fp16 rows (token
-// order: sinks, then residual rows), 32 tokens at a time on the fp16 matrix cores
+// V^T staging of the fp16 rows in a wave's LDS slice: [D][32 tokens + 4] halves (the pad spreads
+// the banks)
+template <int D>
+constexpr int kVtBytes = D * 36 * 2;
+
+// One wave over the 32-token pieces first, first + stride, ... of the fp16 rows (token order:
+// sinks, then residual rows) on the fp16 matrix cores
 // (v_mfma_f32_16x16x32_f16, exact fp16 products, fp32 sums):
 // * logits transposed, S^T[token][head] = K q^T: the A operand is the key rows as loaded (16
 //   bytes of one token per lane), the B operand the queries (head = lane column);
@@ -378,13 +383,15 @@ __device__ void write_empty_partial(const DecodeArgs& a, const PartOut& po) {
 //   the lane's 8 tokens, then over the four lane groups.
 // t_new >= 0: fp16 row t_new (sinks first, then residual rows) is the fused append's new row,
 // read from k_new / v_new instead of the cache.
+// mo != NULL: the same wave's page partial (o [n_g][D], then (m, l) [n_g][2]) is in LDS at mo;
+// it is merged into this partial (log-sum-exp rule) before the store.
 template <int D>
 __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, const PartOut& po,
-                            int sink_len, int res_len, int chunk, int n_chunk_splits,
-                            uint8_t* lds, int t_new) {
+                            int sink_len, int res_len, int first, int stride, uint8_t* lds,
+                            int t_new, const lds_f32* mo) {
   constexpr int KS = D / 32;         // 32-channel K-steps of S^T
   constexpr int CT = D / 16;         // 16-channel tiles of O^T
-  constexpr int VS = 36;             // V^T row stride in halves: 32 tokens + 4 (bank spread)
+  constexpr int VS = kVtBytes<D> / (2 * D);  // V^T row stride in halves: 32 tokens + 4
   constexpr int OC = D / 8;          // 8-channel pieces of a row
   constexpr int VU = (8 * OC + 63) / 64;  // (4 tokens x 8 channels) staging units per lane
   const int lane = threadIdx.x & 63;
@@ -418,9 +425,9 @@ __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, const
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) acc[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // 32-token pieces of this split's chunks; the loads of the next piece are issued before the
-  // current one is computed
-  auto s0_of = [&](int k) { return 64 * (chunk + (k >> 1) * n_chunk_splits) + 32 * (k & 1); };
+  // this wave's 32-token pieces; the loads of the next piece are issued before the current one
+  // is computed
+  auto s0_of = [&](int k) { return 32 * (first + k * stride); };
   auto load_piece = [&](int s0, v4u (&ka)[2][KS], v4u (&vr)[VU][4]) {
     // key rows (A of S^T): tile tt holds tokens s0 + 16 tt + n, channels 32 ks + 8 g ...
 #pragma unroll
@@ -524,6 +531,23 @@ __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, const
   }
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  if (mo) {
+    wave_sync();  // the page partial is in LDS
+    if (n < ng) {
+      const lds_f32* mml = mo + ng * D;
+      const float mp = mml[2 * n], lp = mml[2 * n + 1];
+      const float M = fmaxf(m, mp);
+      const float f1 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+      const float f2 = mp == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
+      l = __builtin_fmaf(lp, f2, l * f1);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const v4f op = *reinterpret_cast<const lds_v4f*>(mo + n * D + 16 * ct + 4 * g);
+        acc[ct] = acc[ct] * f1 + op * f2;
+      }
+      m = M;
+    }
+  }
   if (n < ng) {
     // O^T: lane (g, n) holds channels 16 ct + 4 g + r of head n
 #pragma unroll
@@ -531,6 +555,29 @@ __device__ void fp16_region(const DecodeArgs& a, int b, int h, int64_t bh, const
       po.o4(n * D + 16 * ct + 4 * g, acc[ct]);
     if (g == 0) po.ml(n, m, l);
   }
+}
+
+// The fp16 rows of (sequence, KV head) bh, 32-token pieces first, first + stride, ...: the
+// lengths (with a fused append's new row) and then fp16_region.
+template <int D>
+__device__ __forceinline__ void fp16_split(const DecodeArgs& a, int64_t bh, const PartOut& po, int first,
+                                           int stride, uint8_t* wl, const lds_f32* mo) {
+  const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
+  pnmix_seq_len L;
+  L.sink_len = kconst(&a.lens[b].sink_len)[0];
+  L.n_pages = kconst(&a.lens[b].n_pages)[0];
+  L.res_len = kconst(&a.lens[b].res_len)[0];
+  int t_new = -1;
+  if (a.k_new) {  // the fused append's row joins the fp16 rows
+    int kind, row;
+    append_slot(L, a.N_s, kind, row);
+    if (kind == 0) L.sink_len = row + 1;
+    if (kind == 1) L.res_len = row + 1;
+    if (kind != 2) t_new = kind == 0 ? row : min(max(L.sink_len, 0), a.N_s) + row;
+  }
+  const int sink_len = min(max(L.sink_len, 0), a.N_s);
+  const int res_len = min(max(L.res_len, 0), kN);
+  fp16_region<D>(a, b, h, bh, po, sink_len, res_len, first, stride, wl, t_new, mo);
 }
 
 // ----------------------------------------------------------------------------- page split
@@ -1138,8 +1185,10 @@ struct KernelWaves {
 
 // One launch per decode call.  Wave w of workgroup x takes split x nw + w of its (sequence, KV
 // head): the first page_splits walk packed pages, the next ones take one 64-token chunk each of
-// the fp16 sink and residual rows, any further ones are empty.  With one wave per workgroup the
-// split writes its partial to the workspace; with nw > 1 the waves leave their partials in
+// the fp16 sink and residual rows (32-token pieces strided over them), any further ones are
+// empty.  With fold16 (one wave per workgroup) the fp16 pieces have no waves of their own: the
+// page splits take them after their pages, the last split first.  With one wave per workgroup
+// the split writes its partial to the workspace; with nw > 1 the waves leave their partials in
 // their LDS slices and the workgroup merges them into one partial (same log-sum-exp rule as
 // the merge kernel), so the merge kernel reads nw times fewer.
 // Two waves per SIMD (at most 256 registers) where the compiler fits them without spills:
@@ -1159,26 +1208,28 @@ decode_kernel(DecodeArgs a) {
   const int64_t pbase = (bh * a.splits + split) * ng;  // nw == 1
   lds_f32* const st = (lds_f32*)(wl);
   const PartOut po{a.part_o + pbase * D, a.part_ml + pbase * 2, st, st + ng * D, nw > 1};
-  if (split < a.page_splits) {
-    page_split<D, NT, KG, KH, PG>(a, wl, split, bh, po);
-  } else if (split < a.page_splits + a.n16) {
-    const int b = (int)(bh / a.H_kv), h = (int)(bh % a.H_kv);
-    pnmix_seq_len L;
-    L.sink_len = kconst(&a.lens[b].sink_len)[0];
-    L.n_pages = kconst(&a.lens[b].n_pages)[0];
-    L.res_len = kconst(&a.lens[b].res_len)[0];
-    int t_new = -1;
-    if (a.k_new) {  // the fused append's row joins the fp16 rows
-      int kind, row;
-      append_slot(L, a.N_s, kind, row);
-      if (kind == 0) L.sink_len = row + 1;
-      if (kind == 1) L.res_len = row + 1;
-      if (kind != 2) t_new = kind == 0 ? row : min(max(L.sink_len, 0), a.N_s) + row;
+  // One call site of each region (the page split, then the fp16 rows).  The fp16 pieces go to
+  // splits of their own (split - page_splits of n16, pieces strided by n16), or with fold16 to
+  // the page splits, last split first (piece i to split page_splits - 1 - i, strided by
+  // page_splits); such a wave leaves its page partial in LDS past the V^T staging and the fp16
+  // pass merges it into the one partial it stores.
+  const bool pages = split < a.page_splits;
+  int first16 = -1, stride16 = 1;
+  if (a.fold16 > 0) {
+    if (pages && a.page_splits - 1 - split < a.fold16) {
+      first16 = a.page_splits - 1 - split;
+      stride16 = a.page_splits;
     }
-    const int sink_len = min(max(L.sink_len, 0), a.N_s);
-    const int res_len = min(max(L.res_len, 0), kN);
-    fp16_region<D>(a, b, h, bh, po, sink_len, res_len, split - a.page_splits, a.n16, wl, t_new);
-  } else {
+  } else if (!pages && split < a.page_splits + a.n16) {
+    first16 = split - a.page_splits;
+    stride16 = a.n16;
+  }
+  lds_f32* const pl = (lds_f32*)(wl + kVtBytes<D>);
+  const bool merge = pages && first16 >= 0;
+  if (pages) page_split<D, NT, KG, KH, PG>(a, wl, split, bh, merge ? PartOut{po.go, po.gml, pl, pl + ng * D, true} : po);
+  if (first16 >= 0) {
+    fp16_split<D>(a, bh, po, first16, stride16, wl, merge ? pl : nullptr);
+  } else if (!pages) {
     write_empty_partial<D>(a, po);
   }
   if (nw == 1) return;
@@ -1231,7 +1282,7 @@ static size_t lds_bytes(const pnmix_cfg& c) {
 }
 
 static size_t lds_fp16_bytes(const pnmix_cfg& c) {
-  return (size_t)c.d * 36 * 2;  // V^T [d][32 tokens + 4] halves
+  return (size_t)c.d * 36 * 2;  // V^T [d][32 tokens + 4] halves (kVtBytes)
 }
 
 // LDS slice of one wave: the larger of the page and fp16 layouts, and at least the partial the
@@ -1327,8 +1378,9 @@ struct BlocksPerCu {
   }
 };
 
-// Split plan.  Large batches (>= 128 (sequence, KV head) items): one wave per workgroup, one
-// fp16 split walking all 64-token chunks.  Small batches: workgroups of nw waves (as many as
+// Split plan.  Large batches (>= 128 (sequence, KV head) items): one wave per workgroup, and the
+// fp16 rows either in one split of their own or spread over the page splits in 32-token pieces,
+// the last split (which has the fewest pages) first.  Small batches: workgroups of nw waves (as many as
 // the instantiation and the LDS allow) merge their waves' partials on chip, and the number of
 // fp16 splits is searched too.  Cost = rounds of resident workgroups x (pages per split + 1 for
 // the set-up), the fp16 splits' chunks counting half a page each; ties go to more page splits.
@@ -1366,6 +1418,7 @@ static DecodePlan generic_plan(const pnmix_cfg& c, int B, int max_pages) {
   p.splits = best_s;
   p.page_splits = p.splits;
   p.n16 = 0;
+  p.fold16 = 0;
   p.nw = 1;
   p.pages_per_split = (max_pages + p.splits - 1) / p.splits;
   const int ng = c.H_q / c.H_kv;
@@ -1390,30 +1443,58 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   p.lds_bytes = (size_t)nw * p.lds_wave;
   const int bpc = dispatch(c, BlocksPerCu{p.lds_bytes, 64 * nw});
   const long long resident = (long long)bpc * device_cus();  // workgroups
-  int ps = 0, n16 = nw == 1 ? (items >= 128 ? 1 : chunks) : 1;
+  // Costs in quarter pages: a page 4, a wave's set-up 4, a 64-token chunk of a split of its own
+  // 2, a 32-token piece inside a page split 8 (one wave waits on its loads; measured with 63
+  // pages: Qwen3-8B at B = 32, 8K, runs 56.0 us with 8 page splits and the pieces spread, 54.6
+  // with 7 and a split of their own; Qwen3-32B at B = 32, 32K, 206 us with 8 page splits and
+  // the pieces spread (one round of resident waves), 213 with 15 and a split of their own)
+  const int pieces = (c.N_s + c.N + 31) / 32;
+  int ps = 0, n16 = nw == 1 ? (items >= 128 ? 1 : chunks) : 1, fold = 0;
   if (max_pages > 0) {
     long long best = -1;
+    auto consider = [&](long long cost, int s, int f, int fo) {  // ties: more splits, no spread
+      if (best < 0 || cost < best || (cost == best && s > ps && !fo)) {
+        best = cost;
+        ps = s;
+        n16 = f;
+        fold = fo;
+      }
+    };
     const int n16_lo = n16, n16_hi = nw == 1 ? n16 : chunks;
     for (int f = n16_lo; f <= n16_hi; ++f) {
-      const int f16 = nw == 1 ? 0 : (chunks + f - 1) / f;  // half pages
+      const int f16 = nw == 1 ? 0 : 2 * ((chunks + f - 1) / f);
       const int ps_max = std::min(max_pages, kMergeSplits * nw - f);
       for (int s = 1; s <= ps_max; ++s) {
         const long long wg = (s + f + nw - 1) / nw;
         const long long rounds = (items * wg + resident - 1) / resident;
-        const long long cost = rounds * (std::max<long long>(2LL * ((max_pages + s - 1) / s), f16) + 2);
-        if (best < 0 || cost < best || (cost == best && s > ps)) {
-          best = cost;
-          ps = s;
-          n16 = f;
+        consider(rounds * (std::max<long long>(4LL * ((max_pages + s - 1) / s), f16) + 4), s, f, 0);
+      }
+    }
+    if (nw == 1 && items >= 128) {
+      // the fp16 pieces spread over the page splits, last split first
+      for (int s = 1; s <= std::min(max_pages, kMergeSplits); ++s) {
+        const long long rounds = (items * s + resident - 1) / resident;
+        long long wave = 0;
+        for (int w = 0; w < s; ++w) {
+          const int pgs = (max_pages - 1 - w) / s + 1;  // w < s <= max_pages
+          const int i = s - 1 - w;
+          const int pcs = i < pieces ? (pieces - 1 - i) / s + 1 : 0;
+          wave = std::max<long long>(wave, 4LL * pgs + 8LL * pcs);
         }
+        consider(rounds * (wave + 4), s, 0, pieces);
       }
     }
   }
   p.page_splits = ps;
   p.n16 = n16;
+  p.fold16 = fold;
   p.pages_per_split = ps > 0 ? (max_pages + ps - 1) / ps : 0;
   p.splits = (ps + n16 + nw - 1) / nw;
   const int ng = c.H_q / c.H_kv;
+  if (fold) {  // the page partial waits in LDS past the V^T staging
+    p.lds_wave = std::max(p.lds_wave, (lds_fp16_bytes(c) + (size_t)ng * (c.d + 2) * 4 + 15) & ~(size_t)15);
+    p.lds_bytes = p.lds_wave;
+  }
   const size_t per = (size_t)items * p.splits * ng;
   const size_t o_bytes = (per * c.d * sizeof(float) + 255) & ~(size_t)255;
   p.ws_bytes = o_bytes + ((per * 2 * sizeof(float) + 255) & ~(size_t)255);
@@ -1509,6 +1590,7 @@ hipError_t launch_decode(const pnmix_cfg& c, int B, int max_pages, const uint16_
   a.splits = p.splits;
   a.page_splits = p.page_splits;
   a.n16 = p.n16;
+  a.fold16 = p.fold16;
   a.nw = p.nw;
   a.lds_T = decode_fast_path(c) ? (int)lds_T_bytes(c) : 0;
   a.lds_wave = (int)p.lds_wave;

@@ -38,8 +38,10 @@ struct DecodeArgs {
   int b_H, b_L, b_V;  // bit widths (the matrix-core kernel serves (3, 1, 2))
   int64_t kpb, vpb;
   int splits;      // partials per (sequence, KV head): workgroups of the split kernel
-  int page_splits; // page splits per (sequence, KV head), then n16 fp16-row splits
+  int page_splits; // page splits per (sequence, KV head), then n16 fp16-row splits (32-token
+                   // pieces strided by n16)
   int n16;
+  int fold16;      // > 0: fp16 piece i goes to page split page_splits - 1 - i (mod page_splits), nw = 1
   int nw;          // waves per workgroup, one split each
   int lds_T;       // bytes of the q.K digit table (KG * NT * 16 rows * TL)
   int lds_wave;    // LDS bytes of one wave's slice

@@ -38,6 +38,8 @@ struct DecodePlan {
   int splits;           // partials per (sequence, KV head): workgroups of the split kernel
   int page_splits;      // waves over the packed pages, per (sequence, KV head)
   int n16;              // waves over the fp16 sink and residual rows, per (sequence, KV head)
+  int fold16;           // > 0: no fp16 splits; the page splits take the fold16 32-token pieces
+                        // of the fp16 rows (one wave per workgroup, n16 = 0)
   int nw;               // waves per workgroup (their partials are merged on chip)
   int pages_per_split;  // most pages of one page wave (a sequence's pages are split evenly)
   size_t ws_bytes;      // workspace for the partials

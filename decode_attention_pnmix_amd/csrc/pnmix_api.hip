@@ -111,6 +111,19 @@ int32_t pnmix_decode_splits(const pnmix_cfg* c, int32_t B, int32_t max_pages) {
   return pnmix::decode_plan(*c, B, max_pages).splits;
 }
 
+pnmix_status pnmix_decode_plan(const pnmix_cfg* c, int32_t B, int32_t max_pages, int32_t* out) {
+  const pnmix_status s = check(c);
+  if (s != PNMIX_OK) return s;
+  if (B <= 0 || max_pages < 0 || !out)
+    return fail(PNMIX_E_INVALID, "decode plan: B > 0, max_pages >= 0 and out needed");
+  const pnmix::DecodePlan p = pnmix::decode_plan(*c, B, max_pages);
+  out[0] = p.splits;
+  out[1] = p.page_splits;
+  out[2] = p.n16;
+  out[3] = p.nw;
+  return PNMIX_OK;
+}
+
 size_t pnmix_decode_workspace_bytes(const pnmix_cfg* c, int32_t B, int32_t max_pages) {
   if (check(c) != PNMIX_OK || B <= 0 || max_pages < 0) return 0;
   return pnmix::decode_plan(*c, B, max_pages).ws_bytes;

@@ -107,6 +107,13 @@ size_t pnmix_v_page_bytes(const pnmix_cfg* cfg);
 size_t pnmix_score_workspace_bytes(const pnmix_cfg* cfg, int32_t B, int32_t P);
 /* Number of split-K partitions pnmix_decode_attn uses for this batch and capacity. */
 int32_t pnmix_decode_splits(const pnmix_cfg* cfg, int32_t B, int32_t max_pages);
+/* The split plan of pnmix_decode_attn for this batch and capacity (diagnostics; it depends on
+ * the device's compute units and occupancy): out[0] partials per (sequence, KV head) (as
+ * pnmix_decode_splits), out[1] waves over the packed pages, out[2] waves over the fp16 sink
+ * and residual rows (0: their 32-token pieces are spread over the page waves), out[3] waves per
+ * workgroup.  out: 4 int32 in host memory, written only on success.  PNMIX_E_INVALID for an
+ * invalid configuration, B <= 0, max_pages < 0 or a NULL out. */
+pnmix_status pnmix_decode_plan(const pnmix_cfg* cfg, int32_t B, int32_t max_pages, int32_t* out);
 /* Device workspace of pnmix_decode_attn (bytes). */
 size_t pnmix_decode_workspace_bytes(const pnmix_cfg* cfg, int32_t B, int32_t max_pages);
 /* Message of the last failed call on this thread ("" if none). */

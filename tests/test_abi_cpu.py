@@ -94,7 +94,17 @@ def test_decode_plan_queries():
         n16_max = 1 if B * c.H_kv >= 128 else (c.N_s + c.N + 63) // 64
         assert 1 <= s <= min(mp + n16_max, 136)
         assert P.pnmix_decode_workspace_bytes(c, B, mp) >= B * 8 * s * 4 * (128 + 2) * 4
+        plan = P.pnmix_decode_plan(c, B, mp)
+        nw = plan["waves_per_group"]
+        assert plan["splits"] == s == -(-(plan["page_splits"] + plan["fp16_splits"]) // nw)
+        assert plan["page_splits"] <= mp
+        # no fp16 waves: only with pages, one wave per workgroup and a large batch
+        if plan["fp16_splits"] == 0:
+            assert mp > 0 and nw == 1 and B * c.H_kv >= 128
     assert P.pnmix_decode_splits(_cfg(G=48), 1, 10) == 0
+    for args in ((_cfg(G=48), 1, 10), (c, 0, 10), (c, 1, -1)):
+        with pytest.raises(P.PnmixError):
+            P.pnmix_decode_plan(*args)
     # the generic kernel (other bit widths): one split per 128-token chunk at most
     for kw in ({"b_V": 16}, {"b_H": 4, "b_L": 2}, {"d": 64, "g_V": 16}):
         for B, mp in ((1, 255), (32, 63), (1, 0)):

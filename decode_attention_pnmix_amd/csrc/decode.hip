@@ -52,7 +52,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kMergeSplits = 136;  // the planner's cap: beyond it the merge costs more than it saves
+constexpr int kMergeSplits = 136;
+constexpr long long kPieceCost = 5;  // planner cost of a 32-token fp16 piece on a page wave (a page: 4)  // the planner's cap: beyond it the merge costs more than it saves
 constexpr int kWS = kN + 16;     // row stride of the p.V digit table (rows on distinct banks)
 constexpr float kLog2e = 1.4426950408889634f;
 // y + 2^23 + 0x8080 rounds y in [0, 2^23 - 0x8080) to an integer (RNE) and leaves y + 0x8080
@@ -1444,22 +1445,14 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   const int bpc = dispatch(c, BlocksPerCu{p.lds_bytes, 64 * nw});
   const long long resident = (long long)bpc * device_cus();  // workgroups
   // Costs in quarter pages: a page 4, a wave's set-up 4, a 64-token chunk of a split of its own
-  // 2, a 32-token piece inside a page split 8 (one wave waits on its loads; measured with 63
-  // pages: Qwen3-8B at B = 32, 8K, runs 56.0 us with 8 page splits and the pieces spread, 54.6
-  // with 7 and a split of their own; Qwen3-32B at B = 32, 32K, 206 us with 8 page splits and
-  // the pieces spread (one round of resident waves), 213 with 15 and a split of their own)
+  // 2, a 32-token piece on a page wave kPieceCost.
   const int pieces = (c.N_s + c.N + 31) / 32;
+  const size_t ng = (size_t)(c.H_q / c.H_kv);
+  // with the pieces spread, a wave's page partial waits in LDS past the V^T staging
+  const size_t fold_wave = std::max(p.lds_wave, (lds_fp16_bytes(c) + ng * (c.d + 2) * 4 + 15) & ~(size_t)15);
   int ps = 0, n16 = nw == 1 ? (items >= 128 ? 1 : chunks) : 1, fold = 0;
   if (max_pages > 0) {
-    long long best = -1;
-    auto consider = [&](long long cost, int s, int f, int fo) {  // ties: more splits, no spread
-      if (best < 0 || cost < best || (cost == best && s > ps && !fo)) {
-        best = cost;
-        ps = s;
-        n16 = f;
-        fold = fo;
-      }
-    };
+    long long best = -1, best_rounds = 0;
     const int n16_lo = n16, n16_hi = nw == 1 ? n16 : chunks;
     for (int f = n16_lo; f <= n16_hi; ++f) {
       const int f16 = nw == 1 ? 0 : 2 * ((chunks + f - 1) / f);
@@ -1467,21 +1460,44 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
       for (int s = 1; s <= ps_max; ++s) {
         const long long wg = (s + f + nw - 1) / nw;
         const long long rounds = (items * wg + resident - 1) / resident;
-        consider(rounds * (std::max<long long>(4LL * ((max_pages + s - 1) / s), f16) + 4), s, f, 0);
+        const long long cost = rounds * (std::max<long long>(4LL * ((max_pages + s - 1) / s), f16) + 4);
+        if (best < 0 || cost < best || (cost == best && s > ps)) {  // ties: more splits
+          best = cost;
+          best_rounds = rounds;
+          ps = s;
+          n16 = f;
+        }
       }
     }
-    if (nw == 1 && items >= 128) {
-      // the fp16 pieces spread over the page splits, last split first
-      for (int s = 1; s <= std::min(max_pages, kMergeSplits); ++s) {
-        const long long rounds = (items * s + resident - 1) / resident;
+    // The fp16 pieces spread over the page splits, last split first, where that saves a round of
+    // resident workgroups (measured: Qwen3-32B at B = 32, 32K, 206 us with 8 page splits in one
+    // round against 213 with 15 and an fp16 split in two; Llama-3.1-8B at B = 110, 8K, 165 us
+    // with 2 page splits in one round against 167.5 with 8 and an fp16 split in four; but
+    // Qwen3-8B at B = 32, 8K, 55.8 us with 8 page splits against 54.4 with 7 and an fp16 split,
+    // one round each, and B = 1 at 32K 19.0 us against 17.8).  The larger slices must still fit
+    // a workgroup; the resident workgroups are counted with them.
+    if ((nw == 1 && items >= 128) || (nw > 1 && nw * fold_wave <= device_lds_per_block())) {
+      const long long resident_f =
+          (long long)dispatch(c, BlocksPerCu{nw * fold_wave, 64 * nw}) * device_cus();
+      const long long rounds_cap = best_rounds;
+      for (int s = 1; s <= std::min(max_pages, kMergeSplits * nw); ++s) {
+        const long long wg = (s + nw - 1) / nw;
+        const long long rounds = (items * wg + resident_f - 1) / resident_f;
+        if (rounds >= rounds_cap) continue;
         long long wave = 0;
         for (int w = 0; w < s; ++w) {
           const int pgs = (max_pages - 1 - w) / s + 1;  // w < s <= max_pages
           const int i = s - 1 - w;
           const int pcs = i < pieces ? (pieces - 1 - i) / s + 1 : 0;
-          wave = std::max<long long>(wave, 4LL * pgs + 8LL * pcs);
+          wave = std::max<long long>(wave, 4LL * pgs + kPieceCost * pcs);
         }
-        consider(rounds * (wave + 4), s, 0, pieces);
+        const long long cost = rounds * (wave + 4);
+        if (cost < best) {
+          best = cost;
+          ps = s;
+          n16 = 0;
+          fold = pieces;
+        }
       }
     }
   }
@@ -1490,10 +1506,9 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   p.fold16 = fold;
   p.pages_per_split = ps > 0 ? (max_pages + ps - 1) / ps : 0;
   p.splits = (ps + n16 + nw - 1) / nw;
-  const int ng = c.H_q / c.H_kv;
-  if (fold) {  // the page partial waits in LDS past the V^T staging
-    p.lds_wave = std::max(p.lds_wave, (lds_fp16_bytes(c) + (size_t)ng * (c.d + 2) * 4 + 15) & ~(size_t)15);
-    p.lds_bytes = p.lds_wave;
+  if (fold) {
+    p.lds_wave = fold_wave;
+    p.lds_bytes = (size_t)nw * p.lds_wave;
   }
   const size_t per = (size_t)items * p.splits * ng;
   const size_t o_bytes = (per * c.d * sizeof(float) + 255) & ~(size_t)255;

@@ -349,11 +349,12 @@ def test_decode_ragged_lengths_and_edges(g_V):
 
 
 def test_decode_ragged_fp16_pieces_on_page_waves():
-    """A large batch (256 (sequence, KV head) items) with a long capacity, where the plan puts
-    the fp16 rows' 32-token pieces on the page waves (no fp16 waves of their own): ragged
+    """A large batch (256 (sequence, KV head) items, d = 128, 4 query heads per KV head: two
+    waves per SIMD) with a long capacity, where the plan puts the fp16 rows' 32-token pieces on
+    the page waves (no fp16 waves of their own: one round of resident waves, not two): ragged
     lengths (no pages, few pages, one residual row, full residual, full capacity, empty
     sequences) against the oracle."""
-    w = synth.Workload("ragged-spread", 1, 1, 8, 2, 64, 1, 1e4, 64, 1024, 0.5, 64)
+    w = synth.Workload("ragged-spread", 1, 1, 8, 2, 128, 1, 1e6, 64, 1024, 0.5, 128)
     lc, _ = cfgs(w)
     B, max_pages = 128, 255
     plan = P.pnmix_decode_plan(lc, B, max_pages)

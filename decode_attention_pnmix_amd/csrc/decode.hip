@@ -1452,7 +1452,7 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
   const size_t fold_wave = std::max(p.lds_wave, (lds_fp16_bytes(c) + ng * (c.d + 2) * 4 + 15) & ~(size_t)15);
   int ps = 0, n16 = nw == 1 ? (items >= 128 ? 1 : chunks) : 1, fold = 0;
   if (max_pages > 0) {
-    long long best = -1, best_rounds = 0;
+    long long best = -1;
     const int n16_lo = n16, n16_hi = nw == 1 ? n16 : chunks;
     for (int f = n16_lo; f <= n16_hi; ++f) {
       const int f16 = nw == 1 ? 0 : 2 * ((chunks + f - 1) / f);
@@ -1463,27 +1463,24 @@ DecodePlan decode_plan(const pnmix_cfg& c, int B, int max_pages) {
         const long long cost = rounds * (std::max<long long>(4LL * ((max_pages + s - 1) / s), f16) + 4);
         if (best < 0 || cost < best || (cost == best && s > ps)) {  // ties: more splits
           best = cost;
-          best_rounds = rounds;
           ps = s;
           n16 = f;
         }
       }
     }
-    // The fp16 pieces spread over the page splits, last split first, where that saves a round of
-    // resident workgroups (measured: Qwen3-32B at B = 32, 32K, 206 us with 8 page splits in one
-    // round against 213 with 15 and an fp16 split in two; Llama-3.1-8B at B = 110, 8K, 165 us
-    // with 2 page splits in one round against 167.5 with 8 and an fp16 split in four; but
-    // Qwen3-8B at B = 32, 8K, 55.8 us with 8 page splits against 54.4 with 7 and an fp16 split,
-    // one round each, and B = 1 at 32K 19.0 us against 17.8).  The larger slices must still fit
-    // a workgroup; the resident workgroups are counted with them.
+    // The fp16 pieces spread over the page splits, last split first.  The plan sees only the
+    // capacity (max_pages); measured side by side at 64 pages with capacity 65 (call us, pieces
+    // spread against an fp16 split of their own): Qwen3-8B B = 32 54.4 against 57.8, Llama-3.1-8B
+    // B = 110 166.2 against 183.1, Qwen3-32B B = 32 (256 pages) 207.9 against 217.4; at 63 pages
+    // with capacity 64 Qwen3-8B takes 55.9 against 54.4 and B = 1 at 32K 19.0 against 17.8 (the
+    // cost model keeps the fp16 split there).  The larger slices must still fit a workgroup; the
+    // resident workgroups are counted with them.
     if ((nw == 1 && items >= 128) || (nw > 1 && nw * fold_wave <= device_lds_per_block())) {
       const long long resident_f =
           (long long)dispatch(c, BlocksPerCu{nw * fold_wave, 64 * nw}) * device_cus();
-      const long long rounds_cap = best_rounds;
       for (int s = 1; s <= std::min(max_pages, kMergeSplits * nw); ++s) {
         const long long wg = (s + nw - 1) / nw;
         const long long rounds = (items * wg + resident_f - 1) / resident_f;
-        if (rounds >= rounds_cap) continue;
         long long wave = 0;
         for (int w = 0; w < s; ++w) {
           const int pgs = (max_pages - 1 - w) / s + 1;  // w < s <= max_pages

@@ -9,7 +9,8 @@
 // chunk's token rows in LDS with 16-byte loads all in flight at once, and lane i owns RoPE pair
 // i and adds its pair norms over the chunk in ascending token order.  Pass 2 gives each (sequence, KV head) one
 // workgroup: its waves add the chunk sums of one head each in ascending chunk order (the loads
-// go out 32 chunks at a time), divide by P, then wave 0 forms sigma, ranks the pairs through
+// go out 32 chunks at a time, the next 32 in flight during the adds; one wave per head for
+// long prompts), divide by P, then wave 0 forms sigma, ranks the pairs through
 // LDS and writes the mask with a wave ballot.  The summation order is fixed, so sigma and the
 // mask are bit-identical to the reference oracle.
 #include "common.h"
@@ -81,7 +82,7 @@ __global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __rest
 
 constexpr int kSelLoads = 32;  // chunk-sum loads in flight per lane
 
-__global__ void __launch_bounds__(256) score_select_kernel(const float* __restrict__ chunk_sums,
+__global__ void __launch_bounds__(1024) score_select_kernel(const float* __restrict__ chunk_sums,
                                                            float* __restrict__ sigma,
                                                            uint32_t* __restrict__ mask, int H_q,
                                                            int H_kv, int d, int P, int n_chunks,
@@ -100,16 +101,33 @@ __global__ void __launch_bounds__(256) score_select_kernel(const float* __restri
     const int head = r < ng ? h * ng + r : H_q + h;
     if (lane < np) {
       const float* cs = chunk_sums + ((int64_t)(seq * H + head) * n_chunks) * np + lane;
-      // the adds stay in ascending chunk order; the loads go out kSelLoads at a time
-      float s = 0.0f;
-      for (int c0 = 0; c0 < n_chunks; c0 += kSelLoads) {
-        float v[kSelLoads];
+      // the adds stay in ascending chunk order; the loads go out kSelLoads at a time, and for
+      // long prompts the next kSelLoads are in flight while the current ones are added (chunk
+      // indices past the end are clamped to the last chunk: no load sits under a branch)
+      auto ld = [&](float (&v)[kSelLoads], int c0) {
 #pragma unroll
-        for (int j = 0; j < kSelLoads; ++j)
-          v[j] = c0 + j < n_chunks ? cs[(int64_t)(c0 + j) * np] : 0.0f;
+        for (int j = 0; j < kSelLoads; ++j) v[j] = cs[(int64_t)min(c0 + j, n_chunks - 1) * np];
+      };
+      float s = 0.0f;
+      auto add = [&](const float (&v)[kSelLoads], int c0) {
 #pragma unroll
         for (int j = 0; j < kSelLoads; ++j)
           if (c0 + j < n_chunks) s = s + v[j];
+      };
+      float va[kSelLoads];
+      ld(va, 0);
+      if (n_chunks <= kSelLoads) {
+        add(va, 0);
+      } else {
+        float vb[kSelLoads];
+        for (int c0 = 0;; c0 += 2 * kSelLoads) {
+          ld(vb, c0 + kSelLoads);
+          add(va, c0);
+          if (c0 + kSelLoads >= n_chunks) break;
+          ld(va, c0 + 2 * kSelLoads);
+          add(vb, c0 + kSelLoads);
+          if (c0 + 2 * kSelLoads >= n_chunks) break;
+        }
       }
       means[r][lane] = s / (float)P;
     }
@@ -166,7 +184,11 @@ hipError_t launch_score_select(const pnmix_cfg& c, int B, int P, const float* ch
                                float* sigma, uint32_t* mask, hipStream_t stream) {
   const int n_chunks = (P + kChunk - 1) / kChunk;
   const int words = (c.d / 2 + 31) / 32;
-  hipLaunchKernelGGL(score_select_kernel, dim3(B * c.H_kv), dim3(256), 0, stream, chunk_sums,
+  // long prompts: one wave per head of the group (the n_g query heads and the KV head), each
+  // walking its chunk sums; short ones: four waves
+  const int rows = c.H_q / c.H_kv + 1;
+  const int threads = n_chunks > kSelLoads ? 64 * std::min(std::max(rows, 4), 16) : 256;
+  hipLaunchKernelGGL(score_select_kernel, dim3(B * c.H_kv), dim3(threads), 0, stream, chunk_sums,
                      sigma, mask, c.H_q, c.H_kv, c.d, P, n_chunks, c.n_hi_pairs, words);
   return hipGetLastError();
 }

@@ -492,6 +492,9 @@ PAGED_CASES = [
     ("qwen3-32b-B3", "qwen3-32b-64L-b32-32k", 3, 32 + 5 * 128 + 9, 3, True),
     ("qwen3-8b-B8", "qwen3-8b-36L-b32-8k", 8, 32 + 6 * 128 + 128, 2, True),
     ("llama-B40", "llama3.1-8b-32L-b110-8k", 40, 32 + 4 * 128 + 1, 0, True),
+    # 128 (sequence, KV head) items and 201 pages: the plan spreads the fp16 pieces over the
+    # page waves
+    ("qwen3-32b-B16-spread", "qwen3-32b-64L-b32-32k", 16, 32 + 200 * 128 + 50, 1, True),
 ]
 
 
@@ -507,6 +510,10 @@ def test_paged_decode_equals_contiguous(case):
     qp, k, v, qd = layer_inputs(w, 4, B, T)
     n_pages = (T - w.N_s) // w.N
     c = fill_cache_bulk(w, lc, qp, k, v, T, max_pages=n_pages + spare)
+    if "spread" in name:
+        plan = P.pnmix_decode_plan(lc, B, c.max_pages)
+        say(f"[paged] {name} plan={plan}")
+        assert plan["fp16_splits"] == 0 and plan["waves_per_group"] == 1
     if ragged:  # fewer pages for some sequences (their residual rows stay)
         for b in range(0, B, 2):
             c.lens[b, 1] = (b // 2) % (n_pages + 1)

@@ -15,7 +15,7 @@ size_t score_workspace_bytes(const pnmix_cfg& c, int B, int P);
 hipError_t launch_score_chunks(const pnmix_cfg& c, int B, int P, const uint16_t* q,
                                const uint16_t* k, float* chunk_sums, int skip_Ns,
                                int skip_pages, hipStream_t stream);
-hipError_t launch_score_select(const pnmix_cfg& c, int B, int P, const float* chunk_sums,
+hipError_t launch_score_select(const pnmix_cfg& c, int B, int P, float* chunk_sums,
                                float* sigma, uint32_t* mask, hipStream_t stream);
 size_t prefill_workspace_bytes(const pnmix_cfg& c, int B, int P);
 hipError_t launch_prefill_fused(const pnmix_cfg& c, int B, int P, const uint16_t* q,

@@ -9,8 +9,8 @@
 // chunk's token rows in LDS with 16-byte loads all in flight at once, and lane i owns RoPE pair
 // i and adds its pair norms over the chunk in ascending token order.  Pass 2 gives each (sequence, KV head) one
 // workgroup: its waves add the chunk sums of one head each in ascending chunk order (the loads
-// go out 32 chunks at a time, the next 32 in flight during the adds; one wave per head for
-// long prompts), divide by P, then wave 0 forms sigma, ranks the pairs through
+// go out 32 chunks at a time, the next 32 in flight during the adds; for long prompts a
+// workgroup per (sequence, head) adds them first, through LDS), divide by P, then wave 0 forms sigma, ranks the pairs through
 // LDS and writes the mask with a wave ballot.  The summation order is fixed, so sigma and the
 // mask are bit-identical to the reference oracle.
 #include "common.h"
@@ -82,11 +82,50 @@ __global__ void __launch_bounds__(64) score_chunks_kernel(const uint16_t* __rest
 
 constexpr int kSelLoads = 32;  // chunk-sum loads in flight per lane
 
+// Long prompts: one workgroup of 16 waves per (sequence, head) adds that head's chunk sums.
+// The chunk sums go to LDS kRowBlk chunks at a time (each wave loads kRowBlk / 16 of them, all
+// in flight at once); wave 0 adds them in ascending chunk order while the waves load the next
+// block into the other buffer.  The mean (sum / P) replaces the head's chunk-0 sums in place,
+// which score_select_kernel then reads.
+constexpr int kRowBlk = 256;
+constexpr int kRowWaves = 16;
+constexpr size_t kRowLds = 2 * (size_t)kRowBlk * 64 * sizeof(float);
+
+__global__ void __launch_bounds__(64 * kRowWaves) score_rowsum_kernel(float* __restrict__ chunk_sums,
+                                                                      int np, int P, int n_chunks) {
+  extern __shared__ __align__(16) float rbuf[];  // [2][kRowBlk][64]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float* cs = chunk_sums + (int64_t)blockIdx.x * n_chunks * np;
+  constexpr int per = kRowBlk / kRowWaves;  // chunks a wave loads per block
+  float s = 0.0f;
+  for (int c0 = 0, k = 0; c0 < n_chunks; c0 += kRowBlk, ++k) {
+    float v[per];
+#pragma unroll
+    for (int j = 0; j < per; ++j) {  // chunk indices past the end are clamped (not added)
+      const int c = min(c0 + wave + kRowWaves * j, n_chunks - 1);
+      v[j] = lane < np ? cs[(int64_t)c * np + lane] : 0.0f;
+    }
+    __syncthreads();  // wave 0 has added the block that used this buffer
+    float* buf = rbuf + (size_t)(k & 1) * kRowBlk * 64;
+#pragma unroll
+    for (int j = 0; j < per; ++j) buf[(wave + kRowWaves * j) * 64 + lane] = v[j];
+    __syncthreads();
+    if (wave == 0) {
+      const int n = min(kRowBlk, n_chunks - c0);
+#pragma unroll 8
+      for (int c = 0; c < n; ++c) s = s + buf[c * 64 + lane];
+    }
+  }
+  __syncthreads();  // every wave has read its chunk sums
+  if (wave == 0 && lane < np) cs[lane] = s / (float)P;
+}
+
 __global__ void __launch_bounds__(1024) score_select_kernel(const float* __restrict__ chunk_sums,
                                                            float* __restrict__ sigma,
                                                            uint32_t* __restrict__ mask, int H_q,
                                                            int H_kv, int d, int P, int n_chunks,
-                                                           int n_hi, int words) {
+                                                           int n_hi, int words, int presummed) {
   __shared__ float means[17][64];  // n_g query heads (<= 16) then the KV head
   __shared__ float sig[64];
   const int seq = blockIdx.x / H_kv;
@@ -99,7 +138,9 @@ __global__ void __launch_bounds__(1024) score_select_kernel(const float* __restr
   const int nwaves = blockDim.x >> 6;
   for (int r = wave; r <= ng; r += nwaves) {
     const int head = r < ng ? h * ng + r : H_q + h;
-    if (lane < np) {
+    if (lane < np && presummed) {
+      means[r][lane] = chunk_sums[((int64_t)(seq * H + head) * n_chunks) * np + lane];
+    } else if (lane < np) {
       const float* cs = chunk_sums + ((int64_t)(seq * H + head) * n_chunks) * np + lane;
       // the adds stay in ascending chunk order; the loads go out kSelLoads at a time, and for
       // long prompts the next kSelLoads are in flight while the current ones are added (chunk
@@ -180,16 +221,30 @@ hipError_t launch_score_chunks(const pnmix_cfg& c, int B, int P, const uint16_t*
   return hipGetLastError();
 }
 
-hipError_t launch_score_select(const pnmix_cfg& c, int B, int P, const float* chunk_sums,
+hipError_t launch_score_select(const pnmix_cfg& c, int B, int P, float* chunk_sums,
                                float* sigma, uint32_t* mask, hipStream_t stream) {
   const int n_chunks = (P + kChunk - 1) / kChunk;
   const int words = (c.d / 2 + 31) / 32;
-  // long prompts: one wave per head of the group (the n_g query heads and the KV head), each
-  // walking its chunk sums; short ones: four waves
+  // long prompts: the chunk sums of every (sequence, head) are added by a workgroup of their
+  // own first (rows in parallel; the means replace the chunk-0 sums), then one workgroup per
+  // (sequence, KV head) ranks the pairs; short prompts: one kernel, four waves adding the rows
+  int presummed = 0;
+  if (n_chunks > kSelLoads && c.d / 2 <= 64) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&score_rowsum_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)kRowLds);
+    if (attr == hipSuccess) {
+      hipLaunchKernelGGL(score_rowsum_kernel, dim3(B * (c.H_q + c.H_kv)), dim3(64 * kRowWaves),
+                         kRowLds, stream, chunk_sums, c.d / 2, P, n_chunks);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      presummed = 1;
+    }
+  }
   const int rows = c.H_q / c.H_kv + 1;
-  const int threads = n_chunks > kSelLoads ? 64 * std::min(std::max(rows, 4), 16) : 256;
+  const int threads = !presummed && n_chunks > kSelLoads ? 64 * std::min(std::max(rows, 4), 16) : 256;
   hipLaunchKernelGGL(score_select_kernel, dim3(B * c.H_kv), dim3(threads), 0, stream, chunk_sums,
-                     sigma, mask, c.H_q, c.H_kv, c.d, P, n_chunks, c.n_hi_pairs, words);
+                     sigma, mask, c.H_q, c.H_kv, c.d, P, n_chunks, c.n_hi_pairs, words, presummed);
   return hipGetLastError();
 }
 
